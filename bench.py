@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of libmgemm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one mgemm_run over the workload (host normalisation and dispatch,
+tile rasterisation, LDS staging, the MFMA/FMA contraction and the epilogue,
+all in one kernel launch) with every operand already resident in HBM.  The
+default workload is FP32 SGEMM 4096^3 row-major (uniform [-1,1] inputs).
+
+Prints ONE JSON line.  `roofline` is measured live with HIP events around
+each launch on the stream the kernel runs on; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload (and checks that sample
+against the GPU result).  Other workloads are measured briefly and reported
+under `workloads` (skip with --only-headline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of MFMA/FP32 peak (HBM GB/s for M≤64) vs CPU oracle, 1 GPU"
+# Pages' number for this exact workload and metric: cuBLAS pure-FP32 SGEMM
+# 4096^3 on an RTX 4090 (SGEMM report, cuBLAS denominator section): context only.
+PAGES_SGEMM_4096_TFLOPS = 57.2424
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    d = os.path.join(ROOT, "dense_gemm_mgemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def workload_table():
+    import workloads as W
+    t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
+         "ffn_bf16": W.ffn_bf16()}
+    for s in W.HGEMM_SHAPES:
+        c = W.hgemm_colmajor(*s)
+        t[c.name] = c
+    for m in W.SKINNY_M:
+        c = W.ffn_bf16(m)
+        t["skinny_bf16_m%d" % m] = c
+    return t
+
+
+def algorithmic(case):
+    from dense_gemm_mgemm_amd import costmodel as cm
+    es = 4 if case.dtype == "f32" else 2
+    flops = cm.gemm_flops(case.M, case.N, case.K)
+    nbytes = cm.min_bytes(case.M, case.N, case.K, es) + (es * case.M * case.N if case.beta else 0)
+    return flops, nbytes
+
+
+def is_hbm_bound(case) -> bool:
+    return case.dtype != "f32" and case.M <= 64
+
+
+def measure(h, case, steps, warmup, rotate=1):
+    """Time `steps` launches; returns timings, the kernel name and device buffers."""
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    from tests.parity import c_initial
+
+    A, B, C0 = case.make()
+    dA = [A.cuda() for _ in range(rotate)]
+    dB = [B.cuda() for _ in range(rotate)]
+    dC = [c_initial(case, C0).cuda() for _ in range(rotate)]
+    stream = torch.cuda.current_stream()
+    kname = mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
+                                   case.alpha, dA[0], case.lda, dB[0], case.ldb, case.beta, dC[0],
+                                   case.ldc, case.dtype)
+
+    def launch(i):
+        j = i % rotate
+        mg.mgemm_run(h, case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, dA[j],
+                     case.lda, dB[j], case.ldb, case.beta, dC[j], case.ldc, case.dtype,
+                     stream=stream)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    total_ms = t_all0.elapsed_time(t_all1)
+    return {
+        "kernel": kname, "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+        "launch_ms_mean": sum(per) / len(per), "launch_ms_median": per[len(per) // 2],
+        "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
+        "inputs": (A, B, C0), "out": dC[(steps - 1) % rotate],
+    }
+
+
+def cpu_baseline(case, out_dev, budget_s):
+    """Time the oracle on a bounded row sample of the workload and check that
+    sample against the GPU output."""
+    import numpy as np
+    import oracle
+    from tests import parity as P
+    from workloads import storage_view
+
+    A, B, C0 = case.inputs
+    a, b = storage_view(A), storage_view(B)
+    c0 = None if C0 is None else storage_view(C0)
+    threads = oracle.max_threads()
+    nrows = max(1, min(case.M, 16))
+    rng = np.random.default_rng(0)
+    spent, rows_done, t_total, results = 0.0, [], 0.0, []
+    while True:
+        rows = np.sort(rng.choice(case.M, size=nrows, replace=False)) if nrows < case.M \
+            else np.arange(case.M)
+        t0 = time.perf_counter()
+        exact = oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
+                            case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
+                            rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        t_total, rows_done, results = dt, rows, exact
+        if nrows >= case.M or dt * 2 > budget_s:
+            break
+        nrows = int(min(case.M, max(nrows * 2, nrows * budget_s / max(dt, 1e-3) * 0.8)))
+    flops = 2.0 * len(rows_done) * case.N * case.K
+    got = P.logical(case, oracle.decode(case.dtype, storage_view(out_dev.cpu())))[rows_done]
+    rep = P.compare(case, got, results)
+    return ({"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
+             "kind": "oracle", "sample": "%d of %d rows of C (%.1f GFLOP in %.1f s, FP64)" % (
+                 len(rows_done), case.M, flops / 1e9, t_total)},
+            {"rows": len(rows_done), "max_err": rep["max_err"], "tol": rep["tol"],
+             "ok": rep["ok"]})
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+        e = t.get("%s/%s" % (kernel, workload))
+        if e and e.get("src_hash") == src_hash():
+            return e["bytes_per_launch"]
+    except (ValueError, KeyError):
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sgemm_4096")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    from dense_gemm_mgemm_amd import costmodel as cm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    h = mg.mgemm_create()
+    table = workload_table()
+    case = table[args.workload]
+    flops, nbytes = algorithmic(case)
+    hbm = is_hbm_bound(case)
+    log("headline:", case.name)
+    r = measure(h, case, args.steps, args.warmup, rotate=4 if hbm else 1)
+    case.inputs = r["inputs"]
+
+    if args.copy_probe:
+        n = args.copy_probe * 2 ** 20 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB x3" % args.copy_probe)
+
+    per_launch_s = r["launch_ms_mean"] * 1e-3
+    if hbm:
+        achieved, peak, unit, bound = nbytes / per_launch_s / 1e9, cm.PEAK_HBM_GBS, "GB/s", "hbm"
+        value, vunit = nbytes / (r["ms_per_step"] * 1e-3) / 1e9, "GB/s"
+    else:
+        achieved, peak = flops / per_launch_s / 1e12, cm.PEAK_TFLOPS[case.dtype]
+        unit, bound = "TFLOP/s", "mfma"
+        value, vunit = flops / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
+    traffic = traffic_for(r["kernel"], case.name)
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": vunit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": (round(value / PAGES_SGEMM_4096_TFLOPS, 3)
+                        if case.name == "sgemm_4096" else None),
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
+                   "layoutA": case.layoutA, "layoutB": case.layoutB, "lda": case.lda,
+                   "ldb": case.ldb, "ldc": case.ldc, "alpha": case.alpha, "beta": case.beta,
+                   "kernel": r["kernel"], "inputs": "%s/%s seeds %s" % (case.kindA, case.kindB,
+                                                                        list(case.seeds[:2])),
+                   "vs_baseline_ref": "cuBLAS pure-FP32 4096^3 on RTX 4090 from the pages, "
+                                      "57.24 TFLOP/s (another machine: context only)"
+                   if case.name == "sgemm_4096" else None},
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_per_launch": flops if not hbm else nbytes,
+                     "launch_ms_mean": round(r["launch_ms_mean"], 5),
+                     "launch_ms_p10": round(r["launch_ms_p10"], 5),
+                     "launch_ms_p90": round(r["launch_ms_p90"], 5)},
+        "cpu_baseline": None,
+        "src_hash": src_hash(),
+    }
+    if not args.no_cpu_baseline:
+        cb, chk = cpu_baseline(case, r["out"], args.cpu_budget)
+        line["cpu_baseline"] = cb
+        line["parity_sample"] = chk
+        if not chk["ok"]:
+            log("PARITY FAILURE on the sampled rows:", chk)
+    if not args.only_headline:
+        others = {}
+        for name, c in table.items():
+            if name == case.name:
+                continue
+            f2, b2 = algorithmic(c)
+            hb = is_hbm_bound(c)
+            log("workload:", name)
+            rr = measure(h, c, 20, 5, rotate=4 if hb else 1)
+            s = rr["launch_ms_mean"] * 1e-3
+            ent = {"kernel": rr["kernel"], "launch_ms_mean": round(rr["launch_ms_mean"], 5),
+                   "dtype": c.dtype}
+            if hb:
+                ent.update(GBs=round(b2 / s / 1e9, 1), frac_hbm=round(b2 / s / 1e9 / cm.PEAK_HBM_GBS, 4))
+            else:
+                tf = f2 / s / 1e12
+                ent.update(TFLOPs=round(tf, 2), frac_peak=round(tf / cm.PEAK_TFLOPS[c.dtype], 4))
+            others[name] = ent
+            del rr
+            torch.cuda.empty_cache()
+        line["workloads"] = others
+    mg.mgemm_destroy(h)
+    print(json.dumps(line), flush=True)
+    if line.get("parity_sample") and not line["parity_sample"]["ok"]:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+"""Python binding of libmgemm (dense GEMM for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmgemm.so``.  The functions carry the names of the C entry
+points declared in ``include/mgemm.h``.  Operands are passed as device
+pointers (ints) or as torch tensors on the GPU, whose ``data_ptr()`` is
+taken; torch is used for device memory and streams only.
+
+There is no fallback: if ``libmgemm.so`` is missing or fails to load, every
+entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmgemm.so")
+
+MGEMM_SUCCESS, MGEMM_ERR_INVALID_ARG, MGEMM_ERR_UNSUPPORTED, MGEMM_ERR_HIP, MGEMM_ERR_ALLOC = range(5)
+MGEMM_ROW_MAJOR, MGEMM_COL_MAJOR = 0, 1
+MGEMM_F32, MGEMM_F16, MGEMM_BF16 = 0, 1, 2
+KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
+           "skinny"]
+MGEMM_KERNEL_AUTO = 0
+
+_LAYOUT = {"row": MGEMM_ROW_MAJOR, "col": MGEMM_COL_MAJOR}
+_DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
+
+EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel",
+            "mgemm_select_kernel", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
+
+
+class MgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, _status_str(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libmgemm.so (raises OSError if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise OSError("libmgemm.so is not built (%s); run `python -m dense_gemm_mgemm_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    i64, f32, vp, ci = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+    run_args = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, ci, vp]
+    lib.mgemm_create.argtypes = [ctypes.POINTER(vp)]
+    lib.mgemm_destroy.argtypes = [vp]
+    lib.mgemm_run.argtypes = [vp] + run_args
+    lib.mgemm_run_kernel.argtypes = [vp, ci] + run_args
+    lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
+    for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel",
+                 "mgemm_select_kernel"):
+        getattr(lib, name).restype = ci
+    lib.mgemm_status_string.argtypes = [ci]
+    lib.mgemm_status_string.restype = ctypes.c_char_p
+    lib.mgemm_kernel_name.argtypes = [ci]
+    lib.mgemm_kernel_name.restype = ctypes.c_char_p
+    lib.mgemm_num_cu.argtypes = [vp]
+    lib.mgemm_num_cu.restype = ci
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _status_str(s: int) -> str:
+    try:
+        return load().mgemm_status_string(s).decode()
+    except OSError:
+        return "status %d" % s
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _enum(x, table):
+    return table[x] if isinstance(x, str) else int(x)
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def mgemm_create() -> int:
+    """Handle bound to the current HIP device."""
+    h = ctypes.c_void_p()
+    st = load().mgemm_create(ctypes.byref(h))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_create")
+    return h.value
+
+
+def mgemm_destroy(h: int) -> None:
+    load().mgemm_destroy(h)
+
+
+def _args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype):
+    return (_enum(layoutA, _LAYOUT), _enum(layoutB, _LAYOUT), int(M), int(N), int(K), float(alpha),
+            _ptr(A), int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+            _enum(dtype, _DTYPE))
+
+
+def mgemm_run(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,
+              stream=None) -> None:
+    """Enqueue C = alpha*op(A)op(B) + beta*C on `stream` (torch's current by default)."""
+    st = load().mgemm_run(h, *_args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                    ldc, dtype), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run")
+
+
+def mgemm_run_kernel(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     dtype, stream=None) -> None:
+    """As mgemm_run with one kernel variant forced (name or number)."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    st = load().mgemm_run_kernel(h, k, *_args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb,
+                                              beta, C, ldc, dtype), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_kernel(%s)" % KERNELS[k] if 0 <= k < len(KERNELS) else k)
+
+
+def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        dtype) -> str:
+    """Name of the variant mgemm_run would launch ("auto": scale-only or nothing)."""
+    out = ctypes.c_int()
+    st = load().mgemm_select_kernel(h, *_args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb,
+                                              beta, C, ldc, dtype), ctypes.byref(out))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_select_kernel")
+    return load().mgemm_kernel_name(out.value).decode()
+
+
+def mgemm_status_string(s: int) -> str:
+    return load().mgemm_status_string(s).decode()
+
+
+def mgemm_kernel_name(k: int) -> str:
+    return load().mgemm_kernel_name(k).decode()
+
+
+def mgemm_num_cu(h) -> int:
+    return load().mgemm_num_cu(h)

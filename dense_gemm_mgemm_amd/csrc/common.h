@@ -1,0 +1,112 @@
+// Internal definitions shared by the libmgemm kernels and host dispatch.
+//
+// Every kernel works on ONE canonical problem: a row-major C (M x N, ldc)
+//     C(m,n) = alpha * sum_k A'(m,k) B'(k,n) + beta * C(m,n)
+// where A' and B' are each either K-contiguous or MN-contiguous in memory.
+// The host reaches this form from any (layoutA, layoutB) pair with the
+// transpose identity of the SGEMM report ("SGEMM measurements and three
+// ledgers", section "how the cuBLAS denominator was fixed"): a column-major C
+// is the row-major C^T = B^T A^T of the same bytes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mgemm {
+
+enum DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct Problem {
+    int64_t M, N, K;
+    float alpha, beta;
+    const void* A;   // A'(m,k) = a_kc ? A[m*lda + k] : A[k*lda + m]
+    int64_t lda;
+    const void* B;   // B'(k,n) = b_kc ? B[n*ldb + k] : B[k*ldb + n]
+    int64_t ldb;
+    void* C;         // C(m,n) = C[m*ldc + n]
+    int64_t ldc;
+    int a_kc, b_kc;
+    int dtype;
+    int num_cu;
+};
+
+// ---------------------------------------------------------------------------
+// Workgroup -> output tile.
+//
+// gfx950 hands consecutive workgroup ids to its 8 XCDs in turn (id % 8 picks
+// the XCD), and each XCD has its own L2.  We first renumber ids so that the
+// workgroups sharing an XCD get consecutive tile numbers, then walk tiles in
+// groups of `group_m` tile-rows (all tile-columns of a group before the next
+// group), so that workgroups resident at the same time on one XCD share A rows
+// and B columns in that XCD's L2.  This is the M-grouped order of the K1 GEMM
+// resource model (GROUP_SIZE_M) and the M-first CTA order of the MTT S4000
+// write-up (section 14), made XCD-aware.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int group_m, int& tm, int& tn) {
+    constexpr int NXCD = 8;
+    int xcd = bid % NXCD;
+    int local = bid / NXCD;
+    int q = nblocks / NXCD, r = nblocks % NXCD;
+    int t = xcd * q + (xcd < r ? xcd : r) + local;
+    int per_group = group_m * tiles_n;
+    int g = t / per_group;
+    int first_m = g * group_m;
+    int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    int within = t - g * per_group;
+    tm = first_m + within % gsize;
+    tn = within / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// Element conversions.  16-bit types travel as raw uint16_t bit patterns.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    // v_cvt_f16_f32 rounds to nearest even under the default float mode.
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    // Round to nearest even on the discarded 16 bits; NaN stays a quiet NaN.
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<F32> {
+    using T = float;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<F16> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return f16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = f32_to_f16_bits(v); }
+};
+template <> struct Elem<BF16> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each kernel file defines its own).  They return a HIP error of
+// the launch; shape/alignment eligibility is checked by the *_supports calls.
+// ---------------------------------------------------------------------------
+hipError_t launch_general(const Problem& p, hipStream_t s);
+hipError_t launch_scale(const Problem& p, hipStream_t s);
+hipError_t launch_f32_mfma(const Problem& p, hipStream_t s);
+bool f32_mfma_supports(const Problem& p);
+hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s);
+bool h_mfma_supports(const Problem& p, int variant);
+hipError_t launch_skinny(const Problem& p, hipStream_t s);
+bool skinny_supports(const Problem& p);
+
+}  // namespace mgemm

@@ -1,0 +1,230 @@
+// libmgemm host side: argument validation, normalisation to one canonical
+// row-major problem, kernel selection and launch.  See include/mgemm.h for
+// the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <string.h>
+
+#include "../../include/mgemm.h"
+#include "common.h"
+
+struct mgemm_handle_s {
+    int device;
+    int num_cu;
+};
+
+namespace {
+
+using mgemm::Problem;
+
+inline bool valid_layout(mgemm_layout_t l) { return l == MGEMM_ROW_MAJOR || l == MGEMM_COL_MAJOR; }
+inline bool valid_dtype(mgemm_dtype_t d) { return d == MGEMM_F32 || d == MGEMM_F16 || d == MGEMM_BF16; }
+inline int64_t max1(int64_t x) { return x > 1 ? x : 1; }
+
+// Checks the rules of mgemm_run and builds the canonical problem.
+mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                            int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                            int64_t ldc, mgemm_dtype_t dtype, Problem* out) {
+    if (!h || !valid_layout(layoutA) || !valid_layout(layoutB) || !valid_dtype(dtype))
+        return MGEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return MGEMM_ERR_INVALID_ARG;
+    const bool rowA = layoutA == MGEMM_ROW_MAJOR, rowB = layoutB == MGEMM_ROW_MAJOR;
+    if (lda < max1(rowA ? K : M)) return MGEMM_ERR_INVALID_ARG;
+    if (ldb < max1(rowB ? N : K)) return MGEMM_ERR_INVALID_ARG;
+    if (ldc < max1(rowA ? N : M)) return MGEMM_ERR_INVALID_ARG;
+    // Offsets are formed in 64-bit; keep every addressed element index below 2^62.
+    const int64_t lim = (int64_t)1 << 62;
+    if (M > lim / max1(ldc) || N > lim / max1(ldc) || K > lim / max1(lda) || K > lim / max1(ldb) ||
+        M > lim / max1(lda) || N > lim / max1(ldb))
+        return MGEMM_ERR_INVALID_ARG;
+    const bool empty = M == 0 || N == 0;
+    const bool reads_ab = !empty && K > 0 && alpha != 0.f;
+    if (!empty && C == nullptr) return MGEMM_ERR_INVALID_ARG;
+    if (reads_ab && (A == nullptr || B == nullptr)) return MGEMM_ERR_INVALID_ARG;
+
+    Problem p;
+    p.K = K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.C = C;
+    p.ldc = ldc;
+    p.dtype = (int)dtype;
+    p.num_cu = h->num_cu;
+    if (rowA) {
+        // Row-major C = A B.  A row-major is K-contiguous; B row-major is
+        // N-contiguous, column-major is K-contiguous.
+        p.M = M; p.N = N;
+        p.A = A; p.lda = lda; p.a_kc = 1;
+        p.B = B; p.ldb = ldb; p.b_kc = rowB ? 0 : 1;
+    } else {
+        // Column-major C is row-major C^T (N x M) = B^T A^T on the same bytes.
+        //   A'' = B^T (N x K): B row-major -> B^T is N-contiguous along its
+        //   rows' index, i.e. not K-contiguous; B column-major -> K-contiguous.
+        //   B'' = A^T (K x M): A column-major -> M-contiguous.
+        p.M = N; p.N = M;
+        p.A = B; p.lda = ldb; p.a_kc = rowB ? 0 : 1;
+        p.B = A; p.ldb = lda; p.b_kc = 0;
+    }
+    *out = p;
+    return MGEMM_SUCCESS;
+}
+
+bool variant_supports(const Problem& p, mgemm_kernel_t k) {
+    switch (k) {
+    case MGEMM_KERNEL_GENERAL: return true;
+    case MGEMM_KERNEL_F32_MFMA: return mgemm::f32_mfma_supports(p);
+    case MGEMM_KERNEL_H_256x256:
+    case MGEMM_KERNEL_H_256x192:
+    case MGEMM_KERNEL_H_128x128: return mgemm::h_mfma_supports(p, (int)k);
+    case MGEMM_KERNEL_SKINNY: return mgemm::skinny_supports(p);
+    default: return false;
+    }
+}
+
+// Kernel choice for a canonical problem.
+mgemm_kernel_t choose(const Problem& p) {
+    if (p.dtype == mgemm::F32) return MGEMM_KERNEL_F32_MFMA;
+    if (p.M <= 64 && mgemm::skinny_supports(p)) return MGEMM_KERNEL_SKINNY;
+    // 16-bit: pick the tile whose grid fills the CUs best, preferring the
+    // larger tile (more reuse per byte staged) when the fill is equal.
+    const mgemm_kernel_t order[3] = {MGEMM_KERNEL_H_256x256, MGEMM_KERNEL_H_256x192,
+                                     MGEMM_KERNEL_H_128x128};
+    const int bm[3] = {256, 256, 128}, bn[3] = {256, 192, 128};
+    mgemm_kernel_t best = MGEMM_KERNEL_GENERAL;
+    double best_score = -1.0;
+    for (int v = 0; v < 3; ++v) {
+        if (!mgemm::h_mfma_supports(p, (int)order[v])) continue;
+        const int64_t tiles = ((p.M + bm[v] - 1) / bm[v]) * ((p.N + bn[v] - 1) / bn[v]);
+        const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+        const int64_t waves = (tiles + slots - 1) / slots;
+        // Useful work over the CU-time the grid occupies, counting the padding
+        // of ragged edge tiles as waste.
+        const double useful = (double)p.M * (double)p.N;
+        const double occupied = (double)waves * slots * bm[v] * bn[v];
+        double score = useful / occupied;
+        if (score > best_score + 1e-9) { best_score = score; best = order[v]; }
+    }
+    return best;
+}
+
+mgemm_status_t launch(const Problem& p, mgemm_kernel_t k, hipStream_t s) {
+    hipError_t e;
+    switch (k) {
+    case MGEMM_KERNEL_GENERAL: e = mgemm::launch_general(p, s); break;
+    case MGEMM_KERNEL_F32_MFMA: e = mgemm::launch_f32_mfma(p, s); break;
+    case MGEMM_KERNEL_H_256x256:
+    case MGEMM_KERNEL_H_256x192:
+    case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)k, s); break;
+    case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
+    default: return MGEMM_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+}
+
+mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, mgemm_layout_t layoutA,
+                        mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                        void* C, int64_t ldc, mgemm_dtype_t dtype, hipStream_t stream) {
+    Problem p;
+    mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc, dtype, &p);
+    if (st != MGEMM_SUCCESS) return st;
+    if (forced != MGEMM_KERNEL_AUTO && (forced <= 0 || forced >= MGEMM_KERNEL_COUNT))
+        return MGEMM_ERR_INVALID_ARG;
+    if (p.M == 0 || p.N == 0) return MGEMM_SUCCESS;
+    if (p.K == 0 || p.alpha == 0.f) {
+        hipError_t e = mgemm::launch_scale(p, stream);
+        return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+    }
+    mgemm_kernel_t k = forced == MGEMM_KERNEL_AUTO ? choose(p) : forced;
+    if (!variant_supports(p, k)) return MGEMM_ERR_UNSUPPORTED;
+    return launch(p, k, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+mgemm_status_t mgemm_create(mgemm_handle_t* out) {
+    if (!out) return MGEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MGEMM_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MGEMM_ERR_HIP;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MGEMM_ERR_UNSUPPORTED;
+    mgemm_handle_s* h = new (std::nothrow) mgemm_handle_s;
+    if (!h) return MGEMM_ERR_ALLOC;
+    h->device = dev;
+    h->num_cu = prop.multiProcessorCount;
+    *out = h;
+    return MGEMM_SUCCESS;
+}
+
+mgemm_status_t mgemm_destroy(mgemm_handle_t h) {
+    delete h;
+    return MGEMM_SUCCESS;
+}
+
+mgemm_status_t mgemm_run(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                         int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                         mgemm_dtype_t dtype, hipStream_t stream) {
+    return run_impl(h, MGEMM_KERNEL_AUTO, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                    ldc, dtype, stream);
+}
+
+mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
+                                mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                float alpha, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, float beta, void* C, int64_t ldc,
+                                mgemm_dtype_t dtype, hipStream_t stream) {
+    if (kernel == MGEMM_KERNEL_AUTO) return MGEMM_ERR_INVALID_ARG;
+    return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                    dtype, stream);
+}
+
+mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
+                                   mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                   float alpha, const void* A, int64_t lda, const void* B,
+                                   int64_t ldb, float beta, void* C, int64_t ldc,
+                                   mgemm_dtype_t dtype, mgemm_kernel_t* kernel_out) {
+    if (!kernel_out) return MGEMM_ERR_INVALID_ARG;
+    Problem p;
+    mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc, dtype, &p);
+    if (st != MGEMM_SUCCESS) return st;
+    if (p.M == 0 || p.N == 0 || p.K == 0 || p.alpha == 0.f) *kernel_out = MGEMM_KERNEL_AUTO;
+    else *kernel_out = choose(p);
+    return MGEMM_SUCCESS;
+}
+
+const char* mgemm_status_string(mgemm_status_t s) {
+    switch (s) {
+    case MGEMM_SUCCESS: return "success";
+    case MGEMM_ERR_INVALID_ARG: return "invalid argument";
+    case MGEMM_ERR_UNSUPPORTED: return "unsupported";
+    case MGEMM_ERR_HIP: return "HIP error";
+    case MGEMM_ERR_ALLOC: return "allocation failed";
+    }
+    return "unknown";
+}
+
+const char* mgemm_kernel_name(mgemm_kernel_t k) {
+    switch (k) {
+    case MGEMM_KERNEL_AUTO: return "auto";
+    case MGEMM_KERNEL_GENERAL: return "general";
+    case MGEMM_KERNEL_F32_MFMA: return "f32_mfma";
+    case MGEMM_KERNEL_H_256x256: return "h_mfma_256x256";
+    case MGEMM_KERNEL_H_256x192: return "h_mfma_256x192";
+    case MGEMM_KERNEL_H_128x128: return "h_mfma_128x128";
+    case MGEMM_KERNEL_SKINNY: return "skinny";
+    default: return "unknown";
+    }
+}
+
+int mgemm_num_cu(mgemm_handle_t h) { return h ? h->num_cu : 0; }
+
+}  // extern "C"

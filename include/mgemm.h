@@ -1,0 +1,151 @@
+/*
+ * mgemm.h -- C ABI of libmgemm, dense matrix multiplication for AMD Instinct
+ * MI355X (gfx950).
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * The operation is the GEMM of the SGEMM report "SGEMM measurements and three
+ * ledgers" (daleiyang; the naive kernel K1 stores alpha*acc + beta*C) with the
+ * (A, B, C, M, N, K, alpha, beta) signature of the zwxr.cn SGEMM post
+ * (section 3.3).  FP16/BF16 inputs accumulate in FP32 and are rounded once to
+ * the output format at the end ("Chapter 5: Operators and Runtime",
+ * ai-infra-book, sections 5.2.1 and 5.4.2, round_to_bf16(acc); the MTT S4000
+ * FP16 GEMM write-up, section 1, FP16 in/out with FP32 accumulation).
+ * Row-major and column-major storage are related by the transpose identity of
+ * the SGEMM report (section "how the cuBLAS denominator was fixed"): row-major
+ * C = A B is the same bytes as column-major C^T = B^T A^T.
+ *
+ * All entry points are plain C.  Pointers passed as A, B, C are DEVICE
+ * pointers (HIP device memory of the handle's GPU).  Sizes and leading
+ * dimensions are counted in elements.
+ */
+#ifndef MGEMM_H_
+#define MGEMM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream type, declared here so this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    MGEMM_SUCCESS = 0,
+    MGEMM_ERR_INVALID_ARG = 1,   /* bad size, enum, leading dimension or null pointer */
+    MGEMM_ERR_UNSUPPORTED = 2,   /* device is not gfx950, or a forced kernel cannot run the problem */
+    MGEMM_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
+    MGEMM_ERR_ALLOC = 4          /* host allocation failed */
+} mgemm_status_t;
+
+typedef enum {
+    MGEMM_ROW_MAJOR = 0,         /* element (r, c) at r*ld + c */
+    MGEMM_COL_MAJOR = 1          /* element (r, c) at c*ld + r */
+} mgemm_layout_t;
+
+typedef enum {
+    MGEMM_F32 = 0,               /* A, B, C in IEEE binary32; FP32 products and sums */
+    MGEMM_F16 = 1,               /* A, B, C in IEEE binary16; FP32 accumulation */
+    MGEMM_BF16 = 2               /* A, B, C in bfloat16; FP32 accumulation */
+} mgemm_dtype_t;
+
+/* Kernel variants.  MGEMM_KERNEL_AUTO lets the library choose; the others
+ * force one code path (each must produce the same result to the stated
+ * tolerance; tests run every one of them). */
+typedef enum {
+    MGEMM_KERNEL_AUTO = 0,
+    MGEMM_KERNEL_GENERAL = 1,    /* any dtype/layout/alignment, VALU FMA, 64x64 tiles */
+    MGEMM_KERNEL_F32_MFMA = 2,   /* FP32 on v_mfma_f32_32x32x2_f32, 128x128 tiles */
+    MGEMM_KERNEL_H_256x256 = 3,  /* FP16/BF16 MFMA, 256x256 tiles */
+    MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles */
+    MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
+    MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
+    MGEMM_KERNEL_COUNT = 7
+} mgemm_kernel_t;
+
+typedef struct mgemm_handle_s* mgemm_handle_t;
+
+/*
+ * mgemm_create -- bind a handle to the CURRENT HIP device.
+ *   out : receives the handle (owned by the caller, release with mgemm_destroy).
+ * Returns MGEMM_ERR_UNSUPPORTED if the device is not gfx950, MGEMM_ERR_HIP if
+ * the device cannot be queried, MGEMM_ERR_INVALID_ARG if out is NULL.
+ * The handle is immutable after creation: concurrent mgemm_run calls on
+ * different streams may share it.  It holds no device memory.
+ */
+mgemm_status_t mgemm_create(mgemm_handle_t* out);
+
+/* mgemm_destroy -- release a handle (NULL is accepted and ignored). */
+mgemm_status_t mgemm_destroy(mgemm_handle_t h);
+
+/*
+ * mgemm_run -- enqueue C = alpha*op(A)*op(B) + beta*C on `stream`.
+ *
+ *   layoutA, layoutB : storage order of the logical A (M x K) and B (K x N).
+ *   C (M x N) is stored in layoutA's order (one order for the call, as in
+ *   cblas).  Leading dimensions must satisfy
+ *       A: lda >= max(1, layoutA == ROW ? K : M)
+ *       B: ldb >= max(1, layoutB == ROW ? N : K)
+ *       C: ldc >= max(1, layoutA == ROW ? N : M)
+ *   M, N, K >= 0.  M == 0 or N == 0 does nothing.  K == 0 or alpha == 0 gives
+ *   C = beta*C and does not read A or B.  beta == 0 never reads C (it may hold
+ *   NaN).  A and B must not overlap C.
+ *   alpha, beta : FP32 scalars by value.
+ *   dtype : element type of A, B and C.
+ *   stream : HIP stream of the handle's device (0 = the null stream).
+ *
+ * Asynchronous: returns once the kernel is enqueued, with no device
+ * synchronisation.  The caller owns A, B, C and keeps them alive until the
+ * stream's work has completed.  No alignment is required: operands that are
+ * not 16-byte aligned (or whose leading dimension breaks the alignment of a
+ * row) take a narrower load path.
+ * Errors: MGEMM_ERR_INVALID_ARG for a violated rule above (nothing enqueued);
+ * MGEMM_ERR_HIP if the launch fails.
+ */
+mgemm_status_t mgemm_run(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                         int64_t M, int64_t N, int64_t K, float alpha,
+                         const void* A, int64_t lda, const void* B, int64_t ldb,
+                         float beta, void* C, int64_t ldc, mgemm_dtype_t dtype,
+                         hipStream_t stream);
+
+/*
+ * mgemm_run_kernel -- as mgemm_run, but force one kernel variant.
+ * Returns MGEMM_ERR_UNSUPPORTED (nothing enqueued) when that variant cannot
+ * run this problem (wrong dtype, alignment or shape class).  Used to check
+ * every dispatch branch against the same reference, so that no branch goes
+ * untested (the lesson of the MTT S4000 GEMM write-up, section 8).
+ */
+mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel,
+                                mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                                int64_t M, int64_t N, int64_t K, float alpha,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                float beta, void* C, int64_t ldc, mgemm_dtype_t dtype,
+                                hipStream_t stream);
+
+/*
+ * mgemm_select_kernel -- the variant mgemm_run would launch for this problem
+ * (validates the arguments exactly as mgemm_run does; pointers are only
+ * inspected for alignment and may be any value with the intended alignment).
+ *   kernel_out : receives the chosen variant; MGEMM_KERNEL_AUTO means the call
+ *   would launch nothing (M == 0 or N == 0) or only scale C (K == 0 or
+ *   alpha == 0).
+ */
+mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
+                                   mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                   float alpha, const void* A, int64_t lda, const void* B,
+                                   int64_t ldb, float beta, void* C, int64_t ldc,
+                                   mgemm_dtype_t dtype, mgemm_kernel_t* kernel_out);
+
+/* Static strings; never NULL (unknown values give "unknown"). */
+const char* mgemm_status_string(mgemm_status_t s);
+const char* mgemm_kernel_name(mgemm_kernel_t k);
+
+/* Number of compute units of the handle's device (0 if h is NULL). */
+int mgemm_num_cu(mgemm_handle_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H_ */

@@ -1,0 +1,272 @@
+"""GPU parity: libmgemm against the CPU oracle, through the C ABI.
+
+Every test here needs an MI355X and the built libmgemm.so (marker `gpu`).
+Each workload family of the pages is run at its full size (sampled rows and
+columns where the oracle would take too long) and every kernel variant is
+forced on problems it supports, so that no dispatch branch goes unchecked.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_mgemm_amd as mg
+import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def h():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.load()
+    handle = mg.mgemm_create()
+    yield handle
+    mg.mgemm_destroy(handle)
+
+
+def supported(h, case, kernel, inputs):
+    """Run a forced kernel; returns None if the variant declines the problem."""
+    try:
+        return P.run_gpu(h, case, kernel, inputs=inputs)
+    except mg.MgemmError as e:
+        if e.status == mg.MGEMM_ERR_UNSUPPORTED:
+            return None
+        raise
+
+
+# ---------------------------------------------------------------------------
+# FP32 SGEMM 256^3: random (tolerance) and integer-valued (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kernel", ["auto"] + P.KERNELS_F32)
+def test_sgemm_256_uniform(h, kernel):
+    case = W.sgemm_256()
+    say("sgemm_256_uniform", kernel)
+    P.check_tolerance(case, *P.run_gpu(h, case, kernel))
+
+
+@pytest.mark.parametrize("kernel", ["auto"] + P.KERNELS_F32)
+def test_sgemm_256_integer_bit_exact(h, kernel):
+    case = W.sgemm_256(int_valued=True)
+    say("sgemm_256_int", kernel)
+    P.check_bit_exact(case, *P.run_gpu(h, case, kernel))
+
+
+def test_sgemm_4096_sampled(h):
+    case = W.sgemm_4096()
+    say("sgemm_4096 auto")
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 128), cols=[0, 127, 128, 4095])
+
+
+def test_ragged_f32_sampled(h):
+    case = W.ragged_f32()
+    say("ragged_f32 auto")
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 128) + [999],
+                      cols=[0, 12288, 12289])
+
+
+# ---------------------------------------------------------------------------
+# FP16 column-major contest shapes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", W.HGEMM_SHAPES[:2])
+@pytest.mark.parametrize("kernel", ["auto"] + P.KERNELS_16)
+def test_hgemm_colmajor_small(h, shape, kernel):
+    case = W.hgemm_colmajor(*shape)
+    say("hgemm", shape, kernel)
+    out = supported(h, case, kernel, case.make())
+    if out is None:
+        pytest.skip("%s declines this problem" % kernel)
+    P.check_tolerance(case, *out)
+
+
+def test_hgemm_colmajor_8k_sampled(h):
+    case = W.hgemm_colmajor(*W.HGEMM_SHAPES[2])
+    say("hgemm 8k auto")
+    out = P.run_gpu(h, case)
+    # Logical rows of column-major C are canonical columns and vice versa, so
+    # sample both.
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 256, extra=6),
+                      cols=[0, 255, 256, 8191])
+
+
+# ---------------------------------------------------------------------------
+# BF16 FFN projection and the skinny M sweep on the same W
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kernel", ["auto"] + P.KERNELS_16)
+def test_ffn_bf16_sampled(h, kernel):
+    case = W.ffn_bf16()
+    say("ffn", kernel)
+    out = supported(h, case, kernel, case.make())
+    if out is None:
+        pytest.skip("%s declines this problem" % kernel)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 256, extra=8),
+                      cols=[0, 191, 192, 12287])
+
+
+@pytest.mark.parametrize("M", W.SKINNY_M)
+def test_skinny_bf16_full(h, M):
+    case = W.ffn_bf16(M)
+    say("skinny", M)
+    P.check_tolerance(case, *P.run_gpu(h, case))
+
+
+# ---------------------------------------------------------------------------
+# Small and ragged shapes, integer data, every variant: bit-exact
+# ---------------------------------------------------------------------------
+SIZES = [1, 2, 3, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _sweep_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = [(1, 1, 1), (257, 255, 129), (64, 64, 64), (65, 63, 33), (16, 257, 31)]
+    while len(shapes) < n:
+        shapes.append(tuple(int(x) for x in rng.choice(SIZES, 3)))
+    return shapes
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_small_shape_sweep_bit_exact(h, dtype):
+    kernels = ["auto"] + (P.KERNELS_F32 if dtype == "f32" else P.KERNELS_16 + ["skinny"])
+    ran = {k: 0 for k in kernels}
+    for si, (M, N, K) in enumerate(_sweep_shapes(14, 7 + len(dtype))):
+        for (la, lb), (alpha, beta) in itertools.product(
+                itertools.product(["row", "col"], ["row", "col"]), [(1.0, 0.0), (1.0, -0.5)]):
+            pad = si % 3
+            case = W.Case("sweep", M, N, K, dtype, layoutA=la, layoutB=lb,
+                          lda=(K if la == "row" else M) + pad, ldb=(N if lb == "row" else K) + pad,
+                          ldc=(N if la == "row" else M) + pad, alpha=alpha, beta=beta,
+                          kindA="int", kindB="int", kindC="int", seeds=(si, si + 100, si + 200))
+            inputs = case.make()
+            for k in kernels:
+                out = supported(h, case, k, inputs)
+                if out is None:
+                    continue
+                ran[k] += 1
+                try:
+                    P.check_bit_exact(case, *out)
+                except AssertionError:
+                    say("FAILED", dtype, (M, N, K), la, lb, alpha, beta, k)
+                    raise
+    say("ran", ran)
+    assert ran["auto"] > 0 and ran["general"] > 0
+
+
+# ---------------------------------------------------------------------------
+# Contract details
+# ---------------------------------------------------------------------------
+def test_beta_zero_ignores_nan_c(h):
+    for dtype in ("f32", "f16", "bf16"):
+        case = W.Case("nanC", 96, 80, 40, dtype, kindA="int", kindB="int", seeds=(1, 2, 3))
+        A, B, _ = case.make()
+        dA, dB = A.cuda(), B.cuda()
+        dC = torch.full((case.c_numel(),), float("nan"), dtype=W.TORCH_DTYPES[dtype], device="cuda")
+        mg.mgemm_run(h, "row", "row", 96, 80, 40, 1.0, dA, 40, dB, 80, 0.0, dC, 80, dtype)
+        torch.cuda.synchronize()
+        assert torch.isfinite(dC.float()).all()
+
+
+def test_degenerate_shapes(h):
+    dtype = "f32"
+    C0 = torch.arange(12, dtype=torch.float32, device="cuda").reshape(3, 4).contiguous()
+    A = torch.ones(3, 5, device="cuda")
+    B = torch.ones(5, 4, device="cuda")
+    C = C0.clone()
+    mg.mgemm_run(h, "row", "row", 0, 4, 5, 1.0, A, 5, B, 4, 2.0, C, 4, dtype)   # M = 0: no-op
+    mg.mgemm_run(h, "row", "row", 3, 0, 5, 1.0, A, 5, B, 4, 2.0, C, 4, dtype)   # N = 0: no-op
+    torch.cuda.synchronize()
+    assert torch.equal(C, C0)
+    mg.mgemm_run(h, "row", "row", 3, 4, 0, 1.0, A, 1, B, 4, 2.0, C, 4, dtype)   # K = 0: C = 2C
+    torch.cuda.synchronize()
+    assert torch.equal(C, 2 * C0)
+    C = C0.clone()
+    nanA = torch.full((3, 5), float("nan"), device="cuda")
+    mg.mgemm_run(h, "row", "row", 3, 4, 5, 0.0, nanA, 5, B, 4, -1.0, C, 4, dtype)  # alpha = 0
+    torch.cuda.synchronize()
+    assert torch.equal(C, -C0)
+    C = C0.clone()
+    mg.mgemm_run(h, "row", "row", 3, 4, 0, 1.0, None, 1, None, 4, 0.0, C, 4, dtype)  # K=0, beta=0
+    torch.cuda.synchronize()
+    assert torch.equal(C, torch.zeros_like(C0))
+
+
+def test_invalid_arguments_leave_c_untouched(h):
+    C0 = torch.arange(16, dtype=torch.float32, device="cuda")
+    A = torch.ones(16, device="cuda")
+    C = C0.clone()
+    bad = [
+        dict(M=-1), dict(lda=3), dict(ldb=3), dict(ldc=3), dict(layoutA=7), dict(dtype=9),
+        dict(C=None), dict(A=None),
+    ]
+    for b in bad:
+        kw = dict(layoutA="row", layoutB="row", M=4, N=4, K=4, alpha=1.0, A=A, lda=4, B=A, ldb=4,
+                  beta=0.0, C=C, ldc=4, dtype="f32")
+        kw.update(b)
+        with pytest.raises(mg.MgemmError) as ei:
+            mg.mgemm_run(h, kw["layoutA"], kw["layoutB"], kw["M"], kw["N"], kw["K"], kw["alpha"],
+                         kw["A"], kw["lda"], kw["B"], kw["ldb"], kw["beta"], kw["C"], kw["ldc"],
+                         kw["dtype"])
+        assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG, b
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_kernel(h, "f32_mfma", "row", "row", 4, 4, 4, 1.0, A, 4, A, 4, 0.0, C, 4, "f16")
+    assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(C, C0)
+
+
+def test_deterministic_run_to_run(h):
+    for case in (W.Case("det32", 1000, 1200, 777, "f32", seeds=(5, 6, 7)),
+                 W.Case("det16", 1024, 1280, 1000, "bf16", kindA="normal", kindB="normal",
+                        seeds=(5, 6, 7))):
+        inputs = case.make()
+        outs = [W.storage_view(P.run_gpu(h, case, inputs=inputs)[4]) for _ in range(3)]
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0]), case.name
+
+
+def test_non_default_stream(h):
+    case = W.Case("stream", 300, 200, 100, "f16", kindA="int", kindB="int", seeds=(8, 9, 10))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = P.run_gpu(h, case, stream=s)
+    P.check_bit_exact(case, *out)
+
+
+def test_unaligned_16bit_operands(h):
+    # Operands one element past a 16-byte boundary, odd leading dimensions.
+    M, N, K = 130, 70, 90
+    case = W.Case("unaligned", M, N, K, "bf16", lda=K + 1, ldb=N + 3, ldc=N + 1,
+                  kindA="int", kindB="int", seeds=(11, 12, 13))
+    A, B, _ = case.make()
+    dA = torch.empty(A.numel() + 1, dtype=A.dtype, device="cuda")
+    dB = torch.empty(B.numel() + 1, dtype=B.dtype, device="cuda")
+    dA[1:] = A.cuda()
+    dB[1:] = B.cuda()
+    Cin = P.c_initial(case, None)
+    dC = torch.empty(Cin.numel() + 1, dtype=Cin.dtype, device="cuda")
+    dC[1:] = Cin.cuda()
+    mg.mgemm_run(h, "row", "row", M, N, K, 1.0, dA.data_ptr() + 2, case.lda, dB.data_ptr() + 2,
+                 case.ldb, 0.0, dC.data_ptr() + 2, case.ldc, "bf16")
+    torch.cuda.synchronize()
+    P.check_bit_exact(case, A, B, None, Cin, dC[1:].cpu())
+
+
+def test_dispatch_choices(h):
+    def sel(case):
+        return mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
+                                      case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
+                                      case.ldc, case.dtype)
+    assert sel(W.sgemm_4096()) == "f32_mfma"
+    assert sel(W.ragged_f32()) == "f32_mfma"
+    say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
+                      + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
