@@ -31,6 +31,8 @@
 // irrelevant as long as A and B use the same assignment, which they do.
 #include "common.h"
 
+#include <type_traits>
+
 namespace mgemm {
 namespace {
 
@@ -76,9 +78,34 @@ struct TileLoader {
     static_assert(!KC || CHUNKS % NT == 0, "K-contiguous tile must split evenly");
     i32x4 v[NREG];
 
+    // FULL: the slice lies entirely inside the matrix (interior tile, whole K
+    // slice), so every load is an unconditional 16-byte load.  Keeping the
+    // edge masks out of this path matters: per-element conditional loads make
+    // the compiler wait for all outstanding loads after each of them.
+    template <bool FULL>
     __device__ __forceinline__ void fetch(const uint16_t* __restrict__ P, int64_t ld, int rlim,
                                           int klim, int tid) {
-        if constexpr (KC) {
+        if constexpr (FULL) {
+            if constexpr (KC) {
+#pragma unroll
+                for (int i = 0; i < PER_T; ++i) {
+                    const int c = tid + i * NT;
+                    const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+                    v[i] = *(const i32x4*)(P + (int64_t)r * ld + kc);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < PER_T; ++i) {
+                    const int b = tid + i * NT;
+                    const int kb = (b % (BK / 8)) * 8, rb = (b / (BK / 8)) * 8;
+                    if (b < R / 8 * (BK / 8)) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[i * 8 + j] = *(const i32x4*)(P + (int64_t)(kb + j) * ld + rb);
+                    }
+                }
+            }
+        } else if constexpr (KC) {
 #pragma unroll
             for (int i = 0; i < PER_T; ++i) {
                 const int c = tid + i * NT;
@@ -193,41 +220,51 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void k_h_mfma(P
 
     const int64_t nk = (p.K + BK - 1) / BK;
     auto klim_of = [&](int64_t kt) { return (int)(p.K - kt * BK < BK ? p.K - kt * BK : BK); };
-
-    la.fetch(a_base, p.lda, mlim, klim_of(0), tid);
-    lb.fetch(b_base, p.ldb, nlim, klim_of(0), tid);
-    la.stash(As, tid);
-    lb.stash(Bs, tid);
-    __syncthreads();
-
     const int fr = lane & 31;            // fragment row within a 32-row block
     const int fk = (lane >> 5) * 8;      // this lane's 8 K elements within a 16-K step
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) {
-            la.fetch(a_base + (kt + 1) * a_kstep, p.lda, mlim, klim_of(kt + 1), tid);
-            lb.fetch(b_base + (kt + 1) * b_kstep, p.ldb, nlim, klim_of(kt + 1), tid);
-        }
-        const uint16_t* as = As + cur * BM * LDS_ROW + (wm * WTM + fr) * LDS_ROW + fk;
-        const uint16_t* bs = Bs + cur * BN * LDS_ROW + (wn * WTN + fr) * LDS_ROW + fk;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            i32x4 af[TM], bf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) af[i] = *(const i32x4*)(as + i * 32 * LDS_ROW + ks * 16);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) bf[j] = *(const i32x4*)(bs + j * 32 * LDS_ROW + ks * 16);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma<DT>(bf[j], af[i], acc[i][j]);
-        }
-        if (kt + 1 < nk) {
-            la.stash(As + (cur ^ 1) * BM * LDS_ROW, tid);
-            lb.stash(Bs + (cur ^ 1) * BN * LDS_ROW, tid);
-        }
+
+    // The whole K loop is instantiated twice: FULL for interior tiles whose
+    // every K slice is complete (unconditional 16-byte loads only), and a
+    // masked copy for edge tiles and ragged K.  Choosing once per tile keeps
+    // the two load paths from merging inside the loop, where the compiler
+    // would have to wait for the loads before the contraction.
+    auto main_loop = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        auto fetch = [&](int64_t kt) {
+            const int kl = klim_of(kt);
+            la.template fetch<FULL>(a_base + kt * a_kstep, p.lda, mlim, kl, tid);
+            lb.template fetch<FULL>(b_base + kt * b_kstep, p.ldb, nlim, kl, tid);
+        };
+        fetch(0);
+        la.stash(As, tid);
+        lb.stash(Bs, tid);
         __syncthreads();
-    }
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int cur = (int)(kt & 1);
+            if (kt + 1 < nk) fetch(kt + 1);
+            const uint16_t* as = As + cur * BM * LDS_ROW + (wm * WTM + fr) * LDS_ROW + fk;
+            const uint16_t* bs = Bs + cur * BN * LDS_ROW + (wn * WTN + fr) * LDS_ROW + fk;
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                i32x4 af[TM], bf[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) af[i] = *(const i32x4*)(as + i * 32 * LDS_ROW + ks * 16);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) bf[j] = *(const i32x4*)(bs + j * 32 * LDS_ROW + ks * 16);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j] = mfma<DT>(bf[j], af[i], acc[i][j]);
+            }
+            if (kt + 1 < nk) {
+                la.stash(As + (cur ^ 1) * BM * LDS_ROW, tid);
+                lb.stash(Bs + (cur ^ 1) * BN * LDS_ROW, tid);
+            }
+            __syncthreads();
+        }
+    };
+    if (mlim == BM && nlim == BN && p.K % BK == 0) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
 
     // Epilogue: lane holds C(m, n..n+3) for m = fr, n = 8q + 4*(lane/32).
     uint16_t* C = (uint16_t*)p.C;

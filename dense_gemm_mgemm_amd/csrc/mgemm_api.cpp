@@ -79,6 +79,7 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_256x192:
     case MGEMM_KERNEL_H_128x128: return mgemm::h_mfma_supports(p, (int)k);
     case MGEMM_KERNEL_SKINNY: return mgemm::skinny_supports(p);
+    case MGEMM_KERNEL_H_PP_256: return mgemm::h_pp_supports(p);
     default: return false;
     }
 }
@@ -87,6 +88,15 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
 mgemm_kernel_t choose(const Problem& p) {
     if (p.dtype == mgemm::F32) return MGEMM_KERNEL_F32_MFMA;
     if (p.M <= 64 && mgemm::skinny_supports(p)) return MGEMM_KERNEL_SKINNY;
+    // Large NN grids that fill the chip several times over: the ping-pong
+    // kernel (measured faster there; on one wave of tiles the 256x192 tile of
+    // the register-staged kernel fills the CUs better).
+    {
+        const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+        const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if (tiles256 >= 2 * slots && tiles256 % slots == 0 && mgemm::h_pp_supports(p))
+            return MGEMM_KERNEL_H_PP_256;
+    }
     // 16-bit: pick the tile whose grid fills the CUs best, preferring the
     // larger tile (more reuse per byte staged) when the fill is equal.
     const mgemm_kernel_t order[3] = {MGEMM_KERNEL_H_256x256, MGEMM_KERNEL_H_256x192,
@@ -118,6 +128,7 @@ mgemm_status_t launch(const Problem& p, mgemm_kernel_t k, hipStream_t s) {
     case MGEMM_KERNEL_H_256x192:
     case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)k, s); break;
     case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
+    case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
@@ -221,6 +232,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_256x192: return "h_mfma_256x192";
     case MGEMM_KERNEL_H_128x128: return "h_mfma_128x128";
     case MGEMM_KERNEL_SKINNY: return "skinny";
+    case MGEMM_KERNEL_H_PP_256: return "h_pp_256x256";
     default: return "unknown";
     }
 }

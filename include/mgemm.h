@@ -61,7 +61,8 @@ typedef enum {
     MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles */
     MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
     MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
-    MGEMM_KERNEL_COUNT = 7
+    MGEMM_KERNEL_H_PP_256 = 7,   /* FP16/BF16 NN, 256x256 tiles, 8-wave ping-pong, direct-to-LDS */
+    MGEMM_KERNEL_COUNT = 8
 } mgemm_kernel_t;
 
 typedef struct mgemm_handle_s* mgemm_handle_t;
