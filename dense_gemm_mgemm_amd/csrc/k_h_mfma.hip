@@ -369,7 +369,5 @@ hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-bool skinny_supports(const Problem&) { return false; }
-hipError_t launch_skinny(const Problem&, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace mgemm
