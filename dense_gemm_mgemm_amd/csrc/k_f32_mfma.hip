@@ -166,3 +166,183 @@ hipError_t launch_f32_mfma(const Problem& p, hipStream_t s) {
 }
 
 }  // namespace mgemm
+
+// ---------------------------------------------------------------------------
+// Fast FP32 path for the canonical NN problem with 16-byte aligned operands
+// (A' K-contiguous, B' N-contiguous, lda % 4 == 0, ldb % 4 == 0, 16-byte
+// aligned bases, N % 4 == 0, K % BK == 0).
+//
+//  * Global loads are 16 bytes per lane (4 floats); edge rows/columns of a
+//    tile are read from the last valid row/4-column chunk instead of being
+//    masked (their results are never stored), so the K loop has no
+//    per-element conditions.
+//  * A is kept in LDS as [m][k] rows of BK+4 floats, written with one
+//    16-byte store per load; B as [k][n] rows of BN+4 floats.  The MFMA only
+//    needs A and B to agree on which k each (lane-half, step) stands for, so
+//    lane-half g at step s uses k = g*BK/2 + s: a lane then reads its BK/2
+//    consecutive A values with 16-byte LDS reads, and the 20-float row
+//    stride keeps those reads free of bank conflicts.
+// ---------------------------------------------------------------------------
+namespace mgemm {
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int BM, int BN, int BK, int WM, int WN, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int AROW = BK + 4, BROW = BN + 4;            // padded LDS rows (floats)
+    constexpr int ACH = BM * BK / 4, BCH = BK * BN / 4;     // 16-byte chunks per slice
+    constexpr int LA = ACH / NT, LB = BCH / NT;
+    constexpr int HALF = BK / 2;                            // k values per lane-half per slice
+    static_assert(LA * NT == ACH && LB * NT == BCH, "tile must split evenly");
+    static_assert(HALF % 4 == 0, "BK must be a multiple of 8");
+
+    __shared__ __align__(16) float As[2][BM * AROW];
+    __shared__ __align__(16) float Bs[2][BK * BROW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    int tmi, tni;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+
+    const float* __restrict__ A = (const float*)p.A;
+    const float* __restrict__ B = (const float*)p.B;
+
+    // Per-thread 16-byte chunks (fixed across K slices).
+    const float* a_src[LA];
+    int a_dst[LA];
+#pragma unroll
+    for (int r = 0; r < LA; ++r) {
+        const int c = tid + r * NT;
+        const int mi = c / (BK / 4), kc = (c % (BK / 4)) * 4;
+        const int mm = mi < mlim ? mi : mlim - 1;
+        a_src[r] = A + (m0 + mm) * p.lda + kc;
+        a_dst[r] = mi * AROW + kc;
+    }
+    const float* b_src[LB];
+    int b_dst[LB];
+#pragma unroll
+    for (int r = 0; r < LB; ++r) {
+        const int c = tid + r * NT;
+        const int ki = c / (BN / 4), nc = (c % (BN / 4)) * 4;
+        const int nn = nc + 4 <= nlim ? nc : nlim - 4;
+        b_src[r] = B + (int64_t)ki * p.ldb + n0 + nn;
+        b_dst[r] = ki * BROW + nc;
+    }
+    const int64_t b_kstep = (int64_t)BK * p.ldb;
+
+    f32x4v ra[LA], rb[LB];
+    auto fetch = [&](int64_t kt) {
+#pragma unroll
+        for (int r = 0; r < LA; ++r) ra[r] = *(const f32x4v*)(a_src[r] + kt * BK);
+#pragma unroll
+        for (int r = 0; r < LB; ++r) rb[r] = *(const f32x4v*)(b_src[r] + kt * b_kstep);
+    };
+    auto stash = [&](int slot) {
+#pragma unroll
+        for (int r = 0; r < LA; ++r) *(f32x4v*)(&As[slot][a_dst[r]]) = ra[r];
+#pragma unroll
+        for (int r = 0; r < LB; ++r) *(f32x4v*)(&Bs[slot][b_dst[r]]) = rb[r];
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+    const int64_t nk = p.K / BK;
+    const int lrow = lane >> 5, lcol = lane & 31;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        if (kt + 1 < nk) fetch(kt + 1);
+        const float* as = &As[cur][(wm * WTM + lcol) * AROW + lrow * HALF];
+        const float* bs = &Bs[cur][(lrow * HALF) * BROW + wn * WTN + lcol];
+#pragma unroll
+        for (int s0 = 0; s0 < HALF; s0 += 4) {
+            f32x4v a4[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a4[i] = *(const f32x4v*)(as + i * 32 * AROW + s0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float b[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) b[j] = bs[(s0 + s) * BROW + j * 32];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[i][s], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (kt + 1 < nk) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    float* C = (float*)p.C;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int ni = wn * WTN + j * 32 + lcol;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int mi = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
+                if (mi < mlim && ni < nlim) {
+                    const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
+                    float v = p.alpha * acc[i][j][r];
+                    if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
+                    C[idx] = v;
+                }
+            }
+        }
+    }
+}
+
+// Two instantiations: a 256x256x32 tile on 16 waves (one workgroup per CU)
+// for grids that fill the chip, and a 128x128x16 tile on 4 waves (two
+// workgroups per CU) for smaller grids.
+struct BigCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 4, OCC = 1; };
+struct SmallCfg { static constexpr int BM = 128, BN = 128, BK = 16, WM = 2, WN = 2, OCC = 2; };
+
+template <class CF>
+bool fast_supports(const Problem& p) {
+    if (p.dtype != F32 || !p.a_kc || p.b_kc) return false;
+    if (p.K <= 0 || p.K % CF::BK != 0 || p.N % 4 != 0) return false;
+    if (p.lda % 4 != 0 || p.ldb % 4 != 0) return false;
+    if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
+    const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
+    return tiles > 0 && tiles <= 0x7fffffff;
+}
+template <class CF>
+hipError_t fast_launch(const Problem& p, hipStream_t s) {
+    const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
+    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC>),
+                       dim3((unsigned)tiles), dim3(64 * CF::WM * CF::WN), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool f32_fast_supports(const Problem& p, bool big) {
+    return big ? fast_supports<BigCfg>(p) : fast_supports<SmallCfg>(p);
+}
+
+hipError_t launch_f32_fast(const Problem& p, bool big, hipStream_t s) {
+    return big ? fast_launch<BigCfg>(p, s) : fast_launch<SmallCfg>(p, s);
+}
+
+}  // namespace mgemm

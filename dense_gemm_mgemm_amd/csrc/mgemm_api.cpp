@@ -80,13 +80,30 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_128x128: return mgemm::h_mfma_supports(p, (int)k);
     case MGEMM_KERNEL_SKINNY: return mgemm::skinny_supports(p);
     case MGEMM_KERNEL_H_PP_256: return mgemm::h_pp_supports(p);
+    case MGEMM_KERNEL_F32_FAST: return mgemm::f32_fast_supports(p, true);
+    case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
     default: return false;
     }
 }
 
 // Kernel choice for a canonical problem.
 mgemm_kernel_t choose(const Problem& p) {
-    if (p.dtype == mgemm::F32) return MGEMM_KERNEL_F32_MFMA;
+    const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+    // Fraction of the CU-time a grid of bm x bn tiles spends on useful
+    // outputs (wave quantisation and ragged-edge padding count as waste).
+    auto fill = [&](int bm, int bn, int per_cu) {
+        const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+        const int64_t cap = slots * per_cu;
+        const int64_t waves = (tiles + cap - 1) / cap;
+        return (double)p.M * (double)p.N / ((double)waves * cap * bm * bn);
+    };
+    if (p.dtype == mgemm::F32) {
+        const bool big = mgemm::f32_fast_supports(p, true), small = mgemm::f32_fast_supports(p, false);
+        if (big && (!small || fill(256, 256, 1) >= fill(128, 128, 2) * 0.9))
+            return MGEMM_KERNEL_F32_FAST;
+        if (small) return MGEMM_KERNEL_F32_FAST_128;
+        return MGEMM_KERNEL_F32_MFMA;
+    }
     if (p.M <= 64 && mgemm::skinny_supports(p)) return MGEMM_KERNEL_SKINNY;
     // Large NN grids that fill the chip several times over: the ping-pong
     // kernel (measured faster there; on one wave of tiles the 256x192 tile of
@@ -129,6 +146,8 @@ mgemm_status_t launch(const Problem& p, mgemm_kernel_t k, hipStream_t s) {
     case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)k, s); break;
     case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
     case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
+    case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
+    case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
@@ -233,6 +252,8 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_128x128: return "h_mfma_128x128";
     case MGEMM_KERNEL_SKINNY: return "skinny";
     case MGEMM_KERNEL_H_PP_256: return "h_pp_256x256";
+    case MGEMM_KERNEL_F32_FAST: return "f32_fast";
+    case MGEMM_KERNEL_F32_FAST_128: return "f32_fast_128";
     default: return "unknown";
     }
 }

@@ -56,13 +56,15 @@ typedef enum {
 typedef enum {
     MGEMM_KERNEL_AUTO = 0,
     MGEMM_KERNEL_GENERAL = 1,    /* any dtype/layout/alignment, VALU FMA, 64x64 tiles */
-    MGEMM_KERNEL_F32_MFMA = 2,   /* FP32 on v_mfma_f32_32x32x2_f32, 128x128 tiles */
+    MGEMM_KERNEL_F32_MFMA = 2,   /* FP32 on v_mfma_f32_32x32x2_f32, 128x128 tiles, any layout */
     MGEMM_KERNEL_H_256x256 = 3,  /* FP16/BF16 MFMA, 256x256 tiles */
     MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles */
     MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
     MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
     MGEMM_KERNEL_H_PP_256 = 7,   /* FP16/BF16 NN, 256x256 tiles, 8-wave ping-pong, direct-to-LDS */
-    MGEMM_KERNEL_COUNT = 8
+    MGEMM_KERNEL_F32_FAST = 8,   /* FP32 NN, 16-byte aligned operands, 256x256x32 tiles, 16 waves */
+    MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
+    MGEMM_KERNEL_COUNT = 10
 } mgemm_kernel_t;
 
 typedef struct mgemm_handle_s* mgemm_handle_t;

@@ -1,0 +1,54 @@
+"""Checks on the generated gfx950 code that the source relies on.
+
+The direct-to-LDS copies are issued through inline asm that sets m0 and
+declares it clobbered.  m0 is a reserved register for the compiler, so that
+is only sound if the compiler itself keeps no value in m0 in these kernels:
+every m0 access in their code must be one of ours.  Also checks that the
+kernels that must not spill registers do not.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "dense_gemm_mgemm_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc"
+
+
+def device_asm(src, tmp_path):
+    out = tmp_path / (os.path.basename(src) + ".s")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-S", "-O3",
+                    "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-I" + os.path.join(ROOT, "include"), src, "-o", str(out)],
+                   check=True, capture_output=True)
+    return out.read_text()
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip"])
+def test_m0_only_written_by_our_copies(name, tmp_path):
+    text = device_asm(os.path.join(CSRC, name), tmp_path)
+    lines = [l.strip() for l in text.splitlines() if re.search(r"\bm0\b", l) and not l.strip().startswith(";")]
+    assert lines, "expected the direct-to-LDS copies to set m0"
+    body = [l.strip() for l in text.splitlines()]
+    for idx, l in enumerate(body):
+        if re.search(r"\bm0\b", l) and not l.startswith(";"):
+            assert l.startswith("s_mov_b32 m0,"), "unexpected m0 use: " + l
+            # our asm: s_mov_b32 m0 / s_nop 0 / global_load_lds_dwordx4
+            assert body[idx + 1] == "s_nop 0" and body[idx + 2].startswith("global_load_lds_dwordx4"), l
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+# k_h_mfma.hip is left out: its 256x256 register-staged instantiations hold
+# 256 accumulators plus a full slice of prefetch registers and spill one VGPR.
+@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip"])
+def test_no_register_spills(name, tmp_path):
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-c", "-O3",
+                        "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-Rpass-analysis=kernel-resource-usage", "-I" + os.path.join(ROOT, "include"),
+                        os.path.join(CSRC, name), "-o", str(tmp_path / "k.o")],
+                       capture_output=True, text=True, check=True)
+    spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", r.stderr)]
+    assert spills and max(spills) == 0, r.stderr[-2000:]

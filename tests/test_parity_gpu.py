@@ -266,7 +266,7 @@ def test_dispatch_choices(h):
         return mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
                                       case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
                                       case.ldc, case.dtype)
-    assert sel(W.sgemm_4096()) == "f32_mfma"
+    assert sel(W.sgemm_4096()) == "f32_fast"
     assert sel(W.ragged_f32()) == "f32_mfma"
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
