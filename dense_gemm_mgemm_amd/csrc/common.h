@@ -111,6 +111,8 @@ bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_h_pp(const Problem& p, hipStream_t s);
 bool h_pp_supports(const Problem& p);
+hipError_t launch_h_dma(const Problem& p, hipStream_t s);
+bool h_dma_supports(const Problem& p);
 bool skinny_supports(const Problem& p);
 
 }  // namespace mgemm

@@ -1,0 +1,304 @@
+// FP16/BF16 GEMM for gfx950: 256x256 output tiles, four waves of 128x128,
+// operands copied straight into a four-slot LDS ring, one workgroup barrier
+// per K slice.  The fast path for the canonical NN problem (A' K-contiguous,
+// B' N-contiguous).
+//
+// Budget that shaped it (measured on MI355X): a CU pulls about 40 B/clk from
+// L2 when every CU does, and a 256x256 tile needs 32 B/clk at the matrix-core
+// peak, so the tile is as large as the registers allow (each wave holds a
+// 128x128 accumulator, 256 AGPRs).  ds_read_b128 reads deliver about twice the
+// bytes per clock of ds_read_b64_tr_b16, and a 128x128 wave tile reads 64 B/clk
+// of fragments at peak, half of what a 64x128 tile would.
+//
+// Schedule of slice j (K = 32 per slice, 2 MFMA K-steps "ks"):
+//   1. wait until this wave's copies of slice j+1 have landed, workgroup
+//      barrier: slice j+1 is now visible to every wave, and every wave is done
+//      reading slice j-1, so its slot can be refilled;
+//   2. request slice j+3 into that slot (eight 1 KiB copies per wave, issued
+//      in two groups between MFMA groups);
+//   3. read the (j, ks=1) fragments, MFMAs of (j, ks=0);
+//   4. read the (j+1, ks=0) fragments, MFMAs of (j, ks=1).
+// Fragments are read one K-step ahead of the MFMAs that use them, so the
+// matrix core never waits for LDS at a slice boundary.  This is the two-slot
+// pipeline of "Chapter 5: Operators and Runtime" (section 5.3.2) stretched
+// to four slots, with the next slot requested n-1 blocks ahead.
+//
+// LDS layouts, copies and fragment reads are those of k_h_pp.hip (same XOR
+// swizzles; B fragments via ds_read_b64_tr_b16); rows past M and columns past
+// N of an edge tile are read from the last valid row/chunk and never stored.
+// Restrictions (host-checked): A' K-contiguous, B' N-contiguous, K % 32 == 0,
+// N % 8 == 0, lda and ldb multiples of 8, 16-byte aligned bases.
+#include "common.h"
+
+namespace mgemm {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, SLOTS = 4, AHEAD = 3;
+constexpr int A_ROW = BK * 2, B_ROW = BN * 2;
+constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;   // 16 KiB each
+constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
+constexpr int COPIES = 8;                                   // 1 KiB copies per wave per slice
+constexpr int TM = 4, TN = 4;                               // 32x32 blocks per wave
+
+__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int b_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float v) {
+    if constexpr (DT == F16) return f32_to_f16_bits(v);
+    else return f32_to_bf16_bits(v);
+}
+template <int DT>
+__device__ __forceinline__ float from_bits(uint16_t b) {
+    if constexpr (DT == F16) return f16_bits_to_f32(b);
+    else return bf16_bits_to_f32(b);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l); see
+// k_h_pp.hip for why it is inline asm.
+__device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void fence_sched() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void slice_barrier() {
+    fence_sched();
+    __builtin_amdgcn_s_barrier();
+    fence_sched();
+}
+
+struct Frags {
+    i32x4 a[TM];
+    i32x4 b[TN];
+};
+
+template <int DT>
+__global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    int tmi, tni;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const uint16_t* __restrict__ A = (const uint16_t*)p.A;
+    const uint16_t* __restrict__ B = (const uint16_t*)p.B;
+
+    // Copies of this wave: A rows [64w, 64w+64) (four copies of 16 rows),
+    // B K-rows [8w, 8w+8) (four copies of 2 rows).
+    const uint16_t* src[COPIES];
+    int dst[COPIES];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wave + 16 * i + (lane >> 2);
+        const int c = (lane & 3) ^ a_swz(r);
+        const int rr = r < mlim ? r : mlim - 1;
+        src[i] = A + (m0 + rr) * p.lda + 8 * c;
+        dst[i] = (64 * wave + 16 * i) * A_ROW;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = 8 * wave + 2 * i + (lane >> 5);
+        int c = (lane & 31) ^ b_swz(k);
+        const int cmax = (nlim >> 3) - 1;
+        c = c <= cmax ? c : cmax;
+        src[4 + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
+        dst[4 + i] = A_BYTES + (8 * wave + 2 * i) * B_ROW;
+    }
+    const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    auto issue = [&](int64_t s, int first, int count) {
+        const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
+#pragma unroll
+        for (int i = first; i < first + count; ++i)
+            copy_to_lds(src[i] + s * (i < 4 ? a_kstep : b_kstep), base + dst[i]);
+    };
+
+    // Fragment read offsets within a slot.
+    int a_off[TM][2];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int r = 128 * wm + 32 * tm + (lane & 31);
+            const int c = 2 * ks + (lane >> 5);
+            a_off[tm][ks] = r * A_ROW + ((c ^ a_swz(r)) << 4);
+        }
+    int b_off[TN][2][2];
+    {
+        const int q = lane >> 4, t = lane & 15;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = ks * 16 + 8 * (q >> 1) + 4 * h + (t >> 2);
+                    const int n = 128 * wn + 32 * tn + 16 * (q & 1) + 4 * (t & 3);
+                    b_off[tn][ks][h] = A_BYTES + k * B_ROW + (((n >> 3) ^ b_swz(k)) << 4) + ((n & 7) << 1);
+                }
+    }
+    auto read = [&](Frags& f, int64_t s, int ks) {
+        const unsigned char* base = smem + (int)(s % SLOTS) * SLOT_BYTES;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][1]));
+            const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+            f.b[tn] = i32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma<DT>(f.b[tn], f.a[tm], acc[tm][tn]);
+    };
+
+    const int64_t nk = p.K / BK;
+    // Prologue: request slices 0..2, make slice 0 visible, read (0, ks=0).
+    const int64_t npro = nk < AHEAD ? nk : AHEAD;
+    for (int64_t s = 0; s < npro; ++s) issue(s, 0, COPIES);
+    if (npro >= 3) wait_vm<2 * COPIES>();
+    else if (npro == 2) wait_vm<COPIES>();
+    else wait_vm<0>();
+    slice_barrier();
+    Frags f0, f1;
+    read(f0, 0, 0);
+
+    for (int64_t j = 0; j < nk; ++j) {
+        // 1. own copies of slice j+1 landed (only j+2 may still be in flight),
+        //    then publish slice j+1 and retire slot (j-1).
+        if (j + 1 < nk) {
+            if (j + 2 < nk) wait_vm<COPIES>();
+            else wait_vm<0>();
+        }
+        slice_barrier();
+        const bool more = j + AHEAD < nk;
+        // 2./3. first half of the next request, (j, ks=1) fragments, MFMAs (j, ks=0).
+        if (more) issue(j + AHEAD, 0, COPIES / 2);
+        read(f1, j, 1);
+        mma(f0);
+        fence_sched();
+        // 4. second half of the request, (j+1, ks=0) fragments, MFMAs (j, ks=1).
+        if (more) issue(j + AHEAD, COPIES / 2, COPIES / 2);
+        if (j + 1 < nk) read(f0, j + 1, 0);
+        mma(f1);
+        fence_sched();
+    }
+
+    // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
+    uint16_t* C = (uint16_t*)p.C;
+    const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
+    const int fr = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int mi = 128 * wm + 32 * tm + fr;
+        if (mi >= mlim) continue;
+        uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ni = 128 * wn + 32 * tn + 8 * q + nq;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[tm][tn][4 * q + e];
+                if (vec_ok && ni + 4 <= nlim) {
+                    uint32_t* d = (uint32_t*)(crow + ni);
+                    if (p.beta != 0.f) {
+                        const uint32_t c0 = d[0], c1 = d[1];
+                        v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
+                        v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
+                        v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
+                        v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
+                    }
+                    const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+                    const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+                    *(uint2*)d = make_uint2(w0, w1);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (ni + e < nlim) {
+                            float x = v[e];
+                            if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[ni + e]), x);
+                            crow[ni + e] = to_bits<DT>(x);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int DT>
+hipError_t launch_dt(const Problem& p, hipStream_t s) {
+    auto kern = k_h_dma<DT>;
+    const size_t lds = (size_t)SLOTS * SLOT_BYTES;
+    static bool attr_set = false;     // benign race: every caller sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool h_dma_supports(const Problem& p) {
+    if (p.dtype != F16 && p.dtype != BF16) return false;
+    if (!p.a_kc || p.b_kc) return false;
+    if (p.K <= 0 || p.K % BK != 0 || p.N % 8 != 0) return false;
+    if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
+    if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    return tiles > 0 && tiles <= 0x7fffffff;
+}
+
+hipError_t launch_h_dma(const Problem& p, hipStream_t s) {
+    return p.dtype == F16 ? launch_dt<F16>(p, s) : launch_dt<BF16>(p, s);
+}
+
+}  // namespace mgemm

@@ -82,6 +82,7 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_PP_256: return mgemm::h_pp_supports(p);
     case MGEMM_KERNEL_F32_FAST: return mgemm::f32_fast_supports(p, true);
     case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
+    case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p);
     default: return false;
     }
 }
@@ -105,33 +106,25 @@ mgemm_kernel_t choose(const Problem& p) {
         return MGEMM_KERNEL_F32_MFMA;
     }
     if (p.M <= 64 && mgemm::skinny_supports(p)) return MGEMM_KERNEL_SKINNY;
-    // Large NN grids that fill the chip several times over: the ping-pong
-    // kernel (measured faster there; on one wave of tiles the 256x192 tile of
-    // the register-staged kernel fills the CUs better).
-    {
-        const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
-        const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if (tiles256 >= 2 * slots && tiles256 % slots == 0 && mgemm::h_pp_supports(p))
-            return MGEMM_KERNEL_H_PP_256;
-    }
-    // 16-bit: pick the tile whose grid fills the CUs best, preferring the
-    // larger tile (more reuse per byte staged) when the fill is equal.
-    const mgemm_kernel_t order[3] = {MGEMM_KERNEL_H_256x256, MGEMM_KERNEL_H_256x192,
-                                     MGEMM_KERNEL_H_128x128};
-    const int bm[3] = {256, 256, 128}, bn[3] = {256, 192, 128};
+    // 16-bit: score each variant by the fraction of CU-time its grid spends
+    // on useful outputs (wave quantisation and the padding of ragged edge
+    // tiles count as waste) times its measured per-CU speed relative to the
+    // register-staged kernel.  The four-wave direct-to-LDS kernel runs a full
+    // 256x256 tile about 1.4x as fast (1024 NN tiles: 2.12 vs 2.58 ms), so it
+    // wins even a grid that leaves a quarter of the CUs idle.
+    struct Cand { mgemm_kernel_t k; int bm, bn; double speed; };
+    const Cand cands[4] = {{MGEMM_KERNEL_H_DMA_256, 256, 256, 1.4},
+                           {MGEMM_KERNEL_H_256x256, 256, 256, 1.0},
+                           {MGEMM_KERNEL_H_256x192, 256, 192, 1.0},
+                           {MGEMM_KERNEL_H_128x128, 128, 128, 1.0}};
     mgemm_kernel_t best = MGEMM_KERNEL_GENERAL;
     double best_score = -1.0;
-    for (int v = 0; v < 3; ++v) {
-        if (!mgemm::h_mfma_supports(p, (int)order[v])) continue;
-        const int64_t tiles = ((p.M + bm[v] - 1) / bm[v]) * ((p.N + bn[v] - 1) / bn[v]);
-        const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
-        const int64_t waves = (tiles + slots - 1) / slots;
-        // Useful work over the CU-time the grid occupies, counting the padding
-        // of ragged edge tiles as waste.
-        const double useful = (double)p.M * (double)p.N;
-        const double occupied = (double)waves * slots * bm[v] * bn[v];
-        double score = useful / occupied;
-        if (score > best_score + 1e-9) { best_score = score; best = order[v]; }
+    for (const Cand& c : cands) {
+        const bool ok = c.k == MGEMM_KERNEL_H_DMA_256 ? mgemm::h_dma_supports(p)
+                                                      : mgemm::h_mfma_supports(p, (int)c.k);
+        if (!ok) continue;
+        const double score = fill(c.bm, c.bn, 1) * c.speed;
+        if (score > best_score + 1e-9) { best_score = score; best = c.k; }
     }
     return best;
 }
@@ -148,6 +141,7 @@ mgemm_status_t launch(const Problem& p, mgemm_kernel_t k, hipStream_t s) {
     case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
     case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
+    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
@@ -254,6 +248,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_PP_256: return "h_pp_256x256";
     case MGEMM_KERNEL_F32_FAST: return "f32_fast";
     case MGEMM_KERNEL_F32_FAST_128: return "f32_fast_128";
+    case MGEMM_KERNEL_H_DMA_256: return "h_dma_256x256";
     default: return "unknown";
     }
 }

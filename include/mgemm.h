@@ -64,7 +64,8 @@ typedef enum {
     MGEMM_KERNEL_H_PP_256 = 7,   /* FP16/BF16 NN, 256x256 tiles, 8-wave ping-pong, direct-to-LDS */
     MGEMM_KERNEL_F32_FAST = 8,   /* FP32 NN, 16-byte aligned operands, 256x256x32 tiles, 16 waves */
     MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
-    MGEMM_KERNEL_COUNT = 10
+    MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 NN, 256x256 tiles, 4 waves of 128x128, direct-to-LDS ring */
+    MGEMM_KERNEL_COUNT = 11
 } mgemm_kernel_t;
 
 typedef struct mgemm_handle_s* mgemm_handle_t;
