@@ -14,14 +14,24 @@
 //   1. wait until this wave's copies of slice j+1 have landed, workgroup
 //      barrier: slice j+1 is now visible to every wave, and every wave is done
 //      reading slice j-1, so its slot can be refilled;
-//   2. request slice j+3 into that slot (eight 1 KiB copies per wave, issued
-//      in two groups between MFMA groups);
-//   3. read the (j, ks=1) fragments, MFMAs of (j, ks=0);
-//   4. read the (j+1, ks=0) fragments, MFMAs of (j, ks=1).
+//   2. request slice j+3 into that slot (eight 1 KiB copies per wave);
+//   3. MFMAs of (j, ks=0) while reading the (j, ks=1) fragments;
+//   4. MFMAs of (j, ks=1) while reading the (j+1, ks=0) fragments.
 // Fragments are read one K-step ahead of the MFMAs that use them, so the
-// matrix core never waits for LDS at a slice boundary.  This is the two-slot
-// pipeline of "Chapter 5: Operators and Runtime" (section 5.3.2) stretched
-// to four slots, with the next slot requested n-1 blocks ahead.
+// matrix core never waits for LDS at a slice boundary.  Within a K-step one
+// instruction group follows each MFMA (a copy every fourth MFMA, one fragment
+// read after each of the first eight), and the order is pinned with
+// scheduling barriers: with one wave per SIMD every stall of the issuing wave
+// is a stall of the matrix core, and bursts of copies or reads back up the
+// memory and LDS queues (measured: 58 -> 40 cycles per 32-cycle MFMA).
+// This is the two-slot pipeline of "Chapter 5: Operators and Runtime"
+// (section 5.3.2) stretched to four slots, with the next slot requested n-1
+// blocks ahead.
+//
+// Under this load the chip is power-limited: the shader clock falls from
+// 2.4 GHz to about 1.5-1.9 GHz when all 256 CUs issue MFMAs, so the
+// published peak is out of reach and fewer stalls partly turn into a lower
+// clock.
 //
 // LDS layouts, copies and fragment reads are those of k_h_pp.hip (same XOR
 // swizzles; B fragments via ds_read_b64_tr_b16); rows past M and columns past
@@ -135,11 +145,9 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     }
     const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-    auto issue = [&](int64_t s, int first, int count) {
-        const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
-#pragma unroll
-        for (int i = first; i < first + count; ++i)
-            copy_to_lds(src[i] + s * (i < 4 ? a_kstep : b_kstep), base + dst[i]);
+    auto copy = [&](int s, int i) {
+        const unsigned base = lds0 + (unsigned)(s & (SLOTS - 1)) * SLOT_BYTES;
+        copy_to_lds(src[i] + (int64_t)s * (i < 4 ? a_kstep : b_kstep), base + dst[i]);
     };
 
     // Fragment read offsets within a slot.
@@ -166,19 +174,18 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                     b_off[tn][ks][h] = A_BYTES + k * B_ROW + (((n >> 3) ^ b_swz(k)) << 4) + ((n & 7) << 1);
                 }
     }
-    auto read = [&](Frags& f, int64_t s, int ks) {
-        const unsigned char* base = smem + (int)(s % SLOTS) * SLOT_BYTES;
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][1]));
-            const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
-            f.b[tn] = i32x4{l2.x, l2.y, h2.x, h2.y};
-        }
+    auto read_a = [&](Frags& f, int s, int ks, int tm) {
+        const unsigned char* base = smem + (s & (SLOTS - 1)) * SLOT_BYTES;
+        f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
+    };
+    auto read_b = [&](Frags& f, int s, int ks, int tn) {
+        const unsigned char* base = smem + (s & (SLOTS - 1)) * SLOT_BYTES;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][1]));
+        const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+        f.b[tn] = i32x4{l2.x, l2.y, h2.x, h2.y};
     };
 
     f32x16 acc[TM][TN];
@@ -186,43 +193,64 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-    auto mma = [&](const Frags& f) {
+
+    // One K-step: the 16 MFMAs on `use`, with the fragment reads that fill
+    // `nxt` (slice rs, k-step rks) and four copies of slice cs (copy indices
+    // c0..c0+3) spread between them, one instruction group after each MFMA.
+    // Reads come in the order the next K-step consumes them (A0, B0..B3,
+    // A1..A3), so its first MFMAs wait on the oldest reads only.
+    auto kstep = [&](const Frags& use, Frags& nxt, bool do_read, int rs, int rks,
+                     bool do_copy, int cs, int c0) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma<DT>(f.b[tn], f.a[tm], acc[tm][tn]);
+        for (int i = 0; i < TM * TN; ++i) {
+            const int tm = i >> 2, tn = i & 3;
+            acc[tm][tn] = mfma<DT>(use.b[tn], use.a[tm], acc[tm][tn]);
+            if (do_copy && (i & 3) == 0) copy(cs, c0 + (i >> 2));
+            if (do_read) {
+                if (i == 1) read_a(nxt, rs, rks, 0);
+                if (i >= 2 && i <= 5) read_b(nxt, rs, rks, i - 2);
+                if (i >= 6 && i <= 8) read_a(nxt, rs, rks, i - 5);
+            }
+            fence_sched();
+        }
     };
 
-    const int64_t nk = p.K / BK;
+    const int nk = (int)(p.K / BK);
     // Prologue: request slices 0..2, make slice 0 visible, read (0, ks=0).
-    const int64_t npro = nk < AHEAD ? nk : AHEAD;
-    for (int64_t s = 0; s < npro; ++s) issue(s, 0, COPIES);
+    const int npro = nk < AHEAD ? nk : AHEAD;
+    for (int s = 0; s < npro; ++s)
+        for (int i = 0; i < COPIES; ++i) copy(s, i);
     if (npro >= 3) wait_vm<2 * COPIES>();
     else if (npro == 2) wait_vm<COPIES>();
     else wait_vm<0>();
     slice_barrier();
     Frags f0, f1;
-    read(f0, 0, 0);
+    read_a(f0, 0, 0, 0);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) read_b(f0, 0, 0, tn);
+#pragma unroll
+    for (int tm = 1; tm < TM; ++tm) read_a(f0, 0, 0, tm);
 
-    for (int64_t j = 0; j < nk; ++j) {
-        // 1. own copies of slice j+1 landed (only j+2 may still be in flight),
-        //    then publish slice j+1 and retire slot (j-1).
-        if (j + 1 < nk) {
-            if (j + 2 < nk) wait_vm<COPIES>();
-            else wait_vm<0>();
-        }
-        slice_barrier();
-        const bool more = j + AHEAD < nk;
-        // 2./3. first half of the next request, (j, ks=1) fragments, MFMAs (j, ks=0).
-        if (more) issue(j + AHEAD, 0, COPIES / 2);
-        read(f1, j, 1);
-        mma(f0);
-        fence_sched();
-        // 4. second half of the request, (j+1, ks=0) fragments, MFMAs (j, ks=1).
-        if (more) issue(j + AHEAD, COPIES / 2, COPIES / 2);
-        if (j + 1 < nk) read(f0, j + 1, 0);
-        mma(f1);
-        fence_sched();
+    // Slice j: wait for this wave's copies of slice j+1 (W = copies that may
+    // stay in flight: those of slice j+2), barrier (slice j+1 visible to all
+    // waves, slot of slice j-1 free), then K-step 0 reading (j, ks=1) and
+    // K-step 1 reading (j+1, ks=0), both carrying copies of slice j+3.
+    auto slice = [&](int j, bool more, bool next, int w) {
+        if (w == COPIES) wait_vm<COPIES>();
+        else if (w == 0) wait_vm<0>();
+        if (next) slice_barrier();
+        kstep(f0, f1, true, j, 1, more, j + AHEAD, 0);
+        kstep(f1, f0, next, j + 1, 0, more, j + AHEAD, 4);
+    };
+    int j = 0;
+    for (; j + AHEAD < nk; ++j) slice(j, true, true, COPIES);
+    for (; j < nk; ++j) {       // last (up to) three slices: no more copies
+        const bool next = j + 1 < nk;
+        if (j + 2 < nk) wait_vm<COPIES>();
+        else if (next) wait_vm<0>();
+        if (next) slice_barrier();
+        kstep(f0, f1, true, j, 1, false, 0, 0);
+        kstep(f1, f0, next, j + 1, 0, false, 0, 0);
     }
 
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
@@ -290,7 +318,7 @@ hipError_t launch_dt(const Problem& p, hipStream_t s) {
 bool h_dma_supports(const Problem& p) {
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (!p.a_kc || p.b_kc) return false;
-    if (p.K <= 0 || p.K % BK != 0 || p.N % 8 != 0) return false;
+    if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || p.N % 8 != 0) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
