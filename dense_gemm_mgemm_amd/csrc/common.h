@@ -30,6 +30,15 @@ struct Problem {
     int num_cu;
 };
 
+// Device workspace of a handle: FP32 partial results and per-block arrival
+// counters (zero between calls) for kernels that split K over workgroups.
+struct Workspace {
+    void* part;
+    int64_t part_bytes;
+    unsigned* counters;
+    int64_t ncounters;
+};
+
 // ---------------------------------------------------------------------------
 // Workgroup -> output tile.
 //
@@ -112,6 +121,9 @@ hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_h_pp(const Problem& p, hipStream_t s);
 bool h_pp_supports(const Problem& p);
 hipError_t launch_h_dma(const Problem& p, hipStream_t s);
+bool skinny_sk_supports(const Problem& p);
+int skinny_sk_splits(const Problem& p, const Workspace& ws);
+hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s);
 bool h_dma_supports(const Problem& p);
 bool skinny_supports(const Problem& p);
 

@@ -49,7 +49,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, SLOTS = 4, AHEAD = 3;
+#ifndef MGEMM_DMA_SLOTS
+#define MGEMM_DMA_SLOTS 4
+#endif
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int SLOTS = MGEMM_DMA_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
 constexpr int A_ROW = BK * 2, B_ROW = BN * 2;
 constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;   // 16 KiB each
 constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
@@ -84,6 +88,15 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// Wait until at most n slices of this wave's copies are still in flight
+// (copies complete in issue order).
+__device__ __forceinline__ void wait_slices(int n) {
+    static_assert(COPIES * 3 < 64, "vmcnt range");
+    if (n <= 0) wait_vm<0>();
+    else if (n == 1) wait_vm<COPIES>();
+    else if (n == 2) wait_vm<2 * COPIES>();
+    else wait_vm<3 * COPIES>();
+}
 // Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l); see
 // k_h_pp.hip for why it is inline asm.
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
@@ -99,6 +112,11 @@ __device__ __forceinline__ void slice_barrier() {
     __builtin_amdgcn_s_barrier();
     fence_sched();
 }
+
+template <int N>
+struct Phase {
+    static constexpr int value = N;
+};
 
 struct Frags {
     i32x4 a[TM];
@@ -146,7 +164,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
-        const unsigned base = lds0 + (unsigned)(s & (SLOTS - 1)) * SLOT_BYTES;
+        const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
         copy_to_lds(src[i] + (int64_t)s * (i < 4 ? a_kstep : b_kstep), base + dst[i]);
     };
 
@@ -175,11 +193,11 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                 }
     }
     auto read_a = [&](Frags& f, int s, int ks, int tm) {
-        const unsigned char* base = smem + (s & (SLOTS - 1)) * SLOT_BYTES;
+        const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
     };
     auto read_b = [&](Frags& f, int s, int ks, int tn) {
-        const unsigned char* base = smem + (s & (SLOTS - 1)) * SLOT_BYTES;
+        const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -198,18 +216,23 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     // `nxt` (slice rs, k-step rks) and four copies of slice cs (copy indices
     // c0..c0+3) spread between them, one instruction group after each MFMA.
     // Reads come in the order the next K-step consumes them (A0, B0..B3,
-    // A1..A3), so its first MFMAs wait on the oldest reads only.
-    auto kstep = [&](const Frags& use, Frags& nxt, bool do_read, int rs, int rks,
+    // A1..A3), so its first MFMAs wait on the oldest reads only.  Phase P
+    // shifts the groups by P MFMAs: the four waves of a workgroup leave the
+    // slice barrier together, and staggering them keeps their copies and
+    // reads from reaching the shared address and LDS queues in bursts.
+    auto kstep = [&](auto phase, const Frags& use, Frags& nxt, bool do_read, int rs, int rks,
                      bool do_copy, int cs, int c0) {
+        constexpr int P = decltype(phase)::value;
 #pragma unroll
         for (int i = 0; i < TM * TN; ++i) {
             const int tm = i >> 2, tn = i & 3;
             acc[tm][tn] = mfma<DT>(use.b[tn], use.a[tm], acc[tm][tn]);
-            if (do_copy && (i & 3) == 0) copy(cs, c0 + (i >> 2));
+            if (do_copy && i >= P && ((i - P) & 3) == 0) copy(cs, c0 + (i >> 2));
             if (do_read) {
-                if (i == 1) read_a(nxt, rs, rks, 0);
-                if (i >= 2 && i <= 5) read_b(nxt, rs, rks, i - 2);
-                if (i >= 6 && i <= 8) read_a(nxt, rs, rks, i - 5);
+                const int r = i - P;
+                if (r == 1) read_a(nxt, rs, rks, 0);
+                if (r >= 2 && r <= 5) read_b(nxt, rs, rks, r - 2);
+                if (r >= 6 && r <= 8) read_a(nxt, rs, rks, r - 5);
             }
             fence_sched();
         }
@@ -220,9 +243,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     const int npro = nk < AHEAD ? nk : AHEAD;
     for (int s = 0; s < npro; ++s)
         for (int i = 0; i < COPIES; ++i) copy(s, i);
-    if (npro >= 3) wait_vm<2 * COPIES>();
-    else if (npro == 2) wait_vm<COPIES>();
-    else wait_vm<0>();
+    wait_slices(npro - 1);
     slice_barrier();
     Frags f0, f1;
     read_a(f0, 0, 0, 0);
@@ -235,22 +256,28 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     // stay in flight: those of slice j+2), barrier (slice j+1 visible to all
     // waves, slot of slice j-1 free), then K-step 0 reading (j, ks=1) and
     // K-step 1 reading (j+1, ks=0), both carrying copies of slice j+3.
-    auto slice = [&](int j, bool more, bool next, int w) {
-        if (w == COPIES) wait_vm<COPIES>();
-        else if (w == 0) wait_vm<0>();
+    auto slice = [&](auto phase, int j, bool more, bool next, int w) {
+        if (w >= 0) wait_slices(w);
         if (next) slice_barrier();
-        kstep(f0, f1, true, j, 1, more, j + AHEAD, 0);
-        kstep(f1, f0, next, j + 1, 0, more, j + AHEAD, 4);
+        kstep(phase, f0, f1, true, j, 1, more, j + AHEAD, 0);
+        kstep(phase, f1, f0, next, j + 1, 0, more, j + AHEAD, 4);
     };
     int j = 0;
-    for (; j + AHEAD < nk; ++j) slice(j, true, true, COPIES);
+    auto main_loop = [&](auto phase) {
+        for (; j + AHEAD < nk; ++j) slice(phase, j, true, true, AHEAD - 2);
+    };
+    switch (wave & 3) {
+    case 0: main_loop(Phase<0>{}); break;
+    case 1: main_loop(Phase<1>{}); break;
+    case 2: main_loop(Phase<2>{}); break;
+    default: main_loop(Phase<3>{}); break;
+    }
     for (; j < nk; ++j) {       // last (up to) three slices: no more copies
         const bool next = j + 1 < nk;
-        if (j + 2 < nk) wait_vm<COPIES>();
-        else if (next) wait_vm<0>();
+        if (next) wait_slices(nk - j - 2);
         if (next) slice_barrier();
-        kstep(f0, f1, true, j, 1, false, 0, 0);
-        kstep(f1, f0, next, j + 1, 0, false, 0, 0);
+        kstep(Phase<0>{}, f0, f1, true, j, 1, false, 0, 0);
+        kstep(Phase<0>{}, f1, f0, next, j + 1, 0, false, 0, 0);
     }
 
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.

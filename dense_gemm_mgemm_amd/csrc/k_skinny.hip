@@ -35,7 +35,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int NW = 4, NT = 256, KS = 32, SLOTS = 4, AHEAD = 3;
+#ifndef MGEMM_SKINNY_SLOTS
+#define MGEMM_SKINNY_SLOTS 4
+#endif
+#ifndef MGEMM_SKINNY_BN
+#define MGEMM_SKINNY_BN 64
+#endif
+constexpr int NW = 4, NT = 256, KS = 32;
+constexpr int SLOTS = MGEMM_SKINNY_SLOTS, AHEAD = SLOTS - 1;   // steps in flight per wave
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
@@ -68,6 +75,16 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// Wait until at most n (<= K) steps of L copies each are still in flight.
+template <int L, int K>
+__device__ __forceinline__ void wait_steps(int n) {
+    if constexpr (K == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= K) wait_vm<K * L>();
+        else wait_steps<L, K - 1>(n);
+    }
+}
 
 __device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 template <int BN>
@@ -96,7 +113,11 @@ __global__ __launch_bounds__(NT, (BN == 32 ? 2 : 1)) void k_skinny(Problem p) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    // Column blocks in XCD-major order: blocks that split one 128-byte line
+    // of W run on the same XCD and share its L2.
+    int tmi, tni;
+    tile_of_block(blockIdx.x, gridDim.x, 1, gridDim.x, 1, tmi, tni);
+    const int64_t n0 = (int64_t)tni * BN;
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
     const int M = (int)p.M;
     const uint16_t* __restrict__ X = (const uint16_t*)p.A;   // K-contiguous
@@ -166,9 +187,7 @@ __global__ __launch_bounds__(NT, (BN == 32 ? 2 : 1)) void k_skinny(Problem p) {
     for (int64_t i = 0; i < mine; ++i) {
         // Own copies of step i complete (newer ones may stay in flight).
         const int64_t newer = (i + AHEAD - 1 < mine - 1 ? i + AHEAD - 1 : mine - 1) - i;
-        if (newer >= 2) wait_vm<2 * LOADS>();
-        else if (newer == 1) wait_vm<LOADS>();
-        else wait_vm<0>();
+        wait_steps<LOADS, AHEAD - 1>((int)newer);
         asm volatile("" ::: "memory");
         const unsigned char* base = lring + (int)(i % SLOTS) * SLOT;
         i32x4 xf[MB], wf[NB];
@@ -246,9 +265,9 @@ hipError_t launch_cfg(const Problem& p, hipStream_t s) {
 
 template <int DT>
 hipError_t launch_dt(const Problem& p, hipStream_t s) {
-    if (p.M <= 16) return launch_cfg<DT, 16, 64>(p, s);
-    if (p.M <= 32) return launch_cfg<DT, 32, 64>(p, s);
-    return launch_cfg<DT, 64, 64>(p, s);
+    if (p.M <= 16) return launch_cfg<DT, 16, MGEMM_SKINNY_BN>(p, s);
+    if (p.M <= 32) return launch_cfg<DT, 32, MGEMM_SKINNY_BN>(p, s);
+    return launch_cfg<DT, 64, MGEMM_SKINNY_BN>(p, s);
 }
 
 }  // namespace

@@ -1,0 +1,457 @@
+// Skinny-M FP16/BF16 GEMM (M <= 64) with K split across workgroups:
+// C[M x N] = X[M x K] * W[K x N], W N-contiguous, read once from HBM.
+//
+// Why a second skinny kernel.  Streaming W as 128-byte row segments (one
+// 64-column block per workgroup over the whole K range) reaches only about
+// 4.2 TB/s on MI355X even with no arithmetic at all; 512-byte segments with
+// the K range split over four workgroups reach about 5.1 TB/s (measured with
+// copy-only kernels of both shapes).  So each workgroup here owns 256 columns
+// (512-byte segments) and one of `ksplit` contiguous K ranges, which also
+// cuts the re-reads of X by four against 64-column blocks.
+//
+// Work split.  256 threads; wave w computes columns [64w, 64w+64) of the
+// block for all M rows, so the waves need no reduction among themselves.  K
+// is walked in 32-row steps through a four-slot LDS ring shared by the
+// workgroup: the waves copy each step straight from global memory into LDS
+// (global_load_lds_dwordx4, lane l's 16 bytes land at base + 16*l; W: sixteen
+// 1 KiB copies of two 512-byte rows, four per wave; X: one 1 KiB copy of 16
+// rows per 16 rows of M, by waves 0..M/16-1).  Step i+4 is requested into
+// slot i%4 once every wave has read step i (one barrier per step), so four
+// steps are in flight per workgroup.
+//
+// Split-K reduction (deterministic, no atomics on data).  With ksplit > 1
+// every workgroup stores its FP32 partial block (rows < M) to a workspace
+// owned by the handle with device-coherent stores, waits for them to
+// complete, and bumps the block's arrival counter with a device-scope atomic.
+// The workgroup that arrives last reads the other partials with
+// device-coherent loads and adds them in split order 0, 1, ..., ksplit-1,
+// whatever the arrival order, so the result does not depend on timing; it
+// then applies alpha and beta, rounds once, stores C and resets the counter
+// to zero for the next call.  Nobody waits for anybody: a workgroup that is
+// not last simply exits.  (Release/acquire fences would do the same job but
+// write back and invalidate whole L2s; measured, they doubled the run time.)
+// This is the fixed-order split-K reduction that "Chapter 5: Operators and
+// Runtime" (section 5.2.4) asks for in place of atomically accumulated
+// outputs.
+//
+// Operands and fragments as in k_skinny.hip: v_mfma_f32_16x16x32 with W^T
+// as the first operand (fragments from ds_read_b64_tr_b16), X rows as the
+// second (ds_read_b128); lane l ends up holding C(m = l%16, n = 4(l/16)+0..3)
+// of each 16x16 block.  W rows are 512 bytes; chunk c of row k sits at chunk
+// position c ^ f(k), f(k) = {0,6,10,12}[k&3] ^ 8*((k>>3)&1), which keeps every
+// transposed read free of bank conflicts.  Rows of X past M are read from row
+// M-1 and columns of W past N from the last valid chunk; neither is stored.
+#include "common.h"
+
+namespace mgemm {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NT = 256, BNS = 256, KS = 32, SLOTS = 4;
+constexpr int W_ROW = BNS * 2, W_BYTES = KS * W_ROW;   // 512 B rows, 16 KiB per step
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float v) {
+    if constexpr (DT == F16) return f32_to_f16_bits(v);
+    else return f32_to_bf16_bits(v);
+}
+template <int DT>
+__device__ __forceinline__ float from_bits(uint16_t b) {
+    if constexpr (DT == F16) return f16_bits_to_f32(b);
+    else return bf16_bits_to_f32(b);
+}
+
+__device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
+    // Inline asm keeps the compiler from draining these copies before LDS
+    // reads; completion is tracked with explicit vmcnt waits.
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Wait until at most n (<= K) steps of L copies each are still in flight.
+template <int L, int K>
+__device__ __forceinline__ void wait_steps(int n) {
+    if constexpr (K == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= K) wait_vm<K * L>();
+        else wait_steps<L, K - 1>(n);
+    }
+}
+// Device-coherent 16-byte store and load of the partial blocks: buffer
+// accesses with the device-scope cache policy (sc1), so the store writes
+// through this XCD's L2 and the load does not hit a stale line there.  A
+// partial written on one XCD and counted with a device-scope atomic is thus
+// read correctly on another, with no whole-L2 write-back or invalidation.
+// The compiler sees both (it resolves the store's register hazards and keeps
+// many loads in flight); offsets past the workspace read as zero.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int CPOL_DEVICE = 16;   // sc1
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws, off, 0, CPOL_DEVICE);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, off, 0, CPOL_DEVICE));
+}
+__device__ __forceinline__ void fence_sched() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int x_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int w_swz(int k) {
+    return ((0xCA60 >> ((k & 3) * 4)) & 15) ^ (8 * ((k >> 3) & 1));
+}
+
+struct SplitArgs {
+    float* part;        // [blocks][ksplit][MT][256] FP32 partials (ksplit > 1)
+    int part_bytes;     // workspace size (bounds the buffer accesses)
+    unsigned* cnt;      // [blocks] arrival counters, zero between calls
+    int ksplit;         // K ranges per column block
+    int per;            // K steps per range (the last range may be shorter)
+};
+
+template <int DT, int MT>
+__global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
+    constexpr int MB = MT / 16;
+    constexpr int X_BYTES = MT * KS * 2;
+    constexpr int SLOT = W_BYTES + X_BYTES;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int last_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool has_x = w < MB;           // waves 0..MB-1 also copy X
+
+    // Workgroup -> (column block, K range); consecutive numbers share an XCD
+    // and a K range, so they share X rows in that XCD's L2.
+    const int blocks = (int)((p.N + BNS - 1) / BNS);
+    int tz, t;
+    tile_of_block(blockIdx.x, gridDim.x, 1, gridDim.x, 1, tz, t);
+    const int blk = t % blocks, split = t / blocks;
+    const int64_t nk = p.K / KS;
+    const int64_t s_begin = (int64_t)split * sa.per;
+    const int64_t s_end = s_begin + sa.per < nk ? s_begin + sa.per : nk;
+    const int nsteps = s_end > s_begin ? (int)(s_end - s_begin) : 0;
+
+    const int64_t n0 = (int64_t)blk * BNS;
+    const int nlim = (int)(p.N - n0 < BNS ? p.N - n0 : BNS);
+    const int M = (int)p.M;
+    const uint16_t* __restrict__ X = (const uint16_t*)p.A;    // K-contiguous
+    const uint16_t* __restrict__ Wt = (const uint16_t*)p.B;   // N-contiguous
+
+    // Copy sources at the first step of the range; step s adds s*KS rows.
+    const uint16_t* w_src[4];
+    int w_dst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * w + i;                     // copy j: rows 2j, 2j+1 of the step
+        const int k = 2 * j + (lane >> 5);
+        int c = (lane & 31) ^ w_swz(k);
+        const int cmax = (nlim >> 3) - 1;
+        c = c <= cmax ? c : cmax;
+        w_src[i] = Wt + (s_begin * KS + k) * p.ldb + n0 + 8 * c;
+        w_dst[i] = j * 1024;
+    }
+    const uint16_t* x_src;
+    {
+        const int r = 16 * (has_x ? w : 0) + (lane >> 2);
+        const int c = (lane & 3) ^ x_swz(r);
+        const int rr = r < M ? r : M - 1;
+        x_src = X + (int64_t)rr * p.lda + s_begin * KS + 8 * c;
+    }
+    const int x_dst = W_BYTES + (has_x ? w : 0) * 1024;
+    const int64_t w_step = (int64_t)KS * p.ldb;
+
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    auto issue = [&](int s) {
+        const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) copy_to_lds(w_src[i] + (int64_t)s * w_step, base + w_dst[i]);
+        if (has_x) copy_to_lds(x_src + (int64_t)s * KS, base + x_dst);
+    };
+    auto wait_own = [&](int n) {        // at most n of this wave's steps in flight
+        if (has_x) wait_steps<5, SLOTS - 1>(n);
+        else wait_steps<4, SLOTS - 1>(n);
+    };
+
+    // Fragment read offsets within a slot.
+    int x_off[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = 16 * mb + (lane & 15), c = lane >> 4;
+        x_off[mb] = W_BYTES + r * 64 + ((c ^ x_swz(r)) << 4);
+    }
+    int w_off[4][2];
+    {
+        const int q = lane >> 4, tt = lane & 15;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = 8 * q + 4 * h + (tt >> 2);
+                const int n = 64 * w + 16 * nb + 4 * (tt & 3);
+                w_off[nb][h] = k * W_ROW + (((n >> 3) ^ w_swz(k)) << 4) + ((n & 7) << 1);
+            }
+    }
+
+    f32x4 acc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int npro = nsteps < SLOTS ? nsteps : SLOTS;
+    for (int s = 0; s < npro; ++s) issue(s);
+    if (nsteps > 0) {
+        wait_own(npro - 1);
+        fence_sched();
+        __syncthreads();
+        fence_sched();
+    }
+    for (int i = 0; i < nsteps; ++i) {
+        const unsigned char* base = smem + (i % SLOTS) * SLOT;
+        i32x4 xf[MB], wf[4];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) xf[mb] = *(const i32x4*)(base + x_off[mb]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + w_off[nb][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + w_off[nb][1]));
+            const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+            wf[nb] = i32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this step's reads are done
+        if (i + 1 < nsteps) {
+            // Own copies of step i+1 landed (later ones may stay in flight),
+            // then every wave's: step i+1 is visible and slot i is free.
+            const int last_issued = i + SLOTS - 1 < nsteps - 1 ? i + SLOTS - 1 : nsteps - 1;
+            wait_own(last_issued - (i + 1));
+            fence_sched();
+            __syncthreads();
+            fence_sched();
+            if (i + SLOTS < nsteps) issue(i + SLOTS);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma16<DT>(wf[nb], xf[mb], acc[mb][nb]);
+    }
+
+    // ---- regroup the block through LDS, row by row ---------------------------
+    // red[m][n] holds row m of the block (RED_LD pads the rows against bank
+    // conflicts).  From here on wave w owns rows w, w+4, ... < M, which move
+    // as whole rows: 1 KiB of FP32 per row, 16 bytes per lane.  The row loops
+    // stay rolled: this code runs once per workgroup, and unrolled copies of
+    // it would mostly cost instruction-cache misses.
+    constexpr int RED_LD = BNS + 4;
+    static_assert(MT * RED_LD * 4 <= SLOT * SLOTS, "regroup buffer must fit in the ring");
+    float* red = (float*)smem;
+    __syncthreads();                         // every wave is done with the ring
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int m = 16 * mb + (lane & 15), n = 64 * w + 16 * nb + 4 * (lane >> 4);
+            *(f32x4*)(red + m * RED_LD + n) = acc[mb][nb];
+        }
+    __syncthreads();
+    const int n = 4 * lane;
+
+    // ---- split-K reduction -------------------------------------------------
+    if (sa.ksplit > 1) {
+        // Publish this range's partial rows with device-coherent stores, wait
+        // for them to complete, then count the arrival.
+        const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(sa.part, 0, sa.part_bytes, 0x00020000);
+        const unsigned blk_off = (unsigned)blk * (unsigned)sa.ksplit * (MT * BNS * 4);
+        auto part_off = [&](int sp, int m) {
+            return blk_off + (unsigned)(sp * (MT * BNS) + m * BNS + n) * 4;
+        };
+        for (int m = w; m < M; m += 4)
+            store_coherent(ws, part_off(split, m), *(const f32x4*)(red + m * RED_LD + n));
+        wait_vm<0>();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned old = __hip_atomic_fetch_add(sa.cnt + blk, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = old == (unsigned)(sa.ksplit - 1);
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        if (tid == 0) sa.cnt[blk] = 0u;
+        // Last arrival: every partial of the block is complete.  Each row is
+        // summed over ranges 0, 1, ..., ksplit-1 in that order (own range from
+        // LDS) and the sum replaces the row in LDS.
+        if (sa.ksplit <= 4) {
+            // One round: the (up to three) other ranges of all this wave's
+            // rows are in flight together; the own range is slotted in at
+            // position `split` of the sum.
+            constexpr int RW = MT / 4;
+            f32x4 v[RW][3];
+#pragma unroll
+            for (int g = 0; g < RW; ++g)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    const int m = w + 4 * g, sp = c < split ? c : c + 1;
+                    v[g][c] = (m < M && sp < sa.ksplit) ? load_coherent(ws, part_off(sp, m))
+                                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int g = 0; g < RW; ++g) {
+                const int m = w + 4 * g;
+                if (m >= M) break;
+                f32x4* row = (f32x4*)(red + m * RED_LD + n);
+                const f32x4 mine = *row;
+                f32x4 tot = split == 0 ? mine : v[g][0];
+#pragma unroll
+                for (int pos = 1; pos < 4; ++pos) {
+                    if (pos >= sa.ksplit) break;
+                    tot = tot + (pos == split ? mine
+                                 : (pos < split ? v[g][pos < 3 ? pos : 2] : v[g][pos - 1]));
+                }
+                *row = tot;
+            }
+        } else {
+            // More ranges: per row, rounds of SPC ranges in flight.
+            constexpr int SPC = 4;
+            for (int m = w; m < M; m += 4) {
+                f32x4* row = (f32x4*)(red + m * RED_LD + n);
+                const f32x4 mine = *row;
+                f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int sp0 = 0; sp0 < sa.ksplit; sp0 += SPC) {
+                    f32x4 v[SPC];
+#pragma unroll
+                    for (int c = 0; c < SPC; ++c) {
+                        const int sp = sp0 + c;
+                        v[c] = (sp < sa.ksplit && sp != split) ? load_coherent(ws, part_off(sp, m)) : mine;
+                    }
+#pragma unroll
+                    for (int c = 0; c < SPC; ++c) {
+                        const int sp = sp0 + c;
+                        if (sp == 0) tot = v[c];
+                        else if (sp < sa.ksplit) tot = tot + v[c];
+                    }
+                }
+                *row = tot;
+            }
+        }
+    }
+
+    // ---- epilogue: alpha, beta, one rounding, row-contiguous stores ----------
+    uint16_t* C = (uint16_t*)p.C;
+    const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
+    if (n >= nlim) return;
+    for (int m = w; m < M; m += 4) {
+        const f32x4 tot = *(const f32x4*)(red + m * RED_LD + n);
+        uint16_t* crow = C + (int64_t)m * p.ldc + n0;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = p.alpha * tot[e];
+        if (vec_ok && n + 4 <= nlim) {
+            uint32_t* d = (uint32_t*)(crow + n);
+            if (p.beta != 0.f) {
+                const uint32_t c0 = d[0], c1 = d[1];
+                v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
+                v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
+                v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
+                v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
+            }
+            const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+            const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+            *(uint2*)d = make_uint2(w0, w1);
+        } else {
+            for (int e = 0; e < 4 && n + e < nlim; ++e) {
+                float x = v[e];
+                if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[n + e]), x);
+                crow[n + e] = to_bits<DT>(x);
+            }
+        }
+    }
+}
+
+template <int DT, int MT>
+hipError_t launch_cfg(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
+    auto kern = k_skinny_sk<DT, MT>;
+    const size_t lds = (size_t)SLOTS * (W_BYTES + MT * KS * 2);
+    static bool attr_set = false;     // benign race: every caller sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, s, p, sa);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
+    if (p.M <= 16) return launch_cfg<DT, 16>(p, sa, grid, s);
+    if (p.M <= 32) return launch_cfg<DT, 32>(p, sa, grid, s);
+    return launch_cfg<DT, 64>(p, sa, grid, s);
+}
+
+int mt_of(int64_t M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
+
+}  // namespace
+
+bool skinny_sk_supports(const Problem& p) {
+    if (p.dtype != F16 && p.dtype != BF16) return false;
+    if (!p.a_kc || p.b_kc) return false;
+    if (p.M < 1 || p.M > 64 || p.K <= 0 || p.K % KS != 0 || p.N % 8 != 0) return false;
+    if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
+    if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
+    return (p.N + BNS - 1) / BNS <= 0x7fffffff / 64;
+}
+
+int skinny_sk_splits(const Problem& p, const Workspace& ws) {
+    const int64_t blocks = (p.N + BNS - 1) / BNS;
+    const int64_t nk = p.K / KS;
+    const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+    // About three workgroups for every four CUs (the copy-only measurements
+    // peak there), at most 16 ranges and never an empty one.
+    int64_t ks = (3 * slots / 4 + blocks - 1) / blocks;
+    if (ks > 16) ks = 16;
+    if (ks > nk) ks = nk;
+    if (ks < 1) ks = 1;
+    const int64_t need = blocks * ks * mt_of(p.M) * BNS * (int64_t)sizeof(float);
+    if (ks > 1 && (ws.part == nullptr || need > ws.part_bytes || blocks > ws.ncounters)) ks = 1;
+    const int64_t per = (nk + ks - 1) / ks;
+    return (int)((nk + per - 1) / per);
+}
+
+hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
+    const int64_t blocks = (p.N + BNS - 1) / BNS;
+    const int64_t nk = p.K / KS;
+    SplitArgs sa;
+    sa.ksplit = skinny_sk_splits(p, ws);
+    sa.per = (int)((nk + sa.ksplit - 1) / sa.ksplit);
+    sa.part = (float*)ws.part;
+    sa.part_bytes = (int)(ws.part_bytes < 0x7fffffff ? ws.part_bytes : 0x7fffffff);
+    sa.cnt = ws.counters;
+    const int64_t grid = blocks * sa.ksplit;
+    return p.dtype == F16 ? launch_dt<F16>(p, sa, grid, s) : launch_dt<BF16>(p, sa, grid, s);
+}
+
+}  // namespace mgemm

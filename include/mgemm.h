@@ -65,7 +65,8 @@ typedef enum {
     MGEMM_KERNEL_F32_FAST = 8,   /* FP32 NN, 16-byte aligned operands, 256x256x32 tiles, 16 waves */
     MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
     MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 NN, 256x256 tiles, 4 waves of 128x128, direct-to-LDS ring */
-    MGEMM_KERNEL_COUNT = 11
+    MGEMM_KERNEL_SKINNY_SK = 11, /* FP16/BF16, M <= 64, 256-column blocks, K split over workgroups */
+    MGEMM_KERNEL_COUNT = 12
 } mgemm_kernel_t;
 
 typedef struct mgemm_handle_s* mgemm_handle_t;
@@ -74,13 +75,18 @@ typedef struct mgemm_handle_s* mgemm_handle_t;
  * mgemm_create -- bind a handle to the CURRENT HIP device.
  *   out : receives the handle (owned by the caller, release with mgemm_destroy).
  * Returns MGEMM_ERR_UNSUPPORTED if the device is not gfx950, MGEMM_ERR_HIP if
- * the device cannot be queried, MGEMM_ERR_INVALID_ARG if out is NULL.
- * The handle is immutable after creation: concurrent mgemm_run calls on
- * different streams may share it.  It holds no device memory.
+ * the device cannot be queried or its workspace cannot be allocated,
+ * MGEMM_ERR_INVALID_ARG if out is NULL.
+ * The handle owns a device workspace (32 MiB of FP32 partial results plus
+ * 64 Ki arrival counters, allocated and zeroed here) that the split-K kernel
+ * uses: calls that run at the same time on different streams must use
+ * different handles; calls on one stream (or otherwise ordered) may share one.
+ * The counters return to zero at the end of every call that uses them.
  */
 mgemm_status_t mgemm_create(mgemm_handle_t* out);
 
-/* mgemm_destroy -- release a handle (NULL is accepted and ignored). */
+/* mgemm_destroy -- release a handle and its workspace (NULL is accepted and
+ * ignored).  No work enqueued with the handle may still be pending. */
 mgemm_status_t mgemm_destroy(mgemm_handle_t h);
 
 /*

@@ -27,7 +27,7 @@ def device_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip"])
+@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_h_dma.hip", "k_skinny_sk.hip"])
 def test_m0_only_written_by_our_copies(name, tmp_path):
     text = device_asm(os.path.join(CSRC, name), tmp_path)
     lines = [l.strip() for l in text.splitlines() if re.search(r"\bm0\b", l) and not l.strip().startswith(";")]
@@ -43,7 +43,7 @@ def test_m0_only_written_by_our_copies(name, tmp_path):
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 # k_h_mfma.hip is left out: its 256x256 register-staged instantiations hold
 # 256 accumulators plus a full slice of prefetch registers and spill one VGPR.
-@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip"])
+@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip"])
 def test_no_register_spills(name, tmp_path):
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-c", "-O3",
                         "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -52,3 +52,15 @@ def test_no_register_spills(name, tmp_path):
                        capture_output=True, text=True, check=True)
     spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", r.stderr)]
     assert spills and max(spills) == 0, r.stderr[-2000:]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("name", sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")))
+def test_no_scalar_cache_writes(name, tmp_path):
+    """No kernel may write through the scalar data cache: no scalar stores or
+    scalar atomics, no scalar-cache write-back or discard.  The split-K
+    kernel's fences must come out as vector L2 write-back/invalidate."""
+    text = device_asm(os.path.join(CSRC, name), tmp_path)
+    bad = [l.strip() for l in text.splitlines()
+           if re.match(r"\s*s_(store|buffer_store|atomic|buffer_atomic|dcache_wb|dcache_discard|scratch_store)", l)]
+    assert not bad, bad[:5]

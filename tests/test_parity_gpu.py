@@ -114,11 +114,32 @@ def test_ffn_bf16_sampled(h, kernel):
                       cols=[0, 191, 192, 12287])
 
 
+@pytest.mark.parametrize("kernel", ["auto", "skinny", "skinny_sk"])
 @pytest.mark.parametrize("M", W.SKINNY_M)
-def test_skinny_bf16_full(h, M):
+def test_skinny_bf16_full(h, M, kernel):
     case = W.ffn_bf16(M)
-    say("skinny", M)
-    P.check_tolerance(case, *P.run_gpu(h, case))
+    say("skinny", M, kernel)
+    P.check_tolerance(case, *P.run_gpu(h, case, kernel))
+
+
+# Shapes that give the split-K skinny kernel 1, 3, 4, 16, 5 and 2 K ranges
+# (one-round and multi-round reductions), a ragged last column block and
+# ragged M, with beta != 0: integer data, so every split order must give the
+# oracle's bits.  Each case runs twice in a row, which also checks that the
+# arrival counters are back at zero.
+SPLIT_SHAPES = [(16, 512, 32), (5, 1000, 96), (64, 12288, 4096), (3, 256, 4096), (33, 2056, 160),
+                (20, 6144, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_skinny_split_k_bit_exact(h, M, N, K):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("split", M, N, K, dtype, kindA="int", kindB="int", kindC="int",
+                      alpha=1.0, beta=-0.5, seeds=(M, N, K))
+        inputs = case.make()
+        for rep in range(2):
+            say("skinny_sk", dtype, (M, N, K), rep)
+            P.check_bit_exact(case, *P.run_gpu(h, case, "skinny_sk", inputs=inputs))
 
 
 # ---------------------------------------------------------------------------
@@ -137,7 +158,7 @@ def _sweep_shapes(n, seed):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_small_shape_sweep_bit_exact(h, dtype):
-    kernels = ["auto"] + (P.KERNELS_F32 if dtype == "f32" else P.KERNELS_16 + ["skinny"])
+    kernels = ["auto"] + (P.KERNELS_F32 if dtype == "f32" else P.KERNELS_16 + ["skinny", "skinny_sk"])
     ran = {k: 0 for k in kernels}
     for si, (M, N, K) in enumerate(_sweep_shapes(14, 7 + len(dtype))):
         for (la, lb), (alpha, beta) in itertools.product(
@@ -227,6 +248,8 @@ def test_invalid_arguments_leave_c_untouched(h):
 def test_deterministic_run_to_run(h):
     for case in (W.Case("det32", 1000, 1200, 777, "f32", seeds=(5, 6, 7)),
                  W.Case("det16", 1024, 1280, 1000, "bf16", kindA="normal", kindB="normal",
+                        seeds=(5, 6, 7)),
+                 W.Case("det_skinny", 16, 12288, 4096, "bf16", kindA="normal", kindB="normal",
                         seeds=(5, 6, 7))):
         inputs = case.make()
         outs = [W.storage_view(P.run_gpu(h, case, inputs=inputs)[4]) for _ in range(3)]
@@ -270,5 +293,6 @@ def test_dispatch_choices(h):
     assert sel(W.ragged_f32()) == "f32_mfma"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x256"
+    assert all(sel(W.ffn_bf16(m)) == "skinny_sk" for m in W.SKINNY_M)
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
