@@ -36,13 +36,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash() -> str:
+# Source file of each kernel variant; the counter summary of a kernel is valid
+# while this file and the shared header are unchanged.
+KERNEL_SOURCE = {
+    "general": "k_general.hip", "f32_mfma": "k_f32_mfma.hip", "f32_fast": "k_f32_mfma.hip",
+    "f32_fast_128": "k_f32_mfma.hip", "h_mfma_256x256": "k_h_mfma.hip",
+    "h_mfma_256x192": "k_h_mfma.hip", "h_mfma_128x128": "k_h_mfma.hip",
+    "h_pp_256x256": "k_h_pp.hip", "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
+    "skinny_sk": "k_skinny_sk.hip",
+}
+
+
+def src_hash(kernel: str | None = None) -> str:
+    """Hash of the kernel's source and the shared header (all sources if None)."""
     d = os.path.join(ROOT, "dense_gemm_mgemm_amd", "csrc")
+    if kernel is None:
+        files = [f for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h", ".cpp"))]
+    else:
+        files = ["common.h", KERNEL_SOURCE[kernel]]
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -164,7 +179,7 @@ def traffic_for(kernel, workload):
     try:
         t = json.load(open(p))
         e = t.get("%s/%s" % (kernel, workload))
-        if e and e.get("src_hash") == src_hash():
+        if e and e.get("src_hash") == src_hash(kernel):
             return e["bytes_per_launch"]
     except (ValueError, KeyError):
         pass
