@@ -120,11 +120,11 @@ bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_h_pp(const Problem& p, hipStream_t s);
 bool h_pp_supports(const Problem& p);
-hipError_t launch_h_dma(const Problem& p, hipStream_t s);
+hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s);
 bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s);
-bool h_dma_supports(const Problem& p);
+bool h_dma_supports(const Problem& p, int bn);
 bool skinny_supports(const Problem& p);
 
 }  // namespace mgemm

@@ -1,7 +1,9 @@
-// FP16/BF16 GEMM for gfx950: 256x256 output tiles, four waves of 128x128,
-// operands copied straight into a four-slot LDS ring, one workgroup barrier
-// per K slice.  The fast path for the canonical NN problem (A' K-contiguous,
-// B' N-contiguous).
+// FP16/BF16 GEMM for gfx950: 256xBN output tiles (BN = 256 or 192), four
+// waves of 128x(BN/2), operands copied straight into a four-slot LDS ring, one
+// workgroup barrier per K slice.  The fast path for the canonical NN problem
+// (A' K-contiguous, B' N-contiguous).  BN = 192 exists for grids that a
+// 256-wide tile fills badly: the 1024x12288 FFN projection is 192 tiles of
+// 256x256 on 256 CUs but exactly 256 tiles of 256x192.
 //
 // Budget that shaped it (measured on MI355X): a CU pulls about 40 B/clk from
 // L2 when every CU does, and a 256x256 tile needs 32 B/clk at the matrix-core
@@ -14,13 +16,14 @@
 //   1. wait until this wave's copies of slice j+1 have landed, workgroup
 //      barrier: slice j+1 is now visible to every wave, and every wave is done
 //      reading slice j-1, so its slot can be refilled;
-//   2. request slice j+3 into that slot (eight 1 KiB copies per wave);
+//   2. request slice j+3 into that slot (1 KiB copies: four of A and BN/64
+//      of B per wave);
 //   3. MFMAs of (j, ks=0) while reading the (j, ks=1) fragments;
 //   4. MFMAs of (j, ks=1) while reading the (j+1, ks=0) fragments.
 // Fragments are read one K-step ahead of the MFMAs that use them, so the
 // matrix core never waits for LDS at a slice boundary.  Within a K-step one
-// instruction group follows each MFMA (a copy every fourth MFMA, one fragment
-// read after each of the first eight), and the order is pinned with
+// instruction group follows each MFMA (the copies spread evenly, one
+// fragment read after each of the first few), and the order is pinned with
 // scheduling barriers: with one wave per SIMD every stall of the issuing wave
 // is a stall of the matrix core, and bursts of copies or reads back up the
 // memory and LDS queues (measured: 58 -> 40 cycles per 32-cycle MFMA).
@@ -33,9 +36,15 @@
 // published peak is out of reach and fewer stalls partly turn into a lower
 // clock.
 //
-// LDS layouts, copies and fragment reads are those of k_h_pp.hip (same XOR
-// swizzles; B fragments via ds_read_b64_tr_b16); rows past M and columns past
-// N of an edge tile are read from the last valid row/chunk and never stored.
+// LDS layouts: A rows of 64 bytes with the XOR swizzle of k_h_pp.hip; B rows
+// of 2*BN bytes, chunk c of K-row k at chunk position pos(c, k): for BN = 256
+// c ^ {0,6,10,12}[k&3], for BN = 192 the 16-byte chunks are permuted inside
+// each 128-byte group by a 16-row XOR table.  Both are free of bank conflicts
+// for the transposed reads (checked exhaustively over every read of a slice).
+// A 1 KiB B copy covers 64 consecutive chunk positions of the slot (two rows
+// for BN = 256, 2 2/3 rows for BN = 192).  B fragments come from
+// ds_read_b64_tr_b16; rows past M and columns past N of an edge tile are read
+// from the last valid row/chunk and never stored.
 // Restrictions (host-checked): A' K-contiguous, B' N-contiguous, K % 32 == 0,
 // N % 8 == 0, lda and ldb multiples of 8, 16-byte aligned bases.
 #include "common.h"
@@ -52,16 +61,31 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 #ifndef MGEMM_DMA_SLOTS
 #define MGEMM_DMA_SLOTS 4
 #endif
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int BM = 256, BK = 32, NT = 256;
 constexpr int SLOTS = MGEMM_DMA_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
-constexpr int A_ROW = BK * 2, B_ROW = BN * 2;
-constexpr int A_BYTES = BM * A_ROW, B_BYTES = BK * B_ROW;   // 16 KiB each
-constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-constexpr int COPIES = 8;                                   // 1 KiB copies per wave per slice
-constexpr int TM = 4, TN = 4;                               // 32x32 blocks per wave
+constexpr int A_ROW = BK * 2, A_BYTES = BM * A_ROW;         // 16 KiB
+constexpr int A_COPIES = 4;                                 // 1 KiB A copies per wave per slice
+constexpr int TM = 4;                                       // 32-row blocks per wave
+
+template <int BN>
+struct Cfg {
+    static_assert(BN == 256 || BN == 192, "tile width");
+    static constexpr int B_ROW = BN * 2, B_CHUNKS = BN / 8;
+    static constexpr int B_BYTES = BK * B_ROW;
+    static constexpr int B_COPIES = B_BYTES / 1024 / 4;     // per wave per slice
+    static constexpr int COPIES = A_COPIES + B_COPIES;
+    static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
+    static constexpr int TN = BN / 64;                      // 32-column blocks per wave
+    static constexpr int WN = BN / 2;                       // columns per wave
+};
 
 __device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-__device__ __forceinline__ int b_swz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }
+// Chunk position of chunk c in K-row k of the B slot (an involution for each k).
+template <int BN>
+__device__ __forceinline__ int b_pos(int c, int k) {
+    if constexpr (BN == 256) return c ^ ((0xCA60 >> ((k & 3) * 4)) & 15);
+    else return (c & ~7) | ((c & 7) ^ (int)((0x6204035651271642ull >> ((k & 15) * 4)) & 7));
+}
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
@@ -88,14 +112,15 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Wait until at most n slices of this wave's copies are still in flight
-// (copies complete in issue order).
+// Wait until at most n slices of L copies each are still in flight (copies
+// complete in issue order).
+template <int L>
 __device__ __forceinline__ void wait_slices(int n) {
-    static_assert(COPIES * 3 < 64, "vmcnt range");
+    static_assert(L * 3 < 64, "vmcnt range");
     if (n <= 0) wait_vm<0>();
-    else if (n == 1) wait_vm<COPIES>();
-    else if (n == 2) wait_vm<2 * COPIES>();
-    else wait_vm<3 * COPIES>();
+    else if (n == 1) wait_vm<L>();
+    else if (n == 2) wait_vm<2 * L>();
+    else wait_vm<3 * L>();
 }
 // Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l); see
 // k_h_pp.hip for why it is inline asm.
@@ -113,18 +138,16 @@ __device__ __forceinline__ void slice_barrier() {
     fence_sched();
 }
 
-template <int N>
-struct Phase {
-    static constexpr int value = N;
-};
-
+template <int TN>
 struct Frags {
     i32x4 a[TM];
     i32x4 b[TN];
 };
 
-template <int DT>
+template <int DT, int BN>
 __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
+    using G = Cfg<BN>;
+    constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES, B_ROW = G::B_ROW;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -140,12 +163,13 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     const uint16_t* __restrict__ A = (const uint16_t*)p.A;
     const uint16_t* __restrict__ B = (const uint16_t*)p.B;
 
-    // Copies of this wave: A rows [64w, 64w+64) (four copies of 16 rows),
-    // B K-rows [8w, 8w+8) (four copies of 2 rows).
+    // Copies of this wave: A rows [64w, 64w+64) (four copies of 16 rows); B
+    // copies j = w*B_COPIES + i, each the 64 chunk positions [64j, 64j+64) of
+    // the B slot (lane l: position 64j+l of the row-major slot).
     const uint16_t* src[COPIES];
     int dst[COPIES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < A_COPIES; ++i) {
         const int r = 64 * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ a_swz(r);
         const int rr = r < mlim ? r : mlim - 1;
@@ -153,19 +177,21 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         dst[i] = (64 * wave + 16 * i) * A_ROW;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int k = 8 * wave + 2 * i + (lane >> 5);
-        int c = (lane & 31) ^ b_swz(k);
+    for (int i = 0; i < G::B_COPIES; ++i) {
+        const int j = wave * G::B_COPIES + i;
+        const int f = 64 * j + lane;
+        const int k = f / G::B_CHUNKS, pos = f % G::B_CHUNKS;
+        int c = b_pos<BN>(pos, k);
         const int cmax = (nlim >> 3) - 1;
         c = c <= cmax ? c : cmax;
-        src[4 + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
-        dst[4 + i] = A_BYTES + (8 * wave + 2 * i) * B_ROW;
+        src[A_COPIES + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
+        dst[A_COPIES + i] = A_BYTES + j * 1024;
     }
     const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
         const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
-        copy_to_lds(src[i] + (int64_t)s * (i < 4 ? a_kstep : b_kstep), base + dst[i]);
+        copy_to_lds(src[i] + (int64_t)s * (i < A_COPIES ? a_kstep : b_kstep), base + dst[i]);
     };
 
     // Fragment read offsets within a slot.
@@ -188,15 +214,15 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int k = ks * 16 + 8 * (q >> 1) + 4 * h + (t >> 2);
-                    const int n = 128 * wn + 32 * tn + 16 * (q & 1) + 4 * (t & 3);
-                    b_off[tn][ks][h] = A_BYTES + k * B_ROW + (((n >> 3) ^ b_swz(k)) << 4) + ((n & 7) << 1);
+                    const int n = G::WN * wn + 32 * tn + 16 * (q & 1) + 4 * (t & 3);
+                    b_off[tn][ks][h] = A_BYTES + k * B_ROW + (b_pos<BN>(n >> 3, k) << 4) + ((n & 7) << 1);
                 }
     }
-    auto read_a = [&](Frags& f, int s, int ks, int tm) {
+    auto read_a = [&](Frags<TN>& f, int s, int ks, int tm) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
     };
-    auto read_b = [&](Frags& f, int s, int ks, int tn) {
+    auto read_b = [&](Frags<TN>& f, int s, int ks, int tn) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
@@ -212,72 +238,63 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    // One K-step: the 16 MFMAs on `use`, with the fragment reads that fill
-    // `nxt` (slice rs, k-step rks) and four copies of slice cs (copy indices
-    // c0..c0+3) spread between them, one instruction group after each MFMA.
-    // Reads come in the order the next K-step consumes them (A0, B0..B3,
-    // A1..A3), so its first MFMAs wait on the oldest reads only.  Phase P
-    // shifts the groups by P MFMAs: the four waves of a workgroup leave the
-    // slice barrier together, and staggering them keeps their copies and
-    // reads from reaching the shared address and LDS queues in bursts.
-    auto kstep = [&](auto phase, const Frags& use, Frags& nxt, bool do_read, int rs, int rks,
-                     bool do_copy, int cs, int c0) {
-        constexpr int P = decltype(phase)::value;
+    // One K-step: the TM*TN MFMAs on `use`, with the fragment reads that fill
+    // `nxt` (slice rs, k-step rks) and copies c0..c1-1 of slice cs spread
+    // evenly between them, one instruction group after each MFMA.  Reads come
+    // in the order the next K-step consumes them (A0, B0.., A1..A3), so its
+    // first MFMAs wait on the oldest reads only.
+    constexpr int NM = TM * TN;
+    auto kstep = [&](const Frags<TN>& use, Frags<TN>& nxt, bool do_read, int rs, int rks,
+                     bool do_copy, int cs, int c0, int c1) {
 #pragma unroll
-        for (int i = 0; i < TM * TN; ++i) {
-            const int tm = i >> 2, tn = i & 3;
+        for (int i = 0; i < NM; ++i) {
+            const int tm = i / TN, tn = i % TN;
             acc[tm][tn] = mfma<DT>(use.b[tn], use.a[tm], acc[tm][tn]);
-            if (do_copy && i >= P && ((i - P) & 3) == 0) copy(cs, c0 + (i >> 2));
+            if (do_copy) {
+#pragma unroll
+                for (int c = c0; c < c1; ++c)
+                    if (i == (c - c0) * NM / (c1 - c0)) copy(cs, c);
+            }
             if (do_read) {
-                const int r = i - P;
-                if (r == 1) read_a(nxt, rs, rks, 0);
-                if (r >= 2 && r <= 5) read_b(nxt, rs, rks, r - 2);
-                if (r >= 6 && r <= 8) read_a(nxt, rs, rks, r - 5);
+                if (i == 1) read_a(nxt, rs, rks, 0);
+                if (i >= 2 && i < 2 + TN) read_b(nxt, rs, rks, i - 2);
+                if (i >= 2 + TN && i < 1 + TN + TM) read_a(nxt, rs, rks, i - 1 - TN);
             }
             fence_sched();
         }
     };
 
     const int nk = (int)(p.K / BK);
-    // Prologue: request slices 0..2, make slice 0 visible, read (0, ks=0).
+    // Prologue: request slices 0..AHEAD-1, make slice 0 visible, read (0, ks=0).
     const int npro = nk < AHEAD ? nk : AHEAD;
     for (int s = 0; s < npro; ++s)
         for (int i = 0; i < COPIES; ++i) copy(s, i);
-    wait_slices(npro - 1);
+    wait_slices<COPIES>(npro - 1);
     slice_barrier();
-    Frags f0, f1;
+    Frags<TN> f0, f1;
     read_a(f0, 0, 0, 0);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) read_b(f0, 0, 0, tn);
 #pragma unroll
     for (int tm = 1; tm < TM; ++tm) read_a(f0, 0, 0, tm);
 
-    // Slice j: wait for this wave's copies of slice j+1 (W = copies that may
-    // stay in flight: those of slice j+2), barrier (slice j+1 visible to all
-    // waves, slot of slice j-1 free), then K-step 0 reading (j, ks=1) and
-    // K-step 1 reading (j+1, ks=0), both carrying copies of slice j+3.
-    auto slice = [&](auto phase, int j, bool more, bool next, int w) {
-        if (w >= 0) wait_slices(w);
-        if (next) slice_barrier();
-        kstep(phase, f0, f1, true, j, 1, more, j + AHEAD, 0);
-        kstep(phase, f1, f0, next, j + 1, 0, more, j + AHEAD, 4);
-    };
+    // Slice j: wait for this wave's copies of slice j+1 (later slices may
+    // stay in flight), barrier (slice j+1 visible to all waves, slot of slice
+    // j-1 free), then K-step 0 reading (j, ks=1) with the A copies of slice
+    // j+AHEAD and K-step 1 reading (j+1, ks=0) with its B copies.
     int j = 0;
-    auto main_loop = [&](auto phase) {
-        for (; j + AHEAD < nk; ++j) slice(phase, j, true, true, AHEAD - 2);
-    };
-    switch (wave & 3) {
-    case 0: main_loop(Phase<0>{}); break;
-    case 1: main_loop(Phase<1>{}); break;
-    case 2: main_loop(Phase<2>{}); break;
-    default: main_loop(Phase<3>{}); break;
+    for (; j + AHEAD < nk; ++j) {
+        wait_slices<COPIES>(AHEAD - 2);
+        slice_barrier();
+        kstep(f0, f1, true, j, 1, true, j + AHEAD, 0, A_COPIES);
+        kstep(f1, f0, true, j + 1, 0, true, j + AHEAD, A_COPIES, COPIES);
     }
-    for (; j < nk; ++j) {       // last (up to) three slices: no more copies
+    for (; j < nk; ++j) {       // last (up to) AHEAD slices: no more copies
         const bool next = j + 1 < nk;
-        if (next) wait_slices(nk - j - 2);
+        if (next) wait_slices<COPIES>(nk - j - 2);
         if (next) slice_barrier();
-        kstep(Phase<0>{}, f0, f1, true, j, 1, false, 0, 0);
-        kstep(Phase<0>{}, f1, f0, next, j + 1, 0, false, 0, 0);
+        kstep(f0, f1, true, j, 1, false, 0, 0, 1);
+        kstep(f1, f0, next, j + 1, 0, false, 0, 0, 1);
     }
 
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int ni = 128 * wn + 32 * tn + 8 * q + nq;
+                const int ni = G::WN * wn + 32 * tn + 8 * q + nq;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[tm][tn][4 * q + e];
@@ -324,10 +341,10 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     }
 }
 
-template <int DT>
+template <int DT, int BN>
 hipError_t launch_dt(const Problem& p, hipStream_t s) {
-    auto kern = k_h_dma<DT>;
-    const size_t lds = (size_t)SLOTS * SLOT_BYTES;
+    auto kern = k_h_dma<DT, BN>;
+    const size_t lds = (size_t)SLOTS * Cfg<BN>::SLOT_BYTES;
     static bool attr_set = false;     // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -342,18 +359,20 @@ hipError_t launch_dt(const Problem& p, hipStream_t s) {
 
 }  // namespace
 
-bool h_dma_supports(const Problem& p) {
+bool h_dma_supports(const Problem& p, int bn) {
+    if (bn != 256 && bn != 192) return false;
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (!p.a_kc || p.b_kc) return false;
     if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || p.N % 8 != 0) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
     return tiles > 0 && tiles <= 0x7fffffff;
 }
 
-hipError_t launch_h_dma(const Problem& p, hipStream_t s) {
-    return p.dtype == F16 ? launch_dt<F16>(p, s) : launch_dt<BF16>(p, s);
+hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s) {
+    if (bn == 192) return p.dtype == F16 ? launch_dt<F16, 192>(p, s) : launch_dt<BF16, 192>(p, s);
+    return p.dtype == F16 ? launch_dt<F16, 256>(p, s) : launch_dt<BF16, 256>(p, s);
 }
 
 }  // namespace mgemm

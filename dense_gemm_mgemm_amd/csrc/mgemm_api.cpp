@@ -83,7 +83,8 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_PP_256: return mgemm::h_pp_supports(p);
     case MGEMM_KERNEL_F32_FAST: return mgemm::f32_fast_supports(p, true);
     case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
-    case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p);
+    case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p, 256);
+    case MGEMM_KERNEL_H_DMA_192: return mgemm::h_dma_supports(p, 192);
     case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_supports(p);
     default: return false;
     }
@@ -117,18 +118,21 @@ mgemm_kernel_t choose(const Problem& p) {
     // on useful outputs (wave quantisation and the padding of ragged edge
     // tiles count as waste) times its measured per-CU speed relative to the
     // register-staged kernel.  The four-wave direct-to-LDS kernel runs a full
-    // 256x256 tile about 1.4x as fast (1024 NN tiles: 2.12 vs 2.58 ms), so it
-    // wins even a grid that leaves a quarter of the CUs idle.
+    // 256x256 tile about 1.4x as fast (1024 NN tiles: 2.12 vs 2.58 ms); its
+    // 256x192 form moves more bytes per flop and is preferred only where the
+    // narrower tile fills the CUs clearly better.
     struct Cand { mgemm_kernel_t k; int bm, bn; double speed; };
-    const Cand cands[4] = {{MGEMM_KERNEL_H_DMA_256, 256, 256, 1.4},
+    const Cand cands[5] = {{MGEMM_KERNEL_H_DMA_256, 256, 256, 1.4},
+                           {MGEMM_KERNEL_H_DMA_192, 256, 192, 1.3},
                            {MGEMM_KERNEL_H_256x256, 256, 256, 1.0},
                            {MGEMM_KERNEL_H_256x192, 256, 192, 1.0},
                            {MGEMM_KERNEL_H_128x128, 128, 128, 1.0}};
     mgemm_kernel_t best = MGEMM_KERNEL_GENERAL;
     double best_score = -1.0;
     for (const Cand& c : cands) {
-        const bool ok = c.k == MGEMM_KERNEL_H_DMA_256 ? mgemm::h_dma_supports(p)
-                                                      : mgemm::h_mfma_supports(p, (int)c.k);
+        const bool ok = c.k == MGEMM_KERNEL_H_DMA_256   ? mgemm::h_dma_supports(p, 256)
+                        : c.k == MGEMM_KERNEL_H_DMA_192 ? mgemm::h_dma_supports(p, 192)
+                                                        : mgemm::h_mfma_supports(p, (int)c.k);
         if (!ok) continue;
         const double score = fill(c.bm, c.bn, 1) * c.speed;
         if (score > best_score + 1e-9) { best_score = score; best = c.k; }
@@ -149,7 +153,8 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, mgemm_kernel_t k, hipS
     case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
     case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
-    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, s); break;
+    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, s); break;
+    case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
@@ -274,6 +279,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_F32_FAST: return "f32_fast";
     case MGEMM_KERNEL_F32_FAST_128: return "f32_fast_128";
     case MGEMM_KERNEL_H_DMA_256: return "h_dma_256x256";
+    case MGEMM_KERNEL_H_DMA_192: return "h_dma_256x192";
     case MGEMM_KERNEL_SKINNY_SK: return "skinny_sk";
     default: return "unknown";
     }

@@ -292,7 +292,7 @@ def test_dispatch_choices(h):
     assert sel(W.sgemm_4096()) == "f32_fast"
     assert sel(W.ragged_f32()) == "f32_mfma"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
-    assert sel(W.ffn_bf16()) == "h_dma_256x256"
+    assert sel(W.ffn_bf16()) == "h_dma_256x192"
     assert all(sel(W.ffn_bf16(m)) == "skinny_sk" for m in W.SKINNY_M)
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
