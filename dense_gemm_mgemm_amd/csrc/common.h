@@ -115,6 +115,8 @@ hipError_t launch_f32_mfma(const Problem& p, hipStream_t s);
 bool f32_mfma_supports(const Problem& p);
 hipError_t launch_f32_fast(const Problem& p, bool big, hipStream_t s);
 bool f32_fast_supports(const Problem& p, bool big);
+bool f32_unaligned_supports(const Problem& p);
+hipError_t launch_f32_unaligned(const Problem& p, hipStream_t s);
 hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s);
 bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);

@@ -168,33 +168,56 @@ hipError_t launch_f32_mfma(const Problem& p, hipStream_t s) {
 }  // namespace mgemm
 
 // ---------------------------------------------------------------------------
-// Fast FP32 path for the canonical NN problem with 16-byte aligned operands
-// (A' K-contiguous, B' N-contiguous, lda % 4 == 0, ldb % 4 == 0, 16-byte
-// aligned bases, N % 4 == 0, K % BK == 0).
+// Fast FP32 path for the canonical NN problem (A' K-contiguous, B'
+// N-contiguous), in two forms:
+//   * k_f32_fast<..., 4, 4>: 16-byte aligned operands (lda % 4 == 0,
+//     ldb % 4 == 0, 16-byte aligned bases, N % 4 == 0) and K % BK == 0;
+//   * the same kernel with narrower global loads for operands that are not
+//     16-byte aligned (VA = 1 float per A load, VB = 1 or 2 floats per B
+//     load, chosen from the alignment of the bases and leading dimensions;
+//     not both single floats) and any K: the last, partial K slice is
+//     fetched element by element, zero beyond K.  This is the ragged row of the pages' workloads
+//     (lda = 4095, ldb = 12290: A rows 4-byte and B rows 8-byte aligned).
 //
-//  * Global loads are 16 bytes per lane (4 floats); edge rows/columns of a
-//    tile are read from the last valid row/4-column chunk instead of being
-//    masked (their results are never stored), so the K loop has no
-//    per-element conditions.
-//  * A is kept in LDS as [m][k] rows of BK+4 floats, written with one
-//    16-byte store per load; B as [k][n] rows of BN+4 floats.  The MFMA only
-//    needs A and B to agree on which k each (lane-half, step) stands for, so
-//    lane-half g at step s uses k = g*BK/2 + s: a lane then reads its BK/2
-//    consecutive A values with 16-byte LDS reads, and the 20-float row
-//    stride keeps those reads free of bank conflicts.
+//  * Edge rows/columns of a tile are read from the last valid row / column
+//    chunk instead of being masked (their results are never stored), so the
+//    full K slices have no per-element conditions.
+//  * A is kept in LDS as [m][k] rows of BK+4 floats; B as [k][n] rows of
+//    BN+4 floats.  The MFMA only needs A and B to agree on which k each
+//    (lane-half, step) stands for, so lane-half g at step s uses
+//    k = g*BK/2 + s: a lane then reads its BK/2 consecutive A values with
+//    16-byte LDS reads, and the 36-float row stride keeps those reads free
+//    of bank conflicts.
 // ---------------------------------------------------------------------------
 namespace mgemm {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+template <int V> struct VecT;
+template <> struct VecT<1> { typedef float T; };
+template <> struct VecT<2> { typedef f32x2v T; };
+template <> struct VecT<4> { typedef f32x4v T; };
+template <int V>
+__device__ __forceinline__ float lane_of(const typename VecT<V>::T& v, int e) {
+    if constexpr (V == 1) return v;
+    else return v[e];
+}
+template <int V>
+__device__ __forceinline__ void set_lane(typename VecT<V>::T& v, int e, float x) {
+    if constexpr (V == 1) v = x;
+    else v[e] = x;
+}
 
-template <int BM, int BN, int BK, int WM, int WN, int OCC>
+template <int BM, int BN, int BK, int WM, int WN, int OCC, int VA, int VB, bool TAIL>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
+    typedef typename VecT<VA>::T TA;
+    typedef typename VecT<VB>::T TB;
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int AROW = BK + 4, BROW = BN + 4;            // padded LDS rows (floats)
-    constexpr int ACH = BM * BK / 4, BCH = BK * BN / 4;     // 16-byte chunks per slice
+    constexpr int ACH = BM * BK / VA, BCH = BK * BN / VB;   // loads per slice
     constexpr int LA = ACH / NT, LB = BCH / NT;
     constexpr int HALF = BK / 2;                            // k values per lane-half per slice
     static_assert(LA * NT == ACH && LB * NT == BCH, "tile must split evenly");
@@ -218,41 +241,84 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
     const float* __restrict__ A = (const float*)p.A;
     const float* __restrict__ B = (const float*)p.B;
 
-    // Per-thread 16-byte chunks (fixed across K slices).
-    const float* a_src[LA];
-    int a_dst[LA];
-#pragma unroll
-    for (int r = 0; r < LA; ++r) {
-        const int c = tid + r * NT;
-        const int mi = c / (BK / 4), kc = (c % (BK / 4)) * 4;
-        const int mm = mi < mlim ? mi : mlim - 1;
-        a_src[r] = A + (m0 + mm) * p.lda + kc;
-        a_dst[r] = mi * AROW + kc;
-    }
-    const float* b_src[LB];
-    int b_dst[LB];
-#pragma unroll
-    for (int r = 0; r < LB; ++r) {
-        const int c = tid + r * NT;
-        const int ki = c / (BN / 4), nc = (c % (BN / 4)) * 4;
-        const int nn = nc + 4 <= nlim ? nc : nlim - 4;
-        b_src[r] = B + (int64_t)ki * p.ldb + n0 + nn;
-        b_dst[r] = ki * BROW + nc;
-    }
-    const int64_t b_kstep = (int64_t)BK * p.ldb;
+    // Load positions: load r of a thread covers A row a_mi0 + r*A_RS (columns
+    // a_kc..a_kc+VA-1 of the slice) and B row b_ki0 + r*B_RS (columns
+    // b_nc..b_nc+VB-1).  Only these few integers stay live across the K loop.
+    constexpr int AK = BK / VA, A_RS = NT / AK;
+    constexpr int BNV = BN / VB, B_RS = NT / BNV;
+    static_assert(NT % AK == 0 && NT % BNV == 0, "loads must tile the slice");
+    const int a_mi0 = tid / AK, a_kc = (tid % AK) * VA;
+    const int b_ki0 = tid / BNV, b_nc = (tid % BNV) * VB;
+    const int b_nn = b_nc + VB <= nlim ? b_nc : nlim - VB;
+    const float* a_base = A + m0 * p.lda + a_kc;
+    const float* b_base = B + (int64_t)b_ki0 * p.ldb + n0 + b_nn;
+    auto a_ptr = [&](int r) {
+        const int mi = a_mi0 + r * A_RS;
+        return a_base + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda;
+    };
+    auto b_ptr = [&](int r) { return b_base + (int64_t)(r * B_RS) * p.ldb; };
 
-    f32x4v ra[LA], rb[LB];
+    TA ra[LA];
+    TB rb[LB];
+    // With 16-byte loads on both operands the per-load pointers are computed
+    // once (they fit in the registers of a 16-wave workgroup and save the
+    // address arithmetic in the loop); with narrower loads there are too
+    // many, and the slice bases pass through an empty asm so that the
+    // compiler forms each load address here instead of keeping LA + LB
+    // loop-invariant 64-bit pointers live across the K loop.
+    constexpr bool WIDE = VA == 4 && VB == 4;
+    const float* a_src[WIDE ? LA : 1];
+    const float* b_src[WIDE ? LB : 1];
+    if constexpr (WIDE) {
+#pragma unroll
+        for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
+#pragma unroll
+        for (int r = 0; r < LB; ++r) b_src[r] = b_ptr(r);
+    }
     auto fetch = [&](int64_t kt) {
+        if constexpr (WIDE) {
 #pragma unroll
-        for (int r = 0; r < LA; ++r) ra[r] = *(const f32x4v*)(a_src[r] + kt * BK);
+            for (int r = 0; r < LA; ++r) ra[r] = *(const TA*)(a_src[r] + kt * BK);
 #pragma unroll
-        for (int r = 0; r < LB; ++r) rb[r] = *(const f32x4v*)(b_src[r] + kt * b_kstep);
+            for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(b_src[r] + kt * BK * p.ldb);
+        } else {
+            const float* ab = a_base + kt * BK;
+            const float* bb = b_base + kt * BK * p.ldb;
+            asm volatile("" : "+v"(ab), "+v"(bb));
+#pragma unroll
+            for (int r = 0; r < LA; ++r) {
+                const int mi = a_mi0 + r * A_RS;
+                ra[r] = *(const TA*)(ab + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda);
+            }
+#pragma unroll
+            for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(bb + (int64_t)(r * B_RS) * p.ldb);
+        }
+    };
+    // The partial last slice: element by element, zero where k >= K (the
+    // address is clamped to k = K-1 so that nothing past the operands is read).
+    auto fetch_tail = [&](int64_t kt) {
+        const int64_t kb = kt * BK;
+#pragma unroll
+        for (int r = 0; r < LA; ++r)
+#pragma unroll
+            for (int e = 0; e < VA; ++e) {
+                const int64_t k = kb + a_kc + e;
+                const float x = a_ptr(r)[(k < p.K ? k : p.K - 1) - a_kc];
+                set_lane<VA>(ra[r], e, k < p.K ? x : 0.f);
+            }
+#pragma unroll
+        for (int r = 0; r < LB; ++r) {
+            const int64_t k = kb + b_ki0 + r * B_RS;
+            const float* row = b_base + ((k < p.K ? k : p.K - 1) - b_ki0) * p.ldb;
+#pragma unroll
+            for (int e = 0; e < VB; ++e) set_lane<VB>(rb[r], e, k < p.K ? row[e] : 0.f);
+        }
     };
     auto stash = [&](int slot) {
 #pragma unroll
-        for (int r = 0; r < LA; ++r) *(f32x4v*)(&As[slot][a_dst[r]]) = ra[r];
+        for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
 #pragma unroll
-        for (int r = 0; r < LB; ++r) *(f32x4v*)(&Bs[slot][b_dst[r]]) = rb[r];
+        for (int r = 0; r < LB; ++r) *(TB*)(&Bs[slot][(b_ki0 + r * B_RS) * BROW + b_nc]) = rb[r];
     };
 
     f32x16 acc[TM][TN];
@@ -261,14 +327,22 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    const int64_t nk = p.K / BK;
+    const int64_t nfull = p.K / BK, nk = (p.K + BK - 1) / BK;
+    auto load = [&](int64_t kt) {
+        if constexpr (TAIL) {
+            if (kt < nfull) fetch(kt);
+            else fetch_tail(kt);
+        } else {
+            fetch(kt);          // K % BK == 0 (host-checked)
+        }
+    };
     const int lrow = lane >> 5, lcol = lane & 31;
-    fetch(0);
+    load(0);
     stash(0);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) fetch(kt + 1);
+        if (kt + 1 < nk) load(kt + 1);
         const float* as = &As[cur][(wm * WTM + lcol) * AROW + lrow * HALF];
         const float* bs = &Bs[cur][(lrow * HALF) * BROW + wn * WTN + lcol];
 #pragma unroll
@@ -312,11 +386,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
     }
 }
 
-// Two instantiations: a 256x256x32 tile on 16 waves (one workgroup per CU)
-// for grids that fill the chip, and a 128x128x16 tile on 4 waves (two
-// workgroups per CU) for smaller grids.
+// Tile shapes: 256x256x32 on 16 waves (one workgroup per CU) for aligned
+// grids that fill the chip, 128x128x16 on 4 waves (two workgroups per CU) for
+// smaller aligned grids, and 256x256x32 on 8 waves of 128x64 for the
+// unaligned form, whose narrower loads need more staging registers than a
+// 16-wave workgroup leaves a wave (128).
 struct BigCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 4, OCC = 1; };
 struct SmallCfg { static constexpr int BM = 128, BN = 128, BK = 16, WM = 2, WN = 2, OCC = 2; };
+struct UnalignedCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = 4, OCC = 1; };
 
 template <class CF>
 bool fast_supports(const Problem& p) {
@@ -327,12 +404,24 @@ bool fast_supports(const Problem& p) {
     const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
     return tiles > 0 && tiles <= 0x7fffffff;
 }
-template <class CF>
+template <class CF, int VA, int VB, bool TAIL>
 hipError_t fast_launch(const Problem& p, hipStream_t s) {
     const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
-    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC>),
+    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL>),
                        dim3((unsigned)tiles), dim3(64 * CF::WM * CF::WN), 0, s, p);
     return hipGetLastError();
+}
+
+// Widest loads the operands allow: A loads of 4 floats need 16-byte aligned
+// rows; B loads of VB floats need VB*4-byte aligned rows and N % VB == 0 (the
+// last chunk of a row is shifted inside the row, never past it).
+int unaligned_va(const Problem& p) {
+    return (p.lda % 4 == 0 && ((uintptr_t)p.A & 15) == 0) ? 4 : 1;
+}
+int unaligned_vb(const Problem& p) {
+    if (p.ldb % 4 == 0 && ((uintptr_t)p.B & 15) == 0 && p.N % 4 == 0) return 4;
+    if (p.ldb % 2 == 0 && ((uintptr_t)p.B & 7) == 0 && p.N % 2 == 0) return 2;
+    return 1;
 }
 
 }  // namespace
@@ -342,7 +431,30 @@ bool f32_fast_supports(const Problem& p, bool big) {
 }
 
 hipError_t launch_f32_fast(const Problem& p, bool big, hipStream_t s) {
-    return big ? fast_launch<BigCfg>(p, s) : fast_launch<SmallCfg>(p, s);
+    return big ? fast_launch<BigCfg, 4, 4, false>(p, s) : fast_launch<SmallCfg, 4, 4, false>(p, s);
+}
+
+bool f32_unaligned_supports(const Problem& p) {
+    if (p.dtype != F32 || !p.a_kc || p.b_kc || p.K <= 0) return false;
+    if (((uintptr_t)p.A & 3) != 0 || ((uintptr_t)p.B & 3) != 0) return false;
+    // Single-float loads on both operands need more registers than a wave
+    // has here; that case stays with k_f32_mfma.
+    if (unaligned_va(p) == 1 && unaligned_vb(p) == 1) return false;
+    const int64_t tiles = ((p.M + UnalignedCfg::BM - 1) / UnalignedCfg::BM) *
+                          ((p.N + UnalignedCfg::BN - 1) / UnalignedCfg::BN);
+    return tiles > 0 && tiles <= 0x7fffffff;
+}
+
+hipError_t launch_f32_unaligned(const Problem& p, hipStream_t s) {
+    const int va = unaligned_va(p), vb = unaligned_vb(p);
+    using U = UnalignedCfg;
+    if (va == 4) {
+        if (vb == 4) return fast_launch<U, 4, 4, true>(p, s);
+        if (vb == 2) return fast_launch<U, 4, 2, true>(p, s);
+        return fast_launch<U, 4, 1, true>(p, s);
+    }
+    if (vb == 4) return fast_launch<U, 1, 4, true>(p, s);
+    return fast_launch<U, 1, 2, true>(p, s);           // (1, 1) is declined by the supports check
 }
 
 }  // namespace mgemm

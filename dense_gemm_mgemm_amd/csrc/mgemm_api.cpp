@@ -85,6 +85,7 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
     case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p, 256);
     case MGEMM_KERNEL_H_DMA_192: return mgemm::h_dma_supports(p, 192);
+    case MGEMM_KERNEL_F32_FAST_U: return mgemm::f32_unaligned_supports(p);
     case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_supports(p);
     default: return false;
     }
@@ -106,6 +107,9 @@ mgemm_kernel_t choose(const Problem& p) {
         if (big && (!small || fill(256, 256, 1) >= fill(128, 128, 2) * 0.9))
             return MGEMM_KERNEL_F32_FAST;
         if (small) return MGEMM_KERNEL_F32_FAST_128;
+        // NN operands that are not 16-byte aligned or a K that is not a
+        // multiple of the slice: the same kernel with narrower loads.
+        if (mgemm::f32_unaligned_supports(p)) return MGEMM_KERNEL_F32_FAST_U;
         return MGEMM_KERNEL_F32_MFMA;
     }
     // M <= 64 streams B once: 256-column blocks with K split over workgroups
@@ -155,6 +159,7 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, mgemm_kernel_t k, hipS
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
     case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, s); break;
     case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, s); break;
+    case MGEMM_KERNEL_F32_FAST_U: e = mgemm::launch_f32_unaligned(p, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
@@ -280,6 +285,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_F32_FAST_128: return "f32_fast_128";
     case MGEMM_KERNEL_H_DMA_256: return "h_dma_256x256";
     case MGEMM_KERNEL_H_DMA_192: return "h_dma_256x192";
+    case MGEMM_KERNEL_F32_FAST_U: return "f32_fast_u";
     case MGEMM_KERNEL_SKINNY_SK: return "skinny_sk";
     default: return "unknown";
     }

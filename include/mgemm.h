@@ -67,7 +67,8 @@ typedef enum {
     MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 NN, 256x256 tiles, 4 waves of 128x128, direct-to-LDS ring */
     MGEMM_KERNEL_SKINNY_SK = 11, /* FP16/BF16, M <= 64, 256-column blocks, K split over workgroups */
     MGEMM_KERNEL_H_DMA_192 = 12, /* FP16/BF16 NN, 256x192 tiles, 4 waves of 128x96, direct-to-LDS ring */
-    MGEMM_KERNEL_COUNT = 13
+    MGEMM_KERNEL_F32_FAST_U = 13, /* FP32 NN, any alignment and K: 256x256x32 tiles, narrower loads */
+    MGEMM_KERNEL_COUNT = 14
 } mgemm_kernel_t;
 
 typedef struct mgemm_handle_s* mgemm_handle_t;

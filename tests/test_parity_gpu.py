@@ -142,6 +142,37 @@ def test_skinny_split_k_bit_exact(h, M, N, K):
             P.check_bit_exact(case, *P.run_gpu(h, case, "skinny_sk", inputs=inputs))
 
 
+# FP32 with operands that are not 16-byte aligned and K that is not a multiple
+# of the K slice: every load width of the unaligned kernel (A 1 or 4 floats,
+# B 1, 2 or 4 floats), a K shorter than one slice, beta != 0.  Integer data:
+# bit-exact.  (M, N, K, lda, ldb, ldc)
+UNALIGNED_F32 = [(300, 514, 100, 101, 514, 514), (260, 257, 64, 64, 257, 257),
+                 (520, 300, 77, 80, 302, 300), (256, 256, 31, 33, 258, 256),
+                 (129, 96, 200, 203, 100, 97)]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", UNALIGNED_F32)
+def test_f32_unaligned_bit_exact(h, M, N, K, lda, ldb, ldc):
+    case = W.Case("f32u", M, N, K, "f32", lda=lda, ldb=ldb, ldc=ldc, alpha=1.0, beta=-0.5,
+                  kindA="int", kindB="int", kindC="int", seeds=(M, N, K))
+    inputs = case.make()
+    for k in ("auto", "f32_fast_u"):
+        out = supported(h, case, k, inputs)
+        if out is None:
+            assert k != "auto"
+            continue
+        say("f32 unaligned", (M, N, K, lda, ldb, ldc), k)
+        P.check_bit_exact(case, *out)
+
+
+@pytest.mark.parametrize("kernel", ["f32_fast_u", "f32_mfma"])
+def test_ragged_f32_forced(h, kernel):
+    case = W.ragged_f32()
+    say("ragged_f32", kernel)
+    out = P.run_gpu(h, case, kernel)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 256, extra=8), cols=[0, 255, 256, 12289])
+
+
 # ---------------------------------------------------------------------------
 # Small and ragged shapes, integer data, every variant: bit-exact
 # ---------------------------------------------------------------------------
@@ -290,7 +321,7 @@ def test_dispatch_choices(h):
                                       case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
                                       case.ldc, case.dtype)
     assert sel(W.sgemm_4096()) == "f32_fast"
-    assert sel(W.ragged_f32()) == "f32_mfma"
+    assert sel(W.ragged_f32()) == "f32_fast_u"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x192"
     assert all(sel(W.ffn_bf16(m)) == "skinny_sk" for m in W.SKINNY_M)
