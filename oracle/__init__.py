@@ -11,6 +11,9 @@ compiles that file with gcc and marshals numpy arrays into it.
 Definition implemented (see the header of ``mgemm_oracle.c`` for the page
 citations):  C = round_out(alpha * op(A) @ op(B) + beta * C), with FP32, FP16 or
 BF16 storage, row- or column-major operands and C stored in A's order.
+
+The SiLU epilogue (``silu_epilogue``) is plain numpy in FP64 on top of that
+result: Y = round_out(SiLU(round_out(C))).
 """
 from __future__ import annotations
 
@@ -118,6 +121,21 @@ def round_to(dtype, x) -> np.ndarray:
     out = np.empty(a.shape, np.float64)
     _load().orc_round_array(d, a.ctypes.data, a.size, out.ctypes.data)
     return out
+
+
+def silu_epilogue(dtype, c_exact) -> np.ndarray:
+    """Unrounded FP64 value of the fused projection Y = SiLU(round(C)).
+
+    "Chapter 5: Operators and Runtime" (ai-infra-book), section 5.4.2 (the
+    loop nest for Y = SiLU(AW): the FP32 sum is rounded to the output format,
+    then the activation is applied) and section 5.4.3 (the activation must
+    come after the whole K reduction and after that rounding).  SiLU(x) is
+    x * sigmoid(x) = x / (1 + e^-x).  ``c_exact`` holds the unrounded GEMM
+    results (as returned by ``gemm``); the stored Y is round_to(dtype, result).
+    """
+    c = round_to(dtype, c_exact)
+    with np.errstate(over="ignore"):
+        return c / (1.0 + np.exp(-c))
 
 
 def gemm(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C_in, C_out, ldc, dtype,

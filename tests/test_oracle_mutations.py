@@ -67,3 +67,34 @@ def test_planted_mistake_is_caught(name, tmp_path):
                        env=dict(os.environ, OMP_NUM_THREADS="2"))
     # exit 3: a pin failed cleanly; a negative code: the mutant crashed the battery.
     assert r.returncode != 0, "no pin caught the planted mistake %s\n%s" % (name, r.stdout)
+
+
+# Planted mistakes in the SiLU epilogue (plain numpy, so the mutants are
+# Python functions swapped in for oracle.silu_epilogue in this process).
+def _silu_no_prerounding(dtype, c_exact):
+    import numpy as np
+    c = np.asarray(c_exact, np.float64)
+    return c / (1.0 + np.exp(-c))
+
+
+def _silu_wrong_exp_sign(dtype, c_exact):
+    import numpy as np
+    c = oracle.round_to(dtype, c_exact)
+    with np.errstate(over="ignore"):
+        return c / (1.0 + np.exp(c))
+
+
+def _sigmoid_only(dtype, c_exact):
+    import numpy as np
+    c = oracle.round_to(dtype, c_exact)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-c))
+
+
+@pytest.mark.parametrize("mutant", [_silu_no_prerounding, _silu_wrong_exp_sign, _sigmoid_only],
+                         ids=lambda f: f.__name__)
+def test_planted_silu_mistake_is_caught(mutant, monkeypatch):
+    from tests.test_oracle_pins import check_silu_epilogue
+    monkeypatch.setattr(oracle, "silu_epilogue", mutant)
+    with pytest.raises(AssertionError):
+        check_silu_epilogue()

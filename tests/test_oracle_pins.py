@@ -310,7 +310,36 @@ def check_brute_force_fractions():
                 assert exact[i, j] == float(s)   # f16 products/sums this small are exact in f64
 
 
-PIN_CHECKS = [check_f16_against_numpy, check_f16_closed_forms, check_bf16_against_torch,
+def check_silu_epilogue():
+    """SiLU epilogue: the pages' two-partial-sums example, a library sigmoid,
+    rounding before the activation, and the limits."""
+    import json, os
+    from scipy.special import expit
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+    ex = g["silu_partial_sums"]
+    # Section 5.4.3: partial sums 1 and -1; activation after the full sum gives
+    # SiLU(0) = 0, activation on each partial sum gives about 0.4621.
+    A = _dense("f32", np.array([[1.0, -1.0]]))
+    B = _dense("f32", np.array([[1.0], [1.0]]))
+    _, exact = _run("row", "row", 1, 1, 2, 1.0, A, 2, B, 1, 0.0, None, 1, "f32", 1)
+    assert oracle.silu_epilogue("f32", exact)[0, 0] == 0.0
+    parts = oracle.silu_epilogue("f32", np.array([1.0, -1.0]))
+    assert abs(parts.sum() - ex["activation_before_sum"]) <= ex["abs_tol"]
+    # A library sigmoid on values that every format holds exactly.
+    for dt in ("f32", "f16", "bf16"):
+        x = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -3.0, 8.0, -8.0, 0.125])
+        y = oracle.silu_epilogue(dt, x)
+        assert np.allclose(y, x * expit(x), rtol=1e-14, atol=0.0), dt
+    # Rounding to the output format comes first: 1 + 2^-9 is 1 in BF16, not in FP32.
+    c = np.array([1.0 + 2.0 ** -9])
+    assert oracle.silu_epilogue("bf16", c)[0] == 1.0 * expit(1.0)
+    assert oracle.silu_epilogue("f32", c)[0] == c[0] * expit(c[0])
+    # Limits: SiLU(x) -> x for large x, -> -0 for very negative x (no NaN from e^-x overflow).
+    big = oracle.silu_epilogue("f32", np.array([1000.0, -1000.0, 60.0]))
+    assert big[0] == 1000.0 and big[1] == 0.0 and np.signbit(big[1]) and big[2] == 60.0
+
+
+PIN_CHECKS = [check_silu_epilogue, check_f16_against_numpy, check_f16_closed_forms, check_bf16_against_torch,
               check_f32_against_numpy, check_decode_all_patterns, check_identity,
               check_permutation, check_all_ones_alpha_beta, check_rank_one,
               check_alpha_zero_and_k_zero, check_beta_zero_never_reads_c,
