@@ -64,7 +64,7 @@ def src_hash(kernel: str | None = None) -> str:
 def workload_table():
     import workloads as W
     t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
-         "ffn_bf16": W.ffn_bf16()}
+         "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu()}
     for s in W.HGEMM_SHAPES:
         c = W.hgemm_colmajor(*s)
         t[c.name] = c
@@ -101,8 +101,15 @@ def measure(h, case, steps, warmup, rotate=1):
                                    case.alpha, dA[0], case.lda, dB[0], case.ldb, case.beta, dC[0],
                                    case.ldc, case.dtype)
 
+    epilogue = case.extra.get("epilogue", "none")
+
     def launch(i):
         j = i % rotate
+        if epilogue != "none":
+            mg.mgemm_run_ex(h, "auto", case.layoutA, case.layoutB, case.M, case.N, case.K,
+                            case.alpha, dA[j], case.lda, dB[j], case.ldb, case.beta, dC[j],
+                            case.ldc, case.dtype, epilogue=epilogue, stream=stream)
+            return
         mg.mgemm_run(h, case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, dA[j],
                      case.lda, dB[j], case.ldb, case.beta, dC[j], case.ldc, case.dtype,
                      stream=stream)
@@ -162,7 +169,13 @@ def cpu_baseline(case, out_dev, budget_s):
         nrows = int(min(case.M, max(nrows * 2, nrows * budget_s / max(dt, 1e-3) * 0.8)))
     flops = 2.0 * len(rows_done) * case.N * case.K
     got = P.logical(case, oracle.decode(case.dtype, storage_view(out_dev.cpu())))[rows_done]
-    rep = P.compare(case, got, results)
+    if case.extra.get("epilogue") == "silu":
+        y, bound = P.silu_reference(case, results)
+        err = np.abs(got - y)
+        rep = {"ok": bool(np.all(err <= bound)), "max_err": float(np.max(err)),
+               "tol": float(np.max(bound))}
+    else:
+        rep = P.compare(case, got, results)
     return ({"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
              "kind": "oracle", "sample": "%d of %d rows of C (%.1f GFLOP in %.1f s, FP64)" % (
                  len(rows_done), case.M, flops / 1e9, t_total)},

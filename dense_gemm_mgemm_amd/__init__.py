@@ -24,11 +24,13 @@ KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h
            "skinny", "h_pp_256x256", "f32_fast", "f32_fast_128",
            "h_dma_256x256", "skinny_sk", "h_dma_256x192", "f32_fast_u"]
 MGEMM_KERNEL_AUTO = 0
+MGEMM_EPILOGUE_NONE, MGEMM_EPILOGUE_SILU = 0, 1
+_EPILOGUE = {"none": MGEMM_EPILOGUE_NONE, "silu": MGEMM_EPILOGUE_SILU}
 
 _LAYOUT = {"row": MGEMM_ROW_MAJOR, "col": MGEMM_COL_MAJOR}
 _DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
 
-EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel",
+EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
             "mgemm_select_kernel", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
 
 
@@ -56,8 +58,9 @@ def load(path: str | None = None):
     lib.mgemm_destroy.argtypes = [vp]
     lib.mgemm_run.argtypes = [vp] + run_args
     lib.mgemm_run_kernel.argtypes = [vp, ci] + run_args
+    lib.mgemm_run_ex.argtypes = [vp, ci] + run_args[:-1] + [ci, vp]
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
-    for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel",
+    for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
                  "mgemm_select_kernel"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
@@ -135,6 +138,16 @@ def mgemm_run_kernel(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb
                                               beta, C, ldc, dtype), _stream(stream))
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_run_kernel(%s)" % KERNELS[k] if 0 <= k < len(KERNELS) else k)
+
+
+def mgemm_run_ex(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,
+                 epilogue="none", stream=None) -> None:
+    """As mgemm_run ("auto") or mgemm_run_kernel, with an output epilogue ("none" or "silu")."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    st = load().mgemm_run_ex(h, k, *_args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta,
+                                          C, ldc, dtype), _enum(epilogue, _EPILOGUE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_ex(%s, %s)" % (kernel, epilogue))
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

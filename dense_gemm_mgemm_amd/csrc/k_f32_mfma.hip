@@ -144,7 +144,7 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_f32_mfma(Problem p) {
                     const int64_t idx = m * p.ldc + n;
                     float v = p.alpha * acc[i][j][r];
                     if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
-                    C[idx] = v;
+                    C[idx] = apply_epilogue<F32>(v, p.epilogue);
                 }
             }
         }
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
                     const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
                     float v = p.alpha * acc[i][j][r];
                     if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
-                    C[idx] = v;
+                    C[idx] = apply_epilogue<F32>(v, p.epilogue);
                 }
             }
         }

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(GNT) void k_general(Problem p) {
             int64_t idx = m * p.ldc + n;
             float v = p.alpha * acc[i][j];
             if (p.beta != 0.f) v = fmaf(p.beta, E::load(C, idx), v);
-            E::store(C, idx, v);
+            E::store(C, idx, apply_epilogue<DT>(v, p.epilogue));
         }
     }
 }
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_scale(Problem p) {
         int64_t m = e / p.N, n = e % p.N;
         int64_t idx = m * p.ldc + n;
         float v = p.beta != 0.f ? p.beta * E::load(C, idx) : 0.f;
-        E::store(C, idx, v);
+        E::store(C, idx, apply_epilogue<DT>(v, p.epilogue));
     }
 }
 

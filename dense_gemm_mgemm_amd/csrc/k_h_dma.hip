@@ -323,6 +323,8 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                         v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
                         v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
                     }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<DT>(v[e], p.epilogue);
                     const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
                     const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
                     *(uint2*)d = make_uint2(w0, w1);
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                         if (ni + e < nlim) {
                             float x = v[e];
                             if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[ni + e]), x);
-                            crow[ni + e] = to_bits<DT>(x);
+                            crow[ni + e] = to_bits<DT>(apply_epilogue<DT>(x, p.epilogue));
                         }
                     }
                 }

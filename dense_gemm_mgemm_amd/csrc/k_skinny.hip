@@ -241,7 +241,7 @@ __global__ __launch_bounds__(NT, (BN == 32 ? 2 : 1)) void k_skinny(Problem p) {
             if (n + q >= nlim) break;
             float v = p.alpha * s[q];
             if (p.beta != 0.f) v = fmaf(p.beta, from_bits<DT>(crow[n + q]), v);
-            crow[n + q] = to_bits<DT>(v);
+            crow[n + q] = to_bits<DT>(apply_epilogue<DT>(v, p.epilogue));
         }
     }
 }

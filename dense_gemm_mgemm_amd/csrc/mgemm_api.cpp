@@ -53,6 +53,7 @@ mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layo
     p.ldc = ldc;
     p.dtype = (int)dtype;
     p.num_cu = h->num_cu;
+    p.epilogue = mgemm::EPI_NONE;
     if (rowA) {
         // Row-major C = A B.  A row-major is K-contiguous; B row-major is
         // N-contiguous, column-major is K-contiguous.
@@ -168,13 +169,17 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, mgemm_kernel_t k, hipS
 mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, mgemm_layout_t layoutA,
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
-                        void* C, int64_t ldc, mgemm_dtype_t dtype, hipStream_t stream) {
+                        void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                        hipStream_t stream) {
     Problem p;
     mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
                                      ldc, dtype, &p);
     if (st != MGEMM_SUCCESS) return st;
     if (forced != MGEMM_KERNEL_AUTO && (forced <= 0 || forced >= MGEMM_KERNEL_COUNT))
         return MGEMM_ERR_INVALID_ARG;
+    if (epilogue != MGEMM_EPILOGUE_NONE && epilogue != MGEMM_EPILOGUE_SILU)
+        return MGEMM_ERR_INVALID_ARG;
+    p.epilogue = epilogue == MGEMM_EPILOGUE_SILU ? mgemm::EPI_SILU : mgemm::EPI_NONE;
     if (p.M == 0 || p.N == 0) return MGEMM_SUCCESS;
     if (p.K == 0 || p.alpha == 0.f) {
         hipError_t e = mgemm::launch_scale(p, stream);
@@ -232,7 +237,7 @@ mgemm_status_t mgemm_run(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_
                          const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
                          mgemm_dtype_t dtype, hipStream_t stream) {
     return run_impl(h, MGEMM_KERNEL_AUTO, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                    ldc, dtype, stream);
+                    ldc, dtype, MGEMM_EPILOGUE_NONE, stream);
 }
 
 mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
@@ -242,7 +247,16 @@ mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_l
                                 mgemm_dtype_t dtype, hipStream_t stream) {
     if (kernel == MGEMM_KERNEL_AUTO) return MGEMM_ERR_INVALID_ARG;
     return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                    dtype, stream);
+                    dtype, MGEMM_EPILOGUE_NONE, stream);
+}
+
+mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
+                            mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
+                            const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                            void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                            hipStream_t stream) {
+    return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                    dtype, epilogue, stream);
 }
 
 mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,

@@ -71,6 +71,12 @@ typedef enum {
     MGEMM_KERNEL_COUNT = 14
 } mgemm_kernel_t;
 
+/* Output epilogues (see mgemm_run_ex). */
+typedef enum {
+    MGEMM_EPILOGUE_NONE = 0,     /* C = round(alpha*op(A)*op(B) + beta*C) */
+    MGEMM_EPILOGUE_SILU = 1      /* C = round(SiLU(round(alpha*op(A)*op(B) + beta*C))) */
+} mgemm_epilogue_t;
+
 typedef struct mgemm_handle_s* mgemm_handle_t;
 
 /*
@@ -134,6 +140,26 @@ mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel,
                                 const void* A, int64_t lda, const void* B, int64_t ldb,
                                 float beta, void* C, int64_t ldc, mgemm_dtype_t dtype,
                                 hipStream_t stream);
+
+/*
+ * mgemm_run_ex -- as mgemm_run (kernel == MGEMM_KERNEL_AUTO) or
+ * mgemm_run_kernel (a forced variant), with an output epilogue.
+ *   epilogue == MGEMM_EPILOGUE_SILU: the fused projection Y = SiLU(XW) of
+ *   "Chapter 5: Operators and Runtime" (ai-infra-book), sections 5.4.2 and
+ *   5.4.3.  Each output v = alpha*acc + beta*C (FP32) is first rounded to the
+ *   output type, exactly as mgemm_run would store it; then
+ *   SiLU(x) = x / (1 + e^-x) is evaluated in FP32 on that rounded value and
+ *   the result is rounded once more and stored.  The activation therefore
+ *   always follows the complete K sum.  K == 0 or alpha == 0 gives
+ *   SiLU(round(beta*C)).  Every kernel variant supports both epilogues.
+ * Errors: as mgemm_run / mgemm_run_kernel; MGEMM_ERR_INVALID_ARG for an
+ * unknown epilogue (nothing enqueued).
+ */
+mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
+                            mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
+                            const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                            void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                            hipStream_t stream);
 
 /*
  * mgemm_select_kernel -- the variant mgemm_run would launch for this problem

@@ -39,14 +39,16 @@ def c_initial(case: Case, C0):
     return t.view(torch.float16 if case.dtype == "f16" else torch.bfloat16)
 
 
-def run_gpu(h, case: Case, kernel: str = "auto", inputs=None, stream=None):
+def run_gpu(h, case: Case, kernel: str = "auto", inputs=None, stream=None, epilogue="none"):
     """Returns (A, B, C0, C_init, C_out) as CPU tensors."""
     A, B, C0 = inputs if inputs is not None else case.make()
     Cin = c_initial(case, C0)
     dA, dB, dC = A.cuda(), B.cuda(), Cin.cuda()
     args = (case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, dA, case.lda, dB,
             case.ldb, case.beta, dC, case.ldc, case.dtype)
-    if kernel == "auto":
+    if epilogue != "none":
+        mg.mgemm_run_ex(h, kernel, *args, epilogue=epilogue, stream=stream)
+    elif kernel == "auto":
         mg.mgemm_run(h, *args, stream=stream)
     else:
         mg.mgemm_run_kernel(h, kernel, *args, stream=stream)
@@ -155,3 +157,51 @@ def sample_rows(M: int, tile: int = 256, extra: int = 16, seed: int = 0) -> list
         t += tile * max(1, (M // tile) // 6)
     rows.update(int(x) for x in rng.integers(0, M, extra))
     return sorted(r for r in rows if 0 <= r < M)
+
+
+# ---------------------------------------------------------------------------
+# SiLU epilogue: Y = round(SiLU(round(C))).
+#
+# Against the oracle's unrounded Y_exact = SiLU(round(C_exact)) (FP64):
+#   * exact GEMM (integer data): the kernel's rounded C equals the oracle's,
+#     so only the FP32 evaluation of SiLU and the final rounding differ:
+#     |Y - Y_exact| <= ulp(Y) (one unit of the output format; FP32: 4 units);
+#   * general data: SiLU is 1.1-Lipschitz, so the GEMM bound on C (plus one
+#     output ulp for rounding C to the other side of a tie) carries over:
+#     |Y - Y_exact| <= 1.1 * (tol_C + ulp(C)) + ulp(Y).
+# ---------------------------------------------------------------------------
+def silu_reference(case: Case, c_exact, exact_gemm=False):
+    """(Y_exact, per-element bound) for the SiLU epilogue given the oracle's
+    unrounded GEMM values."""
+    y_exact = oracle.silu_epilogue(case.dtype, c_exact)
+    y_r = oracle.round_to(case.dtype, y_exact)
+    c_r = oracle.round_to(case.dtype, c_exact)
+    if case.dtype == "f32":
+        uy = np.maximum(np.abs(y_r), 2.0 ** -126) * 2.0 ** -23 * 4
+        uc = np.maximum(np.abs(c_r), 2.0 ** -126) * 2.0 ** -23
+        scale = float(np.max(np.abs(c_exact))) if np.size(c_exact) else 0.0
+        tol_c = tol_f32_rel(case.K) * max(scale, 1e-30)
+    else:
+        uy, uc = _ulp(case.dtype, y_r), _ulp(case.dtype, c_r)
+        tol_c = tol_half(case.K)
+    bound = uy if exact_gemm else 1.1 * (tol_c + uc) + uy
+    return y_exact, bound
+
+
+def check_silu(case: Case, A, B, C0, Cin, Cout, rows=None, exact_gemm=False):
+    a, b = storage_view(A), storage_view(B)
+    c0 = None if C0 is None else storage_view(C0)
+    c_exact = oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
+                          case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
+                          rows=None if rows is None else np.asarray(rows, np.int64))
+    y_exact, bound = silu_reference(case, c_exact, exact_gemm)
+    got_all = logical(case, oracle.decode(case.dtype, storage_view(Cout)))
+    got = got_all if rows is None else got_all[np.asarray(rows)]
+    err = np.abs(got - y_exact)
+    bad = np.argwhere(~(err <= bound))
+    assert bad.size == 0, "%s: %d outputs off, first %s: got %r want %r (bound %r)" % (
+        case.name, len(bad), tuple(bad[0]), got[tuple(bad[0])], y_exact[tuple(bad[0])],
+        bound[tuple(bad[0])] if np.ndim(bound) else bound)
+    pad = padding_mask(case)
+    assert np.array_equal(storage_view(Cout)[pad], storage_view(Cin)[pad]), "%s: wrote outside C" % case.name
+    return float(np.max(err)) if err.size else 0.0

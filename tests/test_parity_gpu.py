@@ -215,6 +215,60 @@ def test_small_shape_sweep_bit_exact(h, dtype):
 
 
 # ---------------------------------------------------------------------------
+# Fused SiLU epilogue (mgemm_run_ex): every variant, small shapes with integer
+# data (exact GEMM), the pages' FFN projection Y = SiLU(XW) and a skinny case
+# with random data, K = 0.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_silu_epilogue_every_variant(h, dtype):
+    kernels = ["auto"] + (P.KERNELS_F32 if dtype == "f32" else P.KERNELS_16 + ["skinny", "skinny_sk"])
+    ran = {k: 0 for k in kernels}
+    for (M, N, K), (la, lb) in itertools.product([(257, 255, 129), (64, 520, 96), (300, 256, 64)],
+                                                  [("row", "row"), ("col", "col")]):
+        # Values small enough that SiLU is far from linear for most outputs.
+        case = W.Case("silu", M, N, K, dtype, layoutA=la, layoutB=lb, alpha=0.25, beta=-0.5,
+                      kindA="int", kindB="int", kindC="int", seeds=(M, N, K))
+        inputs = case.make()
+        for k in kernels:
+            try:
+                out = P.run_gpu(h, case, k, inputs=inputs, epilogue="silu")
+            except mg.MgemmError as e:
+                if e.status == mg.MGEMM_ERR_UNSUPPORTED:
+                    continue
+                raise
+            ran[k] += 1
+            say("silu", dtype, (M, N, K), la, lb, k)
+            P.check_silu(case, *out, exact_gemm=True)
+    say("ran", ran)
+    assert ran["auto"] > 0 and ran["general"] > 0
+
+
+def test_silu_ffn_bf16_sampled(h):
+    case = W.ffn_bf16()
+    say("silu ffn")
+    out = P.run_gpu(h, case, "auto", epilogue="silu")
+    P.check_silu(case, *out, rows=P.sample_rows(case.M, 256, extra=8))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_silu_skinny(h, M):
+    case = W.ffn_bf16(M)
+    say("silu skinny", M)
+    P.check_silu(case, *P.run_gpu(h, case, "auto", epilogue="silu"))
+
+
+def test_silu_k_zero_and_bad_epilogue(h):
+    case = W.Case("silu_k0", 40, 48, 0, "bf16", alpha=1.0, beta=0.75, kindC="normal",
+                  seeds=(1, 2, 3))
+    P.check_silu(case, *P.run_gpu(h, case, "auto", epilogue="silu"), exact_gemm=True)
+    A = torch.zeros(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_ex(h, "auto", "row", "row", 4, 4, 4, 1.0, A, 4, A, 4, 0.0, A, 4, "f32",
+                        epilogue=7)
+    assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
 # Contract details
 # ---------------------------------------------------------------------------
 def test_beta_zero_ignores_nan_c(h):

@@ -153,6 +153,15 @@ def ffn_bf16(M: int = 1024) -> Case:
                 scaleA=1.0, scaleB=0.02, seeds=seeds)
 
 
+def ffn_bf16_silu() -> Case:
+    """The FFN projection with the fused activation, Y = SiLU(XW) (same inputs
+    as ffn_bf16(); the epilogue is named in `extra`)."""
+    c = ffn_bf16()
+    c.name = "ffn_bf16_silu_m1024"
+    c.extra = {"epilogue": "silu"}
+    return c
+
+
 SKINNY_M = [1, 16, 64]
 
 
