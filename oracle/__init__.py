@@ -12,8 +12,9 @@ Definition implemented (see the header of ``mgemm_oracle.c`` for the page
 citations):  C = round_out(alpha * op(A) @ op(B) + beta * C), with FP32, FP16 or
 BF16 storage, row- or column-major operands and C stored in A's order.
 
-The SiLU epilogue (``silu_epilogue``) is plain numpy in FP64 on top of that
-result: Y = round_out(SiLU(round_out(C))).
+The SiLU epilogue (``silu_epilogue``) and the gated pair (``swiglu``) are
+plain numpy in FP64 on top of those results: Y = round_out(SiLU(round_out(C)))
+and Z = round_out(round_out(SiLU(round_out(G))) * round_out(U)).
 """
 from __future__ import annotations
 
@@ -136,6 +137,20 @@ def silu_epilogue(dtype, c_exact) -> np.ndarray:
     c = round_to(dtype, c_exact)
     with np.errstate(over="ignore"):
         return c / (1.0 + np.exp(-c))
+
+
+def swiglu(dtype, g_exact, u_exact) -> np.ndarray:
+    """Unrounded FP64 value of the gated FFN pair Z = SiLU(G) * U.
+
+    "Chapter 5: Operators and Runtime", section 5.3.1 (G = X W_g and
+    U = X W_u, Z = SiLU(G) elementwise-times U, every tensor stored in the
+    output format) and Figure 5-14 (fusing keeps the rounding of the
+    intermediate results): G and U are rounded as stored tensors, T = SiLU(G)
+    is rounded as the stored intermediate, and Z = T * U is rounded on store.
+    ``g_exact`` and ``u_exact`` are the unrounded GEMM results from ``gemm``.
+    """
+    t = round_to(dtype, silu_epilogue(dtype, g_exact))
+    return t * round_to(dtype, u_exact)
 
 
 def gemm(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C_in, C_out, ldc, dtype,

@@ -98,3 +98,21 @@ def test_planted_silu_mistake_is_caught(mutant, monkeypatch):
     monkeypatch.setattr(oracle, "silu_epilogue", mutant)
     with pytest.raises(AssertionError):
         check_silu_epilogue()
+
+
+def _swiglu_no_t_rounding(dtype, g_exact, u_exact):
+    return oracle.silu_epilogue(dtype, g_exact) * oracle.round_to(dtype, u_exact)
+
+
+def _swiglu_gate_on_u(dtype, g_exact, u_exact):
+    t = oracle.round_to(dtype, oracle.silu_epilogue(dtype, u_exact))
+    return t * oracle.round_to(dtype, g_exact)
+
+
+@pytest.mark.parametrize("mutant", [_swiglu_no_t_rounding, _swiglu_gate_on_u],
+                         ids=lambda f: f.__name__)
+def test_planted_swiglu_mistake_is_caught(mutant, monkeypatch):
+    from tests.test_oracle_pins import check_swiglu
+    monkeypatch.setattr(oracle, "swiglu", mutant)
+    with pytest.raises(AssertionError):
+        check_swiglu()

@@ -339,7 +339,32 @@ def check_silu_epilogue():
     assert big[0] == 1000.0 and big[1] == 0.0 and np.signbit(big[1]) and big[2] == 60.0
 
 
-PIN_CHECKS = [check_silu_epilogue, check_f16_against_numpy, check_f16_closed_forms, check_bf16_against_torch,
+def check_swiglu():
+    """Gated pair Z = SiLU(G) * U: closed forms and the rounding of the stored
+    intermediates."""
+    from scipy.special import expit
+    g = np.array([0.0, 1.0, -1.0, 2.0, -4.0, 0.5, 3.0])
+    u = np.array([5.0, 1.0, 2.0, -3.0, 1.0, 0.0, -0.25])
+    for dt in ("f32", "bf16", "f16"):
+        z = oracle.swiglu(dt, g, u)
+        t = oracle.round_to(dt, g * expit(g))
+        assert np.array_equal(z, t * u), dt          # g and u are exact in every format
+    assert oracle.swiglu("bf16", np.array([0.0]), np.array([7.0]))[0] == 0.0
+    # U = 1 reduces to the SiLU epilogue rounded once.
+    x = np.array([0.3, -1.7, 2.2])
+    assert np.array_equal(oracle.swiglu("f16", x, np.ones(3)),
+                          oracle.round_to("f16", oracle.silu_epilogue("f16", x)))
+    # The stored T is rounded before the product: with T = SiLU(1) in BF16 and
+    # U = 3, the unrounded SiLU(1) * 3 differs from round(SiLU(1)) * 3.
+    z = oracle.swiglu("bf16", np.array([1.0]), np.array([3.0]))[0]
+    assert z == oracle.round_to("bf16", np.array([expit(1.0)]))[0] * 3.0
+    assert z != expit(1.0) * 3.0
+    # G and U are rounded as stored tensors before use.
+    z = oracle.swiglu("bf16", np.array([1.0 + 2.0 ** -10]), np.array([1.0 + 2.0 ** -10]))[0]
+    assert z == oracle.round_to("bf16", np.array([expit(1.0)]))[0] * 1.0
+
+
+PIN_CHECKS = [check_silu_epilogue, check_swiglu, check_f16_against_numpy, check_f16_closed_forms, check_bf16_against_torch,
               check_f32_against_numpy, check_decode_all_patterns, check_identity,
               check_permutation, check_all_ones_alpha_beta, check_rank_one,
               check_alpha_zero_and_k_zero, check_beta_zero_never_reads_c,
