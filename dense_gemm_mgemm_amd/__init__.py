@@ -31,6 +31,7 @@ _LAYOUT = {"row": MGEMM_ROW_MAJOR, "col": MGEMM_COL_MAJOR}
 _DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
 
 EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
+            "mgemm_run_gated",
             "mgemm_select_kernel", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
 
 
@@ -59,9 +60,10 @@ def load(path: str | None = None):
     lib.mgemm_run.argtypes = [vp] + run_args
     lib.mgemm_run_kernel.argtypes = [vp, ci] + run_args
     lib.mgemm_run_ex.argtypes = [vp, ci] + run_args[:-1] + [ci, vp]
+    lib.mgemm_run_gated.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, i64, ci, vp]
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
     for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
-                 "mgemm_select_kernel"):
+                 "mgemm_run_gated", "mgemm_select_kernel"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
@@ -148,6 +150,14 @@ def mgemm_run_ex(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, be
                                           C, ldc, dtype), _enum(epilogue, _EPILOGUE), _stream(stream))
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_run_ex(%s, %s)" % (kernel, epilogue))
+
+
+def mgemm_run_gated(h, M, N, K, X, ldx, Wg, Wu, ldw, Z, ldz, dtype, stream=None) -> None:
+    """Enqueue Z = SiLU(X W_g) * (X W_u) (row-major, 16-bit) on `stream`."""
+    st = load().mgemm_run_gated(h, int(M), int(N), int(K), _ptr(X), int(ldx), _ptr(Wg), _ptr(Wu),
+                                int(ldw), _ptr(Z), int(ldz), _enum(dtype, _DTYPE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_gated")
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mgemm {
 
 enum DType : int { F32 = 0, F16 = 1, BF16 = 2 };
@@ -29,6 +31,8 @@ struct Problem {
     int dtype;
     int num_cu;
     int epilogue;    // Epilogue below, applied to alpha*acc + beta*C before the final rounding
+    const void* B2;  // gated pair only: second B' (N-contiguous, leading dimension ldb2)
+    int64_t ldb2;
 };
 
 // Device workspace of a handle: FP32 partial results and per-block arrival
@@ -103,22 +107,104 @@ __device__ __forceinline__ float round_trip(float v) {
     else if constexpr (DT == F16) return f16_bits_to_f32(f32_to_f16_bits(v));
     else return bf16_bits_to_f32(f32_to_bf16_bits(v));
 }
+// 16-bit storage <-> FP32 for the two 16-bit formats.
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float v) {
+    if constexpr (DT == F16) return f32_to_f16_bits(v);
+    else return f32_to_bf16_bits(v);
+}
+template <int DT>
+__device__ __forceinline__ float from_bits(uint16_t b) {
+    if constexpr (DT == F16) return f16_bits_to_f32(b);
+    else return bf16_bits_to_f32(b);
+}
+// SiLU(c) = c / (1 + e^-c) in FP32.  In the far negative tail (c < -87 for
+// FP32 outputs, c < -20 for 16-bit ones) it is evaluated as c * e^c, equal
+// to it within 2e-9 relative there, so neither the overflowing e^-c nor a
+// denormal reciprocal is ever formed.
+template <int DT>
+__device__ __forceinline__ float silu_f32(float c) {
+    constexpr float LOG2E = 1.44269504088896341f;
+    if constexpr (DT == F32) {
+        if (!(c >= -87.0f)) return c * expf(c);           // also NaN in, NaN out
+        return c / (1.0f + expf(-c));
+    } else {
+        // 16-bit outputs: the hardware exp2 and reciprocal (relative errors
+        // near 1e-6) are far below the final rounding (2^-9 or 2^-12) and
+        // much cheaper than the IEEE forms.  The hardware exp2 has no
+        // denormal results, so the tail takes e^c * 2^64 (normal down to
+        // c = -131; below that the result is under half the smallest BF16
+        // denormal anyway) and scales the product back by 2^-64, a multiply
+        // that rounds into the denormal range correctly.  Both branches share
+        // one exp2 and end in a select, so the unrolled store loops stay
+        // straight-line code.
+        const bool tail = !(c >= -20.0f);                 // also NaN in, NaN out
+        const float e = __builtin_amdgcn_exp2f(tail ? fmaf(c, LOG2E, 64.0f) : -c * LOG2E);
+        const float head = c * __builtin_amdgcn_rcpf(1.0f + e);
+        return tail ? (c * e) * 0x1p-64f : head;
+    }
+}
+template <int DT, int EPI>
+__device__ __forceinline__ float epilogue_op(float v) {
+    if constexpr (EPI == EPI_SILU) return silu_f32<DT>(round_trip<DT>(v));
+    else return v;
+}
 template <int DT>
 __device__ __forceinline__ float apply_epilogue(float v, int epi) {
-    if (epi == EPI_SILU) {
-        const float c = round_trip<DT>(v);
-        if constexpr (DT == F32) {
-            return c / (1.0f + expf(-c));
+    return epi == EPI_SILU ? epilogue_op<DT, EPI_SILU>(v) : v;
+}
+// Calls f(E) with E an integral_constant holding the epilogue, so each store
+// loop is compiled once per epilogue and the plain path carries no
+// activation code between its stores.
+template <class F>
+__device__ __forceinline__ void with_epilogue(int epi, F&& f) {
+    if (epi == EPI_SILU) f(std::integral_constant<int, EPI_SILU>{});
+    else f(std::integral_constant<int, EPI_NONE>{});
+}
+// Gated pair ("Chapter 5: Operators and Runtime", section 5.3.1): from the
+// FP32 sums g = (X W_g)(m,n) and u = (X W_u)(m,n), Z = round(T * round(u)) with
+// T = round(SiLU(round(g))): G, U and T keep the rounding they would get as
+// stored tensors; the caller rounds the returned value once on store.
+template <int DT>
+__device__ __forceinline__ float swiglu_out(float g, float u) {
+    const float t = round_trip<DT>(silu_f32<DT>(round_trip<DT>(g)));
+    return t * round_trip<DT>(u);
+}
+
+// Writes the four 16-bit outputs crow[ni .. ni+3] (those below nlim) from
+// v = alpha * acc: adds beta * C, applies the epilogue once, rounds, and
+// stores 8 bytes at once when all four are in range and aligned (vec_ok).
+template <int DT, int EPI>
+__device__ __forceinline__ void store_out4(uint16_t* crow, int ni, int nlim, bool vec_ok,
+                                           float beta, float (&v)[4]) {
+    const bool full = vec_ok && ni + 4 <= nlim;
+    if (beta != 0.f) {
+        float c[4] = {0.f, 0.f, 0.f, 0.f};
+        if (full) {
+            const uint2 cw = *(const uint2*)(crow + ni);
+            c[0] = from_bits<DT>((uint16_t)cw.x);
+            c[1] = from_bits<DT>((uint16_t)(cw.x >> 16));
+            c[2] = from_bits<DT>((uint16_t)cw.y);
+            c[3] = from_bits<DT>((uint16_t)(cw.y >> 16));
         } else {
-            // 16-bit outputs: the hardware exp2 and reciprocal (relative
-            // errors near 1e-6 for |c| up to ~100) are far below the final
-            // rounding (2^-9 or 2^-12), and much cheaper than the IEEE forms
-            // in an epilogue that runs once per output.
-            const float e = __builtin_amdgcn_exp2f(-c * 1.44269504088896341f);
-            return c * __builtin_amdgcn_rcpf(1.0f + e);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ni + e < nlim) c[e] = from_bits<DT>(crow[ni + e]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
     }
-    return v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = epilogue_op<DT, EPI>(v[e]);
+    if (full) {
+        const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
+        *(uint2*)(crow + ni) = make_uint2(w0, w1);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (ni + e < nlim) crow[ni + e] = to_bits<DT>(v[e]);
+    }
 }
 
 template <int DT> struct Elem;
@@ -156,6 +242,8 @@ hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_h_pp(const Problem& p, hipStream_t s);
 bool h_pp_supports(const Problem& p);
 hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s);
+bool h_gated_supports(const Problem& p);
+hipError_t launch_h_gated(const Problem& p, hipStream_t s);
 bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s);

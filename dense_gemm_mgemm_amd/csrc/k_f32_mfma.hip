@@ -132,23 +132,26 @@ __global__ __launch_bounds__(64 * WM * WN, 2) void k_f32_mfma(Problem p) {
     // Epilogue.  32x32 accumulator layout: register r of lane l holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.
     float* C = (float*)p.C;
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 32 + lcol;
+            for (int j = 0; j < TN; ++j) {
+                const int64_t n = n0 + wn * WTN + j * 32 + lcol;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
-                if (m < p.M && n < p.N) {
-                    const int64_t idx = m * p.ldc + n;
-                    float v = p.alpha * acc[i][j][r];
-                    if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
-                    C[idx] = apply_epilogue<F32>(v, p.epilogue);
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t m = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
+                    if (m < p.M && n < p.N) {
+                        const int64_t idx = m * p.ldc + n;
+                        float v = p.alpha * acc[i][j][r];
+                        if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
+                        C[idx] = epilogue_op<F32, EPI>(v);
+                    }
                 }
             }
         }
-    }
+    });
 }
 
 constexpr int F_BM = 128, F_BN = 128;
@@ -367,23 +370,26 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
     }
 
     float* C = (float*)p.C;
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int ni = wn * WTN + j * 32 + lcol;
+            for (int j = 0; j < TN; ++j) {
+                const int ni = wn * WTN + j * 32 + lcol;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int mi = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
-                if (mi < mlim && ni < nlim) {
-                    const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
-                    float v = p.alpha * acc[i][j][r];
-                    if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
-                    C[idx] = apply_epilogue<F32>(v, p.epilogue);
+                for (int r = 0; r < 16; ++r) {
+                    const int mi = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
+                    if (mi < mlim && ni < nlim) {
+                        const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
+                        float v = p.alpha * acc[i][j][r];
+                        if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
+                        C[idx] = epilogue_op<F32, EPI>(v);
+                    }
                 }
             }
         }
-    }
+    });
 }
 
 // Tile shapes: 256x256x32 on 16 waves (one workgroup per CU) for aligned

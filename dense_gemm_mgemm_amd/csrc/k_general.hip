@@ -70,20 +70,23 @@ __global__ __launch_bounds__(GNT) void k_general(Problem p) {
     }
 
     T* C = (T*)p.C;
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t m = m0 + ty * 4 + i;
-        if (m >= p.M) continue;
+        for (int i = 0; i < 4; ++i) {
+            int64_t m = m0 + ty * 4 + i;
+            if (m >= p.M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t n = n0 + tx * 4 + j;
-            if (n >= p.N) continue;
-            int64_t idx = m * p.ldc + n;
-            float v = p.alpha * acc[i][j];
-            if (p.beta != 0.f) v = fmaf(p.beta, E::load(C, idx), v);
-            E::store(C, idx, apply_epilogue<DT>(v, p.epilogue));
+            for (int j = 0; j < 4; ++j) {
+                int64_t n = n0 + tx * 4 + j;
+                if (n >= p.N) continue;
+                int64_t idx = m * p.ldc + n;
+                float v = p.alpha * acc[i][j];
+                if (p.beta != 0.f) v = fmaf(p.beta, E::load(C, idx), v);
+                E::store(C, idx, epilogue_op<DT, EPI>(v));
+            }
         }
-    }
+    });
 }
 
 // C = beta * C (K == 0 or alpha == 0: A and B are not read).

@@ -65,18 +65,26 @@ constexpr int BM = 256, BK = 32, NT = 256;
 constexpr int SLOTS = MGEMM_DMA_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
 constexpr int A_ROW = BK * 2, A_BYTES = BM * A_ROW;         // 16 KiB
 constexpr int A_COPIES = 4;                                 // 1 KiB A copies per wave per slice
-constexpr int TM = 4;                                       // 32-row blocks per wave
 
-template <int BN>
+// BN is the width of the B slot.  The plain GEMM lays its four waves out 2x2
+// (128 rows x BN/2 columns each).  The gated pair (DUAL) fills the 192-wide
+// slot with 96 columns of each of two B matrices and lays the waves out 4x1
+// (64 rows x all 192 columns each), so that every wave holds the G and U
+// blocks of the same outputs in matching registers.
+template <int BN, bool DUAL>
 struct Cfg {
     static_assert(BN == 256 || BN == 192, "tile width");
+    static_assert(!DUAL || BN == 192, "the gated pair uses the 192-wide slot");
     static constexpr int B_ROW = BN * 2, B_CHUNKS = BN / 8;
     static constexpr int B_BYTES = BK * B_ROW;
     static constexpr int B_COPIES = B_BYTES / 1024 / 4;     // per wave per slice
     static constexpr int COPIES = A_COPIES + B_COPIES;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-    static constexpr int TN = BN / 64;                      // 32-column blocks per wave
-    static constexpr int WN = BN / 2;                       // columns per wave
+    static constexpr int WROWS = DUAL ? 64 : 128;           // rows per wave
+    static constexpr int TM = WROWS / 32;                   // 32-row blocks per wave
+    static constexpr int TN = DUAL ? BN / 32 : BN / 64;     // 32-column blocks per wave
+    static constexpr int WN = DUAL ? 0 : BN / 2;            // column offset of wave column 1
+    static constexpr int OUT = DUAL ? BN / 2 : BN;          // output columns per tile
 };
 
 __device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -95,16 +103,6 @@ __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-template <int DT>
-__device__ __forceinline__ uint16_t to_bits(float v) {
-    if constexpr (DT == F16) return f32_to_f16_bits(v);
-    else return f32_to_bf16_bits(v);
-}
-template <int DT>
-__device__ __forceinline__ float from_bits(uint16_t b) {
-    if constexpr (DT == F16) return f16_bits_to_f32(b);
-    else return bf16_bits_to_f32(b);
 }
 
 template <int N>
@@ -138,30 +136,33 @@ __device__ __forceinline__ void slice_barrier() {
     fence_sched();
 }
 
-template <int TN>
+template <int TM, int TN>
 struct Frags {
     i32x4 a[TM];
     i32x4 b[TN];
 };
 
-template <int DT, int BN>
+template <int DT, int BN, bool DUAL, int EPI>
 __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
-    using G = Cfg<BN>;
-    constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES, B_ROW = G::B_ROW;
+    using G = Cfg<BN, DUAL>;
+    constexpr int TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
+    constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
+    using Fr = Frags<TM, TN>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = DUAL ? wave : wave >> 1, wn = DUAL ? 0 : wave & 1;
 
-    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + OUT - 1) / OUT);
     int tmi, tni;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
-    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
-    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const int nlim = (int)(p.N - n0 < OUT ? p.N - n0 : OUT);
     const uint16_t* __restrict__ A = (const uint16_t*)p.A;
     const uint16_t* __restrict__ B = (const uint16_t*)p.B;
+    const uint16_t* __restrict__ B2 = (const uint16_t*)p.B2;   // gated pair: U's matrix
 
     // Copies of this wave: A rows [64w, 64w+64) (four copies of 16 rows); B
     // copies j = w*B_COPIES + i, each the 64 chunk positions [64j, 64j+64) of
@@ -183,10 +184,19 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         const int k = f / G::B_CHUNKS, pos = f % G::B_CHUNKS;
         int c = b_pos<BN>(pos, k);
         const int cmax = (nlim >> 3) - 1;
-        c = c <= cmax ? c : cmax;
-        src[A_COPIES + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
+        if constexpr (DUAL) {
+            // Chunks 0..11 of a slot row come from B (G), 12..23 from B2 (U).
+            const bool second = c >= G::B_CHUNKS / 2;
+            int cc = second ? c - G::B_CHUNKS / 2 : c;
+            cc = cc <= cmax ? cc : cmax;
+            src[A_COPIES + i] = (second ? B2 : B) + (int64_t)k * p.ldb + n0 + 8 * cc;
+        } else {
+            c = c <= cmax ? c : cmax;
+            src[A_COPIES + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
+        }
         dst[A_COPIES + i] = A_BYTES + j * 1024;
     }
+    // (The gated pair's two B matrices share ldb: host-checked.)
     const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
@@ -200,7 +210,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int r = 128 * wm + 32 * tm + (lane & 31);
+            const int r = G::WROWS * wm + 32 * tm + (lane & 31);
             const int c = 2 * ks + (lane >> 5);
             a_off[tm][ks] = r * A_ROW + ((c ^ a_swz(r)) << 4);
         }
@@ -218,11 +228,11 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                     b_off[tn][ks][h] = A_BYTES + k * B_ROW + (b_pos<BN>(n >> 3, k) << 4) + ((n & 7) << 1);
                 }
     }
-    auto read_a = [&](Frags<TN>& f, int s, int ks, int tm) {
+    auto read_a = [&](Fr& f, int s, int ks, int tm) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
     };
-    auto read_b = [&](Frags<TN>& f, int s, int ks, int tn) {
+    auto read_b = [&](Fr& f, int s, int ks, int tn) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     // in the order the next K-step consumes them (A0, B0.., A1..A3), so its
     // first MFMAs wait on the oldest reads only.
     constexpr int NM = TM * TN;
-    auto kstep = [&](const Frags<TN>& use, Frags<TN>& nxt, bool do_read, int rs, int rks,
+    auto kstep = [&](const Fr& use, Fr& nxt, bool do_read, int rs, int rks,
                      bool do_copy, int cs, int c0, int c1) {
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         for (int i = 0; i < COPIES; ++i) copy(s, i);
     wait_slices<COPIES>(npro - 1);
     slice_barrier();
-    Frags<TN> f0, f1;
+    Fr f0, f1;
     read_a(f0, 0, 0, 0);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) read_b(f0, 0, 0, tn);
@@ -303,9 +313,26 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     const int fr = lane & 31, nq = 4 * (lane >> 5);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int mi = 128 * wm + 32 * tm + fr;
+        const int mi = G::WROWS * wm + 32 * tm + fr;
         if (mi >= mlim) continue;
         uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
+        if constexpr (DUAL) {
+            // Gated pair: block tn holds G and block tn + TN/2 holds U of the
+            // same outputs (same lane layout); Z = round(T * round(U)),
+            // T = round(SiLU(round(G))).
+#pragma unroll
+            for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ni = 32 * tn + 8 * q + nq;
+                    float z[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        z[e] = swiglu_out<DT>(acc[tm][tn][4 * q + e], acc[tm][tn + TN / 2][4 * q + e]);
+                    store_out4<DT, EPI_NONE>(crow, ni, nlim, vec_ok, 0.f, z);
+                }
+            continue;
+        }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -314,39 +341,16 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[tm][tn][4 * q + e];
-                if (vec_ok && ni + 4 <= nlim) {
-                    uint32_t* d = (uint32_t*)(crow + ni);
-                    if (p.beta != 0.f) {
-                        const uint32_t c0 = d[0], c1 = d[1];
-                        v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
-                        v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
-                        v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
-                        v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<DT>(v[e], p.epilogue);
-                    const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-                    *(uint2*)d = make_uint2(w0, w1);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (ni + e < nlim) {
-                            float x = v[e];
-                            if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[ni + e]), x);
-                            crow[ni + e] = to_bits<DT>(apply_epilogue<DT>(x, p.epilogue));
-                        }
-                    }
-                }
+                store_out4<DT, EPI>(crow, ni, nlim, vec_ok, p.beta, v);
             }
         }
     }
 }
 
-template <int DT, int BN>
-hipError_t launch_dt(const Problem& p, hipStream_t s) {
-    auto kern = k_h_dma<DT, BN>;
-    const size_t lds = (size_t)SLOTS * Cfg<BN>::SLOT_BYTES;
+template <int DT, int BN, bool DUAL, int EPI>
+hipError_t launch_epi(const Problem& p, hipStream_t s) {
+    auto kern = k_h_dma<DT, BN, DUAL, EPI>;
+    const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
     static bool attr_set = false;     // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -354,9 +358,20 @@ hipError_t launch_dt(const Problem& p, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    constexpr int OUT = Cfg<BN, DUAL>::OUT;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + OUT - 1) / OUT);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p);
     return hipGetLastError();
+}
+
+// One kernel per epilogue: the store loop is unrolled over every output of
+// the tile, so a runtime choice would put the activation's code between the
+// plain stores (and the 256-wide tile has no registers to spare for it).
+template <int DT, int BN, bool DUAL>
+hipError_t launch_dt(const Problem& p, hipStream_t s) {
+    if constexpr (!DUAL)
+        if (p.epilogue == EPI_SILU) return launch_epi<DT, BN, false, EPI_SILU>(p, s);
+    return launch_epi<DT, BN, DUAL, EPI_NONE>(p, s);
 }
 
 }  // namespace
@@ -373,8 +388,18 @@ bool h_dma_supports(const Problem& p, int bn) {
 }
 
 hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s) {
-    if (bn == 192) return p.dtype == F16 ? launch_dt<F16, 192>(p, s) : launch_dt<BF16, 192>(p, s);
-    return p.dtype == F16 ? launch_dt<F16, 256>(p, s) : launch_dt<BF16, 256>(p, s);
+    if (bn == 192)
+        return p.dtype == F16 ? launch_dt<F16, 192, false>(p, s) : launch_dt<BF16, 192, false>(p, s);
+    return p.dtype == F16 ? launch_dt<F16, 256, false>(p, s) : launch_dt<BF16, 256, false>(p, s);
+}
+
+bool h_gated_supports(const Problem& p) {
+    if (!h_dma_supports(p, 192) || p.B2 == nullptr || p.ldb2 != p.ldb) return false;
+    return ((uintptr_t)p.B2 & 15) == 0;
+}
+
+hipError_t launch_h_gated(const Problem& p, hipStream_t s) {
+    return p.dtype == F16 ? launch_dt<F16, 192, true>(p, s) : launch_dt<BF16, 192, true>(p, s);
 }
 
 }  // namespace mgemm

@@ -55,17 +55,6 @@ __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int DT>
-__device__ __forceinline__ uint16_t to_bits(float v) {
-    if constexpr (DT == F16) return f32_to_f16_bits(v);
-    else return f32_to_bf16_bits(v);
-}
-template <int DT>
-__device__ __forceinline__ float from_bits(uint16_t b) {
-    if constexpr (DT == F16) return f16_bits_to_f32(b);
-    else return bf16_bits_to_f32(b);
-}
-
 // One operand tile of R rows (M or N index) by BK (K index).
 //   KC: the global operand is K-contiguous: element (r, k) at P[r*ld + k].
 //   else MN-contiguous: element (r, k) at P[k*ld + r].
@@ -270,46 +259,26 @@ __global__ __launch_bounds__(NT, (BM * BN <= 128 * 128) ? 2 : 1) void k_h_mfma(P
     uint16_t* C = (uint16_t*)p.C;
     const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
     const int nq = 4 * (lane >> 5);
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int mi = wm * WTM + i * 32 + fr;
-        if (mi >= mlim) continue;
-        uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
+        for (int i = 0; i < TM; ++i) {
+            const int mi = wm * WTM + i * 32 + fr;
+            if (mi >= mlim) continue;
+            uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+            for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ni = wn * WTN + j * 32 + 8 * q + nq;
-                float v[4];
+                for (int q = 0; q < 4; ++q) {
+                    const int ni = wn * WTN + j * 32 + 8 * q + nq;
+                    float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
-                if (vec_ok && ni + 4 <= nlim) {
-                    uint32_t* dst = (uint32_t*)(crow + ni);
-                    if (p.beta != 0.f) {
-                        const uint32_t c0 = dst[0], c1 = dst[1];
-                        v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
-                        v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
-                        v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
-                        v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<DT>(v[e], p.epilogue);
-                    const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-                    *(uint2*)dst = make_uint2(w0, w1);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (ni + e < nlim) {
-                            float x = v[e];
-                            if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[ni + e]), x);
-                            crow[ni + e] = to_bits<DT>(apply_epilogue<DT>(x, p.epilogue));
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[i][j][4 * q + e];
+                    store_out4<DT, EPI>(crow, ni, nlim, vec_ok, p.beta, v);
                 }
             }
         }
-    }
+    });
 }
 
 template <int DT, int BM, int BN, bool AKC, bool BKC>
@@ -370,6 +339,5 @@ hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s) {
     }
     return hipErrorInvalidValue;
 }
-
 
 }  // namespace mgemm

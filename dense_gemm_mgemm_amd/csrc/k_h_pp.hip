@@ -263,46 +263,26 @@ __global__ __launch_bounds__(NT, 1) void k_h_pp(Problem p) {
     uint16_t* C = (uint16_t*)p.C;
     const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
     const int fr = lane & 31, nq = 4 * (lane >> 5);
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int mi = 128 * g + 64 * wm + 32 * tm + fr;
-        if (mi >= mlim) continue;
-        uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
+        for (int tm = 0; tm < TM; ++tm) {
+            const int mi = 128 * g + 64 * wm + 32 * tm + fr;
+            if (mi >= mlim) continue;
+            uint16_t* crow = C + (m0 + mi) * p.ldc + n0;
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
+            for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ni = 128 * wn + 32 * tn + 8 * q + nq;
-                float v[4];
+                for (int q = 0; q < 4; ++q) {
+                    const int ni = 128 * wn + 32 * tn + 8 * q + nq;
+                    float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[tm][tn][4 * q + e];
-                if (vec_ok && ni + 4 <= nlim) {
-                    uint32_t* dst = (uint32_t*)(crow + ni);
-                    if (p.beta != 0.f) {
-                        const uint32_t c0 = dst[0], c1 = dst[1];
-                        v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
-                        v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
-                        v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
-                        v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<DT>(v[e], p.epilogue);
-                    const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-                    const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-                    *(uint2*)dst = make_uint2(w0, w1);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (ni + e < nlim) {
-                            float x = v[e];
-                            if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[ni + e]), x);
-                            crow[ni + e] = to_bits<DT>(apply_epilogue<DT>(x, p.epilogue));
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = p.alpha * acc[tm][tn][4 * q + e];
+                    store_out4<DT, EPI>(crow, ni, nlim, vec_ok, p.beta, v);
                 }
             }
         }
-    }
+    });
 }
 
 template <int DT>

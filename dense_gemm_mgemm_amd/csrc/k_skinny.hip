@@ -53,16 +53,6 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-template <int DT>
-__device__ __forceinline__ uint16_t to_bits(float v) {
-    if constexpr (DT == F16) return f32_to_f16_bits(v);
-    else return f32_to_bf16_bits(v);
-}
-template <int DT>
-__device__ __forceinline__ float from_bits(uint16_t b) {
-    if constexpr (DT == F16) return f16_bits_to_f32(b);
-    else return bf16_bits_to_f32(b);
-}
 
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
     // See k_h_pp.hip: inline asm keeps the compiler from draining these
@@ -226,24 +216,27 @@ __global__ __launch_bounds__(NT, (BN == 32 ? 2 : 1)) void k_skinny(Problem p) {
         }
     __syncthreads();
     uint16_t* C = (uint16_t*)p.C;
-    for (int e = tid * 4; e < MT * BN; e += NT * 4) {
-        const int m = e / BN, n = e % BN;
-        if (m >= M) continue;
-        f32x4 s = *(const f32x4*)(red + m * BN + n);
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
+        for (int e = tid * 4; e < MT * BN; e += NT * 4) {
+            const int m = e / BN, n = e % BN;
+            if (m >= M) continue;
+            f32x4 s = *(const f32x4*)(red + m * BN + n);
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) {
-            const f32x4 t = *(const f32x4*)(red + (ww * MT + m) * BN + n);
-            s = s + t;
-        }
-        uint16_t* crow = C + (int64_t)m * p.ldc + n0;
+            for (int ww = 1; ww < NW; ++ww) {
+                const f32x4 t = *(const f32x4*)(red + (ww * MT + m) * BN + n);
+                s = s + t;
+            }
+            uint16_t* crow = C + (int64_t)m * p.ldc + n0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (n + q >= nlim) break;
-            float v = p.alpha * s[q];
-            if (p.beta != 0.f) v = fmaf(p.beta, from_bits<DT>(crow[n + q]), v);
-            crow[n + q] = to_bits<DT>(apply_epilogue<DT>(v, p.epilogue));
+            for (int q = 0; q < 4; ++q) {
+                if (n + q >= nlim) break;
+                float v = p.alpha * s[q];
+                if (p.beta != 0.f) v = fmaf(p.beta, from_bits<DT>(crow[n + q]), v);
+                crow[n + q] = to_bits<DT>(epilogue_op<DT, EPI>(v));
+            }
         }
-    }
+    });
 }
 
 template <int DT, int MT, int BN>

@@ -64,16 +64,6 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-template <int DT>
-__device__ __forceinline__ uint16_t to_bits(float v) {
-    if constexpr (DT == F16) return f32_to_f16_bits(v);
-    else return f32_to_bf16_bits(v);
-}
-template <int DT>
-__device__ __forceinline__ float from_bits(uint16_t b) {
-    if constexpr (DT == F16) return f16_bits_to_f32(b);
-    else return bf16_bits_to_f32(b);
-}
 
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
     // Inline asm keeps the compiler from draining these copies before LDS
@@ -362,34 +352,17 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     uint16_t* C = (uint16_t*)p.C;
     const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
     if (n >= nlim) return;
-    for (int m = w; m < M; m += 4) {
-        const f32x4 tot = *(const f32x4*)(red + m * RED_LD + n);
-        uint16_t* crow = C + (int64_t)m * p.ldc + n0;
-        float v[4];
+    with_epilogue(p.epilogue, [&](auto E) {
+        constexpr int EPI = decltype(E)::value;
+        for (int m = w; m < M; m += 4) {
+            const f32x4 tot = *(const f32x4*)(red + m * RED_LD + n);
+            uint16_t* crow = C + (int64_t)m * p.ldc + n0;
+            float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = p.alpha * tot[e];
-        if (vec_ok && n + 4 <= nlim) {
-            uint32_t* d = (uint32_t*)(crow + n);
-            if (p.beta != 0.f) {
-                const uint32_t c0 = d[0], c1 = d[1];
-                v[0] = fmaf(p.beta, from_bits<DT>((uint16_t)c0), v[0]);
-                v[1] = fmaf(p.beta, from_bits<DT>((uint16_t)(c0 >> 16)), v[1]);
-                v[2] = fmaf(p.beta, from_bits<DT>((uint16_t)c1), v[2]);
-                v[3] = fmaf(p.beta, from_bits<DT>((uint16_t)(c1 >> 16)), v[3]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = apply_epilogue<DT>(v[e], p.epilogue);
-            const uint32_t w0 = (uint32_t)to_bits<DT>(v[0]) | ((uint32_t)to_bits<DT>(v[1]) << 16);
-            const uint32_t w1 = (uint32_t)to_bits<DT>(v[2]) | ((uint32_t)to_bits<DT>(v[3]) << 16);
-            *(uint2*)d = make_uint2(w0, w1);
-        } else {
-            for (int e = 0; e < 4 && n + e < nlim; ++e) {
-                float x = v[e];
-                if (p.beta != 0.f) x = fmaf(p.beta, from_bits<DT>(crow[n + e]), x);
-                crow[n + e] = to_bits<DT>(apply_epilogue<DT>(x, p.epilogue));
-            }
+            for (int e = 0; e < 4; ++e) v[e] = p.alpha * tot[e];
+            store_out4<DT, EPI>(crow, n, nlim, vec_ok, p.beta, v);
         }
-    }
+    });
 }
 
 template <int DT, int MT>

@@ -54,6 +54,8 @@ mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layo
     p.dtype = (int)dtype;
     p.num_cu = h->num_cu;
     p.epilogue = mgemm::EPI_NONE;
+    p.B2 = nullptr;
+    p.ldb2 = 0;
     if (rowA) {
         // Row-major C = A B.  A row-major is K-contiguous; B row-major is
         // N-contiguous, column-major is K-contiguous.
@@ -257,6 +259,32 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
                             hipStream_t stream) {
     return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                     dtype, epilogue, stream);
+}
+
+mgemm_status_t mgemm_run_gated(mgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* X,
+                               int64_t ldx, const void* Wg, const void* Wu, int64_t ldw, void* Z,
+                               int64_t ldz, mgemm_dtype_t dtype, hipStream_t stream) {
+    if (dtype != MGEMM_F16 && dtype != MGEMM_BF16) {
+        if (!valid_dtype(dtype)) return MGEMM_ERR_INVALID_ARG;
+    }
+    Problem p;
+    mgemm_status_t st = make_problem(h, MGEMM_ROW_MAJOR, MGEMM_ROW_MAJOR, M, N, K, 1.0f, X, ldx,
+                                     Wg, ldw, 0.0f, Z, ldz, dtype, &p);
+    if (st != MGEMM_SUCCESS) return st;
+    if (M > 0 && N > 0 && K > 0 && Wu == nullptr) return MGEMM_ERR_INVALID_ARG;
+    if (dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_ERR_UNSUPPORTED;
+    if (p.M == 0 || p.N == 0) return MGEMM_SUCCESS;
+    p.B2 = Wu;
+    p.ldb2 = ldw;
+    if (p.K == 0) {
+        // G = U = 0, so Z = SiLU(0) * 0 = 0.
+        p.beta = 0.0f;
+        hipError_t e = mgemm::launch_scale(p, stream);
+        return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+    }
+    if (!mgemm::h_gated_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+    hipError_t e = mgemm::launch_h_gated(p, stream);
+    return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
 mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,

@@ -162,6 +162,30 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
                             hipStream_t stream);
 
 /*
+ * mgemm_run_gated -- the gated FFN pair Z = SiLU(X * W_g) (.) (X * W_u) in one
+ * kernel ("Chapter 5: Operators and Runtime" (ai-infra-book), section 5.3.1:
+ * G = X W_g, U = X W_u, Z = SiLU(G) multiplied elementwise by U; fused, the
+ * intermediate results keep their rounding, Figure 5-14).
+ *   X   : M x K, row-major, leading dimension ldx >= max(1, K);
+ *   W_g, W_u : K x N each, row-major, one shared leading dimension
+ *         ldw >= max(1, N);
+ *   Z   : M x N, row-major, ldz >= max(1, N); written, never read.
+ *   dtype : MGEMM_F16 or MGEMM_BF16 for all four matrices.
+ * Per output, with FP32 sums g and u over the whole K range:
+ *   Z = round(round(SiLU(round(g))) * round(u))
+ * (G, U and T = SiLU(G) rounded as if they were stored tensors).  K == 0
+ * gives Z = 0.  Asynchronous on `stream`, like mgemm_run.
+ * Errors: MGEMM_ERR_INVALID_ARG for a violated size/leading-dimension rule or
+ * a NULL pointer with a nonzero extent; MGEMM_ERR_UNSUPPORTED for MGEMM_F32,
+ * K % 32 != 0, N % 8 != 0, leading dimensions that are not multiples of 8
+ * or bases that are not 16-byte aligned (nothing enqueued);
+ * MGEMM_ERR_HIP if the launch fails.
+ */
+mgemm_status_t mgemm_run_gated(mgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* X,
+                               int64_t ldx, const void* Wg, const void* Wu, int64_t ldw, void* Z,
+                               int64_t ldz, mgemm_dtype_t dtype, hipStream_t stream);
+
+/*
  * mgemm_select_kernel -- the variant mgemm_run would launch for this problem
  * (validates the arguments exactly as mgemm_run does; pointers are only
  * inspected for alignment and may be any value with the intended alignment).

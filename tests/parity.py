@@ -205,3 +205,41 @@ def check_silu(case: Case, A, B, C0, Cin, Cout, rows=None, exact_gemm=False):
     pad = padding_mask(case)
     assert np.array_equal(storage_view(Cout)[pad], storage_view(Cin)[pad]), "%s: wrote outside C" % case.name
     return float(np.max(err)) if err.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# Gated pair: Z = round(T * round(U)), T = round(SiLU(round(G))).
+#   * exact GEMMs (integer data): G and U round exactly as in the oracle; T
+#     may land one unit of the format away (FP32 SiLU), which moves T*U by
+#     |U| ulp(T): |Z - Z_exact| <= |U| ulp(T) + ulp(Z);
+#   * general data: dT <= 1.1 (tol + ulp(G)) + ulp(T), dU <= tol + ulp(U),
+#     |Z - Z_exact| <= |U| dT + |T| dU + dT dU + ulp(Z).
+# ---------------------------------------------------------------------------
+def check_gated(case: Case, X, Wg, Wu, Zout, rows=None, exact_gemm=False):
+    xs, gs, us = storage_view(X), storage_view(Wg), storage_view(Wu)
+    r = None if rows is None else np.asarray(rows, np.int64)
+    kw = dict(rows=r)
+    g = oracle.gemm("row", "row", case.M, case.N, case.K, 1.0, xs, case.lda, gs, case.ldb, 0.0,
+                    None, None, case.ldc, case.dtype, **kw)
+    u = oracle.gemm("row", "row", case.M, case.N, case.K, 1.0, xs, case.lda, us, case.ldb, 0.0,
+                    None, None, case.ldc, case.dtype, **kw)
+    z = oracle.swiglu(case.dtype, g, u)
+    t_r = oracle.round_to(case.dtype, oracle.silu_epilogue(case.dtype, g))
+    u_r = oracle.round_to(case.dtype, u)
+    g_r = oracle.round_to(case.dtype, g)
+    uz = _ulp(case.dtype, oracle.round_to(case.dtype, z))
+    ut = _ulp(case.dtype, t_r)
+    if exact_gemm:
+        bound = np.abs(u_r) * ut + uz
+    else:
+        tol = tol_half(case.K)
+        dT = 1.1 * (tol + _ulp(case.dtype, g_r)) + ut
+        dU = tol + _ulp(case.dtype, u_r)
+        bound = np.abs(u_r) * dT + np.abs(t_r) * dU + dT * dU + uz
+    got_all = oracle.decode(case.dtype, storage_view(Zout)).reshape(-1, case.ldc)[: case.M, : case.N]
+    got = got_all if rows is None else got_all[np.asarray(rows)]
+    err = np.abs(got - z)
+    bad = np.argwhere(~(err <= bound))
+    assert bad.size == 0, "%s: %d outputs off, first %s: got %r want %r (bound %r)" % (
+        case.name, len(bad), tuple(bad[0]), got[tuple(bad[0])], z[tuple(bad[0])], bound[tuple(bad[0])])
+    return float(np.max(err)) if err.size else 0.0

@@ -269,6 +269,52 @@ def test_silu_k_zero_and_bad_epilogue(h):
 
 
 # ---------------------------------------------------------------------------
+# Gated pair Z = SiLU(X W_g) * (X W_u) (mgemm_run_gated)
+# ---------------------------------------------------------------------------
+def _run_gated(h, case, inputs):
+    X, Wg, Wu = inputs
+    Z = P.c_initial(case, None)
+    dZ = Z.cuda()
+    mg.mgemm_run_gated(h, case.M, case.N, case.K, X.cuda(), case.lda, Wg.cuda(), Wu.cuda(),
+                       case.ldb, dZ, case.ldc, case.dtype)
+    torch.cuda.synchronize()
+    return Z, dZ.cpu()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 64), (256, 96, 32), (130, 520, 96), (37, 104, 160)])
+def test_gated_pair_integer(h, dtype, M, N, K):
+    case = W.Case("gated", M, N, K, dtype, kindA="int", kindB="int", seeds=(M, N, K),
+                  extra={"gated": True, "seed_u": K + 7})
+    inputs = W.gated_inputs(case)
+    Zin, Zout = _run_gated(h, case, inputs)
+    say("gated", dtype, (M, N, K))
+    P.check_gated(case, *inputs, Zout, exact_gemm=True)
+    pad = P.padding_mask(case)
+    assert np.array_equal(W.storage_view(Zout)[pad], W.storage_view(Zin)[pad])
+
+
+def test_gated_pair_ffn_sampled(h):
+    case = W.ffn_gated_bf16()
+    inputs = W.gated_inputs(case)
+    say("gated ffn")
+    _, Zout = _run_gated(h, case, inputs)
+    P.check_gated(case, *inputs, Zout, rows=P.sample_rows(case.M, 256, extra=8))
+
+
+def test_gated_pair_unsupported_and_k_zero(h):
+    A = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_gated(h, 16, 64, 64, A, 64, A, A, 64, A, 64, "f32")
+    assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
+    Z = torch.full((16 * 64,), 3.0, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
+    mg.mgemm_run_gated(h, 16, 64, 0, B, 1, B, B, 64, Z, 64, "bf16")
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Z).item() == 0
+
+
+# ---------------------------------------------------------------------------
 # Contract details
 # ---------------------------------------------------------------------------
 def test_beta_zero_ignores_nan_c(h):

@@ -162,6 +162,24 @@ def ffn_bf16_silu() -> Case:
     return c
 
 
+def ffn_gated_bf16(M: int = 1024) -> Case:
+    """Gate/up pair of the FFN: X[Mx4096] with W_g and W_u [4096x12288], both
+    N(0, 0.02^2).  X and W_g are those of ffn_bf16(); W_u has its own seed
+    (extra["seed_u"]).  Z = SiLU(X W_g) * (X W_u)."""
+    c = ffn_bf16(M)
+    c.name = "ffn_gated_bf16_m%d" % M
+    c.extra = {"gated": True, "seed_u": 4004}
+    return c
+
+
+def gated_inputs(case: Case):
+    """(X, W_g, W_u) CPU tensors of a gated-pair case."""
+    X, Wg, _ = case.make()
+    Wu = operand(case.kindB, case.extra["seed_u"], case.K, case.N, "row", case.ldb, case.dtype,
+                 case.scaleB)
+    return X, Wg, Wu
+
+
 SKINNY_M = [1, 16, 64]
 
 
