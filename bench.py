@@ -44,6 +44,7 @@ KERNEL_SOURCE = {
     "h_mfma_256x192": "k_h_mfma.hip", "h_mfma_128x128": "k_h_mfma.hip",
     "h_pp_256x256": "k_h_pp.hip", "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
     "skinny_sk": "k_skinny_sk.hip", "h_dma_256x192": "k_h_dma.hip", "f32_fast_u": "k_f32_mfma.hip",
+    "h_dma_gated": "k_h_dma.hip",
 }
 
 
@@ -64,7 +65,8 @@ def src_hash(kernel: str | None = None) -> str:
 def workload_table():
     import workloads as W
     t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
-         "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu()}
+         "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu(),
+         "ffn_gated_bf16": W.ffn_gated_bf16()}
     for s in W.HGEMM_SHAPES:
         c = W.hgemm_colmajor(*s)
         t[c.name] = c
@@ -77,6 +79,9 @@ def workload_table():
 def algorithmic(case):
     from dense_gemm_mgemm_amd import costmodel as cm
     es = 4 if case.dtype == "f32" else 2
+    if case.extra.get("gated"):     # two products sharing X; one output
+        flops = 2 * cm.gemm_flops(case.M, case.N, case.K)
+        return flops, es * (case.M * case.K + 2 * case.K * case.N + case.M * case.N)
     flops = cm.gemm_flops(case.M, case.N, case.K)
     nbytes = cm.min_bytes(case.M, case.N, case.K, es) + (es * case.M * case.N if case.beta else 0)
     return flops, nbytes
@@ -86,37 +91,55 @@ def is_hbm_bound(case) -> bool:
     return case.dtype != "f32" and case.M <= 64
 
 
-def measure(h, case, steps, warmup, rotate=1):
-    """Time `steps` launches; returns timings, the kernel name and device buffers."""
+def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
+    """Time `steps` launches after `warmup` untimed ones (continued until
+    `warm_s` seconds have passed, so short kernels run at a settled clock);
+    returns timings, the kernel name and device buffers."""
     import torch
     import dense_gemm_mgemm_amd as mg
     from tests.parity import c_initial
 
-    A, B, C0 = case.make()
-    dA = [A.cuda() for _ in range(rotate)]
-    dB = [B.cuda() for _ in range(rotate)]
-    dC = [c_initial(case, C0).cuda() for _ in range(rotate)]
     stream = torch.cuda.current_stream()
-    kname = mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
-                                   case.alpha, dA[0], case.lda, dB[0], case.ldb, case.beta, dC[0],
-                                   case.ldc, case.dtype)
-
     epilogue = case.extra.get("epilogue", "none")
+    if case.extra.get("gated"):
+        import workloads as W
+        X, Wg, Wu = W.gated_inputs(case)
+        A, B, C0 = X, (Wg, Wu), None
+        dX, dWg, dWu = X.cuda(), Wg.cuda(), Wu.cuda()
+        dC = [c_initial(case, None).cuda()]
+        kname = "h_dma_gated"
 
-    def launch(i):
-        j = i % rotate
-        if epilogue != "none":
-            mg.mgemm_run_ex(h, "auto", case.layoutA, case.layoutB, case.M, case.N, case.K,
-                            case.alpha, dA[j], case.lda, dB[j], case.ldb, case.beta, dC[j],
-                            case.ldc, case.dtype, epilogue=epilogue, stream=stream)
-            return
-        mg.mgemm_run(h, case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, dA[j],
-                     case.lda, dB[j], case.ldb, case.beta, dC[j], case.ldc, case.dtype,
-                     stream=stream)
+        def launch(i):
+            mg.mgemm_run_gated(h, case.M, case.N, case.K, dX, case.lda, dWg, dWu, case.ldb,
+                               dC[0], case.ldc, case.dtype, stream=stream)
+    else:
+        A, B, C0 = case.make()
+        dA = [A.cuda() for _ in range(rotate)]
+        dB = [B.cuda() for _ in range(rotate)]
+        dC = [c_initial(case, C0).cuda() for _ in range(rotate)]
+        kname = mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
+                                       case.alpha, dA[0], case.lda, dB[0], case.ldb, case.beta,
+                                       dC[0], case.ldc, case.dtype)
+
+        def launch(i):
+            j = i % rotate
+            if epilogue != "none":
+                mg.mgemm_run_ex(h, "auto", case.layoutA, case.layoutB, case.M, case.N, case.K,
+                                case.alpha, dA[j], case.lda, dB[j], case.ldb, case.beta, dC[j],
+                                case.ldc, case.dtype, epilogue=epilogue, stream=stream)
+                return
+            mg.mgemm_run(h, case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha,
+                         dA[j], case.lda, dB[j], case.ldb, case.beta, dC[j], case.ldc,
+                         case.dtype, stream=stream)
 
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < warm_s:
+        for i in range(8):
+            launch(i)
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -136,7 +159,7 @@ def measure(h, case, steps, warmup, rotate=1):
         "kernel": kname, "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
         "launch_ms_mean": sum(per) / len(per), "launch_ms_median": per[len(per) // 2],
         "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
-        "inputs": (A, B, C0), "out": dC[(steps - 1) % rotate],
+        "inputs": (A, B, C0), "out": dC[(steps - 1) % len(dC)],
     }
 
 
@@ -149,33 +172,44 @@ def cpu_baseline(case, out_dev, budget_s):
     from workloads import storage_view
 
     A, B, C0 = case.inputs
-    a, b = storage_view(A), storage_view(B)
+    gated = bool(case.extra.get("gated"))
+    a = storage_view(A)
+    bs = [storage_view(x) for x in (B if gated else (B,))]
     c0 = None if C0 is None else storage_view(C0)
     threads = oracle.max_threads()
     nrows = max(1, min(case.M, 16))
     rng = np.random.default_rng(0)
-    spent, rows_done, t_total, results = 0.0, [], 0.0, []
+    rows_done, t_total, results = [], 0.0, []
     while True:
         rows = np.sort(rng.choice(case.M, size=nrows, replace=False)) if nrows < case.M \
             else np.arange(case.M)
         t0 = time.perf_counter()
-        exact = oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
-                            case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
-                            rows=rows, nthreads=threads)
+        exact = [oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
+                             case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
+                             rows=rows, nthreads=threads) for b in bs]
+        if gated:
+            exact.append(oracle.swiglu(case.dtype, exact[0], exact[1]))
         dt = time.perf_counter() - t0
         t_total, rows_done, results = dt, rows, exact
         if nrows >= case.M or dt * 2 > budget_s:
             break
         nrows = int(min(case.M, max(nrows * 2, nrows * budget_s / max(dt, 1e-3) * 0.8)))
-    flops = 2.0 * len(rows_done) * case.N * case.K
-    got = P.logical(case, oracle.decode(case.dtype, storage_view(out_dev.cpu())))[rows_done]
-    if case.extra.get("epilogue") == "silu":
-        y, bound = P.silu_reference(case, results)
-        err = np.abs(got - y)
-        rep = {"ok": bool(np.all(err <= bound)), "max_err": float(np.max(err)),
-               "tol": float(np.max(bound))}
+    flops = 2.0 * len(rows_done) * case.N * case.K * len(bs)
+    if gated:
+        try:
+            err = P.check_gated(case, A, B[0], B[1], out_dev.cpu(), rows=rows_done)
+            rep = {"ok": True, "max_err": err, "tol": None}
+        except AssertionError as e:
+            rep = {"ok": False, "max_err": None, "tol": None, "what": str(e)[:200]}
     else:
-        rep = P.compare(case, got, results)
+        got = P.logical(case, oracle.decode(case.dtype, storage_view(out_dev.cpu())))[rows_done]
+        if case.extra.get("epilogue") == "silu":
+            y, bound = P.silu_reference(case, results[0])
+            err = np.abs(got - y)
+            rep = {"ok": bool(np.all(err <= bound)), "max_err": float(np.max(err)),
+                   "tol": float(np.max(bound))}
+        else:
+            rep = P.compare(case, got, results[0])
     return ({"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
              "kind": "oracle", "sample": "%d of %d rows of C (%.1f GFLOP in %.1f s, FP64)" % (
                  len(rows_done), case.M, flops / 1e9, t_total)},
@@ -289,7 +323,7 @@ def main():
             f2, b2 = algorithmic(c)
             hb = is_hbm_bound(c)
             log("workload:", name)
-            rr = measure(h, c, 20, 5, rotate=4 if hb else 1)
+            rr = measure(h, c, 20, 5, rotate=4 if hb else 1, warm_s=0.25)
             s = rr["launch_ms_mean"] * 1e-3
             ent = {"kernel": rr["kernel"], "launch_ms_mean": round(rr["launch_ms_mean"], 5),
                    "dtype": c.dtype}

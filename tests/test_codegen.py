@@ -42,8 +42,12 @@ def test_m0_only_written_by_our_copies(name, tmp_path):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 # k_h_mfma.hip is left out: its 256x256 register-staged instantiations hold
-# 256 accumulators plus a full slice of prefetch registers and spill one VGPR.
-@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip"])
+# 256 accumulators plus a full slice of prefetch registers and spill a few
+# VGPRs outside the main loop.  Scratch memory also appears when a store loop
+# over the accumulators is too large to unroll fully (the array then lives in
+# memory), so the per-lane scratch size must be zero as well.
+@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip",
+                                  "k_h_dma.hip", "k_general.hip"])
 def test_no_register_spills(name, tmp_path):
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-c", "-O3",
                         "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -52,6 +56,8 @@ def test_no_register_spills(name, tmp_path):
                        capture_output=True, text=True, check=True)
     spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", r.stderr)]
     assert spills and max(spills) == 0, r.stderr[-2000:]
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)]
+    assert len(scratch) == len(spills) and max(scratch) == 0, r.stderr[-2000:]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
