@@ -54,7 +54,7 @@ def src_hash(kernel: str | None = None) -> str:
     if kernel is None:
         files = [f for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h", ".cpp"))]
     else:
-        files = ["common.h", KERNEL_SOURCE[kernel]]
+        files = ["common.h", KERNEL_SOURCE[kernel.split("/")[0]]]
     h = hashlib.sha256()
     for f in files:
         h.update(f.encode())
@@ -66,7 +66,8 @@ def workload_table():
     import workloads as W
     t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
          "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu(),
-         "ffn_gated_bf16": W.ffn_gated_bf16()}
+         "ffn_gated_bf16": W.ffn_gated_bf16(), "ffn_share_bf16": W.ffn_share_bf16(),
+         "ffn_gated_share_bf16": W.ffn_gated_share_bf16()}
     for s in W.HGEMM_SHAPES:
         c = W.hgemm_colmajor(*s)
         t[c.name] = c
@@ -117,9 +118,11 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
         dA = [A.cuda() for _ in range(rotate)]
         dB = [B.cuda() for _ in range(rotate)]
         dC = [c_initial(case, C0).cuda() for _ in range(rotate)]
-        kname = mg.mgemm_select_kernel(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
-                                       case.alpha, dA[0], case.lda, dB[0], case.ldb, case.beta,
-                                       dC[0], case.ldc, case.dtype)
+        kname, ks = mg.mgemm_select_variant(h, case.layoutA, case.layoutB, case.M, case.N,
+                                            case.K, case.alpha, dA[0], case.lda, dB[0], case.ldb,
+                                            case.beta, dC[0], case.ldc, case.dtype)
+        if ks > 1:
+            kname += "/k%d" % ks
 
         def launch(i):
             j = i % rotate

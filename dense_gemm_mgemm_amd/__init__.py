@@ -31,8 +31,8 @@ _LAYOUT = {"row": MGEMM_ROW_MAJOR, "col": MGEMM_COL_MAJOR}
 _DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
 
 EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
-            "mgemm_run_gated",
-            "mgemm_select_kernel", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
+            "mgemm_run_variant", "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_select_kernel",
+            "mgemm_select_variant", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
 
 
 class MgemmError(RuntimeError):
@@ -42,6 +42,13 @@ class MgemmError(RuntimeError):
 
 
 _lib = None
+
+MGEMM_MAX_KSPLIT = 32
+
+
+class MgemmVariant(ctypes.Structure):
+    """mgemm_variant_t: a kernel (mgemm_kernel_t) and its number of K ranges."""
+    _fields_ = [("kernel", ctypes.c_int32), ("ksplit", ctypes.c_int32)]
 
 
 def load(path: str | None = None):
@@ -61,9 +68,14 @@ def load(path: str | None = None):
     lib.mgemm_run_kernel.argtypes = [vp, ci] + run_args
     lib.mgemm_run_ex.argtypes = [vp, ci] + run_args[:-1] + [ci, vp]
     lib.mgemm_run_gated.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i64, vp, i64, ci, vp]
+    lib.mgemm_run_gated_ex.argtypes = [vp, ctypes.c_int32, i64, i64, i64, vp, i64, vp, vp, i64, vp,
+                                       i64, ci, vp]
+    lib.mgemm_run_variant.argtypes = [vp, ctypes.POINTER(MgemmVariant)] + run_args[:-1] + [ci, vp]
+    lib.mgemm_select_variant.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(MgemmVariant)]
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
     for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
-                 "mgemm_run_gated", "mgemm_select_kernel"):
+                 "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
+                 "mgemm_select_variant", "mgemm_select_kernel"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
@@ -158,6 +170,38 @@ def mgemm_run_gated(h, M, N, K, X, ldx, Wg, Wu, ldw, Z, ldz, dtype, stream=None)
                                 int(ldw), _ptr(Z), int(ldz), _enum(dtype, _DTYPE), _stream(stream))
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_run_gated")
+
+
+def mgemm_run_variant(h, kernel, ksplit, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                      ldc, dtype, epilogue="none", stream=None) -> None:
+    """As mgemm_run_ex with a split of K (0: the library's choice, 1: none, n: at most n ranges)."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    v = MgemmVariant(k, int(ksplit))
+    st = load().mgemm_run_variant(h, ctypes.byref(v), *_args(layoutA, layoutB, M, N, K, alpha, A,
+                                                             lda, B, ldb, beta, C, ldc, dtype),
+                                  _enum(epilogue, _EPILOGUE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_variant(%s, %d)" % (kernel, ksplit))
+
+
+def mgemm_run_gated_ex(h, ksplit, M, N, K, X, ldx, Wg, Wu, ldw, Z, ldz, dtype, stream=None) -> None:
+    """mgemm_run_gated with a split of K (0: the library's choice)."""
+    st = load().mgemm_run_gated_ex(h, int(ksplit), int(M), int(N), int(K), _ptr(X), int(ldx),
+                                   _ptr(Wg), _ptr(Wu), int(ldw), _ptr(Z), int(ldz),
+                                   _enum(dtype, _DTYPE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_gated_ex(%d)" % ksplit)
+
+
+def mgemm_select_variant(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         dtype) -> tuple:
+    """(kernel name, K ranges) that mgemm_run would launch (("auto", 0): scale-only or nothing)."""
+    out = MgemmVariant()
+    st = load().mgemm_select_variant(h, *_args(layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb,
+                                               beta, C, ldc, dtype), ctypes.byref(out))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_select_variant")
+    return load().mgemm_kernel_name(out.kernel).decode(), int(out.ksplit)
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

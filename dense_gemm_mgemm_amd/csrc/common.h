@@ -56,13 +56,17 @@ struct Workspace {
 // resource model (GROUP_SIZE_M) and the M-first CTA order of the MTT S4000
 // write-up (section 14), made XCD-aware.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
-                                              int group_m, int& tm, int& tn) {
+// Workgroup id -> position in an order where each XCD's workgroups are consecutive.
+__device__ __forceinline__ int xcd_linear(int bid, int nblocks) {
     constexpr int NXCD = 8;
     int xcd = bid % NXCD;
     int local = bid / NXCD;
     int q = nblocks / NXCD, r = nblocks % NXCD;
-    int t = xcd * q + (xcd < r ? xcd : r) + local;
+    return xcd * q + (xcd < r ? xcd : r) + local;
+}
+// Position t -> (tm, tn) in the M-grouped order.
+__device__ __forceinline__ void tile_from_linear(int t, int tiles_m, int tiles_n, int group_m,
+                                                 int& tm, int& tn) {
     int per_group = group_m * tiles_n;
     int g = t / per_group;
     int first_m = g * group_m;
@@ -70,6 +74,10 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m,
     int within = t - g * per_group;
     tm = first_m + within % gsize;
     tn = within / gsize;
+}
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int group_m, int& tm, int& tn) {
+    tile_from_linear(xcd_linear(bid, nblocks), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // ---------------------------------------------------------------------------
@@ -241,12 +249,18 @@ bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_h_pp(const Problem& p, hipStream_t s);
 bool h_pp_supports(const Problem& p);
-hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s);
+// Direct-to-LDS FP16/BF16 kernel.  ksplit > 1 cuts K into that many ranges
+// (two launches, partials in ws); h_dma_splits gives the number of ranges a
+// request for at most `requested` turns into (whole 32-slices per range; 1
+// for requests <= 1), 0 when the partials would not fit the workspace.
+constexpr int MAX_KSPLIT = 32;
+int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws);
+hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s);
 bool h_gated_supports(const Problem& p);
-hipError_t launch_h_gated(const Problem& p, hipStream_t s);
+hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s);
 bool skinny_sk_supports(const Problem& p);
-int skinny_sk_splits(const Problem& p, const Workspace& ws);
-hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s);
+int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested);
+hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s);
 bool h_dma_supports(const Problem& p, int bn);
 bool skinny_supports(const Problem& p);
 

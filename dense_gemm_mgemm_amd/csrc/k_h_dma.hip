@@ -45,6 +45,16 @@
 // for BN = 256, 2 2/3 rows for BN = 192).  B fragments come from
 // ds_read_b64_tr_b16; rows past M and columns past N of an edge tile are read
 // from the last valid row/chunk and never stored.
+// Split K: when a grid of tiles fills the CUs badly (the 1024x1536 share of
+// the FFN projection is 32 tiles on 256 CUs), each tile's K slices are cut
+// into ksplit ranges of whole slices, one workgroup per (tile, range).  Each
+// workgroup stores its FP32 accumulators in the handle's workspace, in
+// register order (16-byte chunks, thread-contiguous, so every store and load
+// of the exchange is fully coalesced), and a second kernel on the same stream
+// sums the ranges of every output in range order and applies the epilogue.
+// The sum order is fixed, so results do not depend on timing; the kernel
+// boundary orders the two phases, so no atomics or fences are needed.
+//
 // Restrictions (host-checked): A' K-contiguous, B' N-contiguous, K % 32 == 0,
 // N % 8 == 0, lda and ldb multiples of 8, 16-byte aligned bases.
 #include "common.h"
@@ -57,6 +67,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Epilogue of the first split-K phase: FP32 accumulators to the workspace.
+constexpr int EPI_PARTIAL = 2;
+
+// K-range arguments.  Without a split: ksplit = 1, nks = K / 32, part unused.
+struct HSplit {
+    float* part;    // [tile][range][chunk][thread] f32x4, tile = tm * tiles_n + tn
+    int ksplit;     // number of K ranges
+    int nks;        // 32-slices per range (the last range may hold fewer)
+};
 
 #ifndef MGEMM_DMA_SLOTS
 #define MGEMM_DMA_SLOTS 4
@@ -143,7 +164,7 @@ struct Frags {
 };
 
 template <int DT, int BN, bool DUAL, int EPI>
-__global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
+__global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     using G = Cfg<BN, DUAL>;
     constexpr int TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
     constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
@@ -155,8 +176,15 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     const int wm = DUAL ? wave : wave >> 1, wn = DUAL ? 0 : wave & 1;
 
     const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + OUT - 1) / OUT);
+    // Workgroups of one XCD take consecutive positions; a position is
+    // range * tiles + tile, so an XCD works on few K ranges at a time and its
+    // L2 holds their A and B panels.
+    const int ntiles = tiles_m * tiles_n;
+    const int pos = xcd_linear(blockIdx.x, gridDim.x);
+    const int split = pos / ntiles;
     int tmi, tni;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+    tile_from_linear(pos - split * ntiles, tiles_m, tiles_n, 8, tmi, tni);
+    const int j0 = split * sp.nks;                        // first 32-slice of this range
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < OUT ? p.N - n0 : OUT);
@@ -174,7 +202,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         const int r = 64 * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ a_swz(r);
         const int rr = r < mlim ? r : mlim - 1;
-        src[i] = A + (m0 + rr) * p.lda + 8 * c;
+        src[i] = A + (m0 + rr) * p.lda + (int64_t)j0 * BK + 8 * c;
         dst[i] = (64 * wave + 16 * i) * A_ROW;
     }
 #pragma unroll
@@ -189,10 +217,10 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
             const bool second = c >= G::B_CHUNKS / 2;
             int cc = second ? c - G::B_CHUNKS / 2 : c;
             cc = cc <= cmax ? cc : cmax;
-            src[A_COPIES + i] = (second ? B2 : B) + (int64_t)k * p.ldb + n0 + 8 * cc;
+            src[A_COPIES + i] = (second ? B2 : B) + ((int64_t)j0 * BK + k) * p.ldb + n0 + 8 * cc;
         } else {
             c = c <= cmax ? c : cmax;
-            src[A_COPIES + i] = B + (int64_t)k * p.ldb + n0 + 8 * c;
+            src[A_COPIES + i] = B + ((int64_t)j0 * BK + k) * p.ldb + n0 + 8 * c;
         }
         dst[A_COPIES + i] = A_BYTES + j * 1024;
     }
@@ -274,7 +302,8 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         }
     };
 
-    const int nk = (int)(p.K / BK);
+    const int nk_all = (int)(p.K / BK);
+    const int nk = nk_all - j0 < sp.nks ? nk_all - j0 : sp.nks;
     // Prologue: request slices 0..AHEAD-1, make slice 0 visible, read (0, ks=0).
     const int npro = nk < AHEAD ? nk : AHEAD;
     for (int s = 0; s < npro; ++s)
@@ -305,6 +334,23 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
         if (next) slice_barrier();
         kstep(f0, f1, true, j, 1, false, 0, 0, 1);
         kstep(f1, f0, next, j + 1, 0, false, 0, 0, 1);
+    }
+
+    if constexpr (EPI == EPI_PARTIAL) {
+        // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3].
+        float* dst = sp.part + ((int64_t)(tmi * tiles_n + tni) * sp.ksplit + split) *
+                                   (int64_t)(NT * TM * TN * 16) + 4 * tid;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& a = acc[tm][tn];
+                    const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    *(f32x4*)(dst + (int64_t)((tm * TN + tn) * 4 + q) * NT * 4) = v;
+                }
+        return;
     }
 
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
@@ -347,8 +393,67 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p) {
     }
 }
 
+// Second split-K phase: one thread per 16-byte chunk of one tile's
+// accumulators (the chunk and thread of the first phase), sums the K ranges in
+// range order and stores four outputs as the one-phase epilogue would.  The
+// gated pair's threads take a G chunk and the U chunk of the same outputs.
 template <int DT, int BN, bool DUAL, int EPI>
-hipError_t launch_epi(const Problem& p, hipStream_t s) {
+__global__ __launch_bounds__(NT) void k_h_dma_reduce(Problem p, HSplit sp) {
+    using G = Cfg<BN, DUAL>;
+    constexpr int TM = G::TM, TN = G::TN, OUT = G::OUT;
+    constexpr int TNO = DUAL ? TN / 2 : TN;                 // blocks that hold outputs
+    constexpr int CH = TM * TNO * 4;                        // chunks walked per tile
+    constexpr int64_t TILE_FLOATS = (int64_t)NT * TM * TN * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = DUAL ? wave : wave >> 1, wn = DUAL ? 0 : wave & 1;
+    const int tiles_n = (int)((p.N + OUT - 1) / OUT);
+    const int t = blockIdx.x / CH, c = blockIdx.x % CH;
+    const int tmi = t / tiles_n, tni = t % tiles_n;
+    const int tm = c / (TNO * 4), tn = (c / 4) % TNO, q = c % 4;
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
+    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+    const int nlim = (int)(p.N - n0 < OUT ? p.N - n0 : OUT);
+    const int mi = G::WROWS * wm + 32 * tm + (lane & 31);
+    const int ni = G::WN * wn + 32 * tn + 8 * q + 4 * (lane >> 5);
+    if (mi >= mlim || ni >= nlim) return;
+    const float* tile = sp.part + (int64_t)t * sp.ksplit * TILE_FLOATS + 4 * tid;
+    auto sum = [&](int chunk) {
+        const float* src = tile + (int64_t)chunk * NT * 4;
+        f32x4 a = *(const f32x4*)src;
+        int s = 1;
+        for (; s + 4 <= sp.ksplit; s += 4) {
+            const f32x4 b0 = *(const f32x4*)(src + s * TILE_FLOATS);
+            const f32x4 b1 = *(const f32x4*)(src + (s + 1) * TILE_FLOATS);
+            const f32x4 b2 = *(const f32x4*)(src + (s + 2) * TILE_FLOATS);
+            const f32x4 b3 = *(const f32x4*)(src + (s + 3) * TILE_FLOATS);
+            a = (((a + b0) + b1) + b2) + b3;
+        }
+        for (; s < sp.ksplit; ++s) a = a + *(const f32x4*)(src + s * TILE_FLOATS);
+        return a;
+    };
+    uint16_t* crow = (uint16_t*)p.C + (m0 + mi) * p.ldc + n0;
+    const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
+    const f32x4 g = sum((tm * TN + tn) * 4 + q);
+    float v[4];
+    if constexpr (DUAL) {
+        const f32x4 u = sum((tm * TN + tn + TN / 2) * 4 + q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = swiglu_out<DT>(g[e], u[e]);
+        store_out4<DT, EPI_NONE>(crow, ni, nlim, vec_ok, 0.f, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = p.alpha * g[e];
+        store_out4<DT, EPI>(crow, ni, nlim, vec_ok, p.beta, v);
+    }
+}
+
+template <int BN, bool DUAL>
+constexpr int64_t tile_part_bytes() {
+    return (int64_t)NT * Cfg<BN, DUAL>::TM * Cfg<BN, DUAL>::TN * 16 * (int64_t)sizeof(float);
+}
+
+template <int DT, int BN, bool DUAL, int EPI>
+hipError_t launch_epi(const Problem& p, const HSplit& sp, hipStream_t s) {
     auto kern = k_h_dma<DT, BN, DUAL, EPI>;
     const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
     static bool attr_set = false;     // benign race: every caller sets the same value
@@ -360,7 +465,17 @@ hipError_t launch_epi(const Problem& p, hipStream_t s) {
     }
     constexpr int OUT = Cfg<BN, DUAL>::OUT;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + OUT - 1) / OUT);
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * sp.ksplit)), dim3(NT), lds, s, p, sp);
+    return hipGetLastError();
+}
+
+template <int DT, int BN, bool DUAL, int EPI>
+hipError_t launch_reduce(const Problem& p, const HSplit& sp, hipStream_t s) {
+    using G = Cfg<BN, DUAL>;
+    constexpr int CH = G::TM * (DUAL ? G::TN / 2 : G::TN) * 4;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + G::OUT - 1) / G::OUT);
+    hipLaunchKernelGGL((k_h_dma_reduce<DT, BN, DUAL, EPI>), dim3((unsigned)(tiles * CH)), dim3(NT), 0,
+                       s, p, sp);
     return hipGetLastError();
 }
 
@@ -368,10 +483,22 @@ hipError_t launch_epi(const Problem& p, hipStream_t s) {
 // the tile, so a runtime choice would put the activation's code between the
 // plain stores (and the 256-wide tile has no registers to spare for it).
 template <int DT, int BN, bool DUAL>
-hipError_t launch_dt(const Problem& p, hipStream_t s) {
+hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
+    const int nk = (int)(p.K / BK);
+    HSplit sp{(float*)ws.part, 1, nk};
+    const bool silu = !DUAL && p.epilogue == EPI_SILU;
+    if (ksplit <= 1) {
+        if constexpr (!DUAL)
+            if (silu) return launch_epi<DT, BN, false, EPI_SILU>(p, sp, s);
+        return launch_epi<DT, BN, DUAL, EPI_NONE>(p, sp, s);
+    }
+    sp.nks = (nk + ksplit - 1) / ksplit;
+    sp.ksplit = (nk + sp.nks - 1) / sp.nks;
+    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL>(p, sp, s);
+    if (e != hipSuccess) return e;
     if constexpr (!DUAL)
-        if (p.epilogue == EPI_SILU) return launch_epi<DT, BN, false, EPI_SILU>(p, s);
-    return launch_epi<DT, BN, DUAL, EPI_NONE>(p, s);
+        if (silu) return launch_reduce<DT, BN, false, EPI_SILU>(p, sp, s);
+    return launch_reduce<DT, BN, DUAL, EPI_NONE>(p, sp, s);
 }
 
 }  // namespace
@@ -384,13 +511,28 @@ bool h_dma_supports(const Problem& p, int bn) {
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
-    return tiles > 0 && tiles <= 0x7fffffff;
+    return tiles > 0 && tiles <= 0x7fffffff / 64;
 }
 
-hipError_t launch_h_dma(const Problem& p, int bn, hipStream_t s) {
+int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws) {
+    const int out = dual ? 96 : bn;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + out - 1) / out);
+    const int64_t nk = p.K / BK;
+    const int64_t tile_bytes = bn == 256 ? tile_part_bytes<256, false>() : tile_part_bytes<192, false>();
+    if (requested <= 1 || nk < 2) return 1;
+    int64_t ks = requested < nk ? requested : nk;
+    const int64_t nks = (nk + ks - 1) / ks;                 // whole slices per range
+    ks = (nk + nks - 1) / nks;
+    if (ws.part == nullptr || tiles * ks * tile_bytes > ws.part_bytes) return 0;
+    return (int)ks;
+}
+
+hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s) {
     if (bn == 192)
-        return p.dtype == F16 ? launch_dt<F16, 192, false>(p, s) : launch_dt<BF16, 192, false>(p, s);
-    return p.dtype == F16 ? launch_dt<F16, 256, false>(p, s) : launch_dt<BF16, 256, false>(p, s);
+        return p.dtype == F16 ? launch_dt<F16, 192, false>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 192, false>(p, ksplit, ws, s);
+    return p.dtype == F16 ? launch_dt<F16, 256, false>(p, ksplit, ws, s)
+                          : launch_dt<BF16, 256, false>(p, ksplit, ws, s);
 }
 
 bool h_gated_supports(const Problem& p) {
@@ -398,8 +540,9 @@ bool h_gated_supports(const Problem& p) {
     return ((uintptr_t)p.B2 & 15) == 0;
 }
 
-hipError_t launch_h_gated(const Problem& p, hipStream_t s) {
-    return p.dtype == F16 ? launch_dt<F16, 192, true>(p, s) : launch_dt<BF16, 192, true>(p, s);
+hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
+    return p.dtype == F16 ? launch_dt<F16, 192, true>(p, ksplit, ws, s)
+                          : launch_dt<BF16, 192, true>(p, ksplit, ws, s);
 }
 
 }  // namespace mgemm

@@ -400,28 +400,36 @@ bool skinny_sk_supports(const Problem& p) {
     return (p.N + BNS - 1) / BNS <= 0x7fffffff / 64;
 }
 
-int skinny_sk_splits(const Problem& p, const Workspace& ws) {
+int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested) {
     const int64_t blocks = (p.N + BNS - 1) / BNS;
     const int64_t nk = p.K / KS;
     const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
-    // About three workgroups for every four CUs (the copy-only measurements
-    // peak there), at most 16 ranges and never an empty one.
-    int64_t ks = (3 * slots / 4 + blocks - 1) / blocks;
-    if (ks > 16) ks = 16;
-    if (ks > nk) ks = nk;
-    if (ks < 1) ks = 1;
-    const int64_t need = blocks * ks * mt_of(p.M) * BNS * (int64_t)sizeof(float);
-    if (ks > 1 && (ws.part == nullptr || need > ws.part_bytes || blocks > ws.ncounters)) ks = 1;
+    const int64_t per_range = blocks * mt_of(p.M) * BNS * (int64_t)sizeof(float);
+    const bool room = ws.part != nullptr && blocks <= ws.ncounters;
+    int64_t ks;
+    if (requested <= 0) {
+        // About three workgroups for every four CUs (the copy-only
+        // measurements peak there), at most 16 ranges and never an empty one.
+        ks = (3 * slots / 4 + blocks - 1) / blocks;
+        if (ks > 16) ks = 16;
+        if (ks > nk) ks = nk;
+        if (ks < 1) ks = 1;
+        if (ks > 1 && (!room || ks * per_range > ws.part_bytes)) ks = 1;
+    } else {
+        ks = requested < nk ? requested : nk;
+        if (ks > 1 && (!room || ks * per_range > ws.part_bytes)) return 0;
+    }
     const int64_t per = (nk + ks - 1) / ks;
     return (int)((nk + per - 1) / per);
 }
 
-hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
+hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s) {
     const int64_t blocks = (p.N + BNS - 1) / BNS;
     const int64_t nk = p.K / KS;
     SplitArgs sa;
-    sa.ksplit = skinny_sk_splits(p, ws);
+    sa.ksplit = ksplit < 1 ? 1 : ksplit;
     sa.per = (int)((nk + sa.ksplit - 1) / sa.ksplit);
+    sa.ksplit = (int)((nk + sa.per - 1) / sa.per);
     sa.part = (float*)ws.part;
     sa.part_bytes = (int)(ws.part_bytes < 0x7fffffff ? ws.part_bytes : 0x7fffffff);
     sa.cnt = ws.counters;

@@ -94,8 +94,58 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     }
 }
 
+// A kernel and its number of K ranges (1: no split).
+struct Choice {
+    mgemm_kernel_t k;
+    int ksplit;
+};
+
+// Predicted time (microseconds) of a 16-bit MFMA kernel on this problem:
+// waves of workgroups times the time of one workgroup (per 32-wide K slice of
+// a bm x bn tile SLICE_US * bm*bn/256^2 / speed, times the workgroups sharing
+// a CU, plus 2 us), and for a split of K the second pass over the FP32
+// partials (4 us plus the partial bytes at 2.6 TB/s).  Constants fitted to
+// MI355X measurements of 1024x1536x4096, 512x1024x2048, 2048^3 and
+// 512x4096x8192 BF16 over every split from 1 to 16; `speed` is a kernel's
+// per-CU rate relative to the register-staged kernel (the direct-to-LDS
+// kernel runs a full 256x256 tile 1.4x as fast: 1024 NN tiles in 2.12 vs
+// 2.58 ms).
+double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int per_cu, int ks) {
+    constexpr double SLICE_US = 0.98, WG_US = 2.0, PASS_US = 4.0, PART_BYTES_PER_US = 2.6e6;
+    const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + out_n - 1) / out_n);
+    const int64_t nk = (p.K + 31) / 32;
+    const int64_t cap = slots * per_cu;
+    const int64_t waves = (tiles * ks + cap - 1) / cap;
+    const int64_t nks = (nk + ks - 1) / ks;
+    const double slice = SLICE_US * (double)(bm * bn) / 65536.0 / speed * per_cu;
+    double t = (double)waves * ((double)nks * slice + WG_US);
+    if (ks > 1) t += PASS_US + (double)tiles * ks * bm * bn * 4.0 / PART_BYTES_PER_US;
+    return t;
+}
+
+// Split of K with the smallest predicted time for the direct-to-LDS kernel
+// (tile width bn; the gated pair's tile holds 96 output columns), among the
+// splits that fit the workspace.
+int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, double* t_out) {
+    const double speed = bn == 256 ? 1.4 : 1.3;
+    const int out_n = dual ? 96 : bn;
+    int best = 1;
+    double best_t = predict_us(p, 256, bn, out_n, speed, 1, 1);
+    int last = 1;
+    for (int req = 2; req <= mgemm::MAX_KSPLIT; ++req) {
+        const int ks = mgemm::h_dma_splits(p, bn, dual, req, ws);
+        if (ks <= last) continue;          // same number of ranges as a smaller request
+        last = ks;
+        const double t = predict_us(p, 256, bn, out_n, speed, 1, ks);
+        if (t < best_t) { best_t = t; best = ks; }
+    }
+    if (t_out) *t_out = best_t;
+    return best;
+}
+
 // Kernel choice for a canonical problem.
-mgemm_kernel_t choose(const Problem& p) {
+Choice choose(const Problem& p, const mgemm::Workspace& ws) {
     const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
     // Fraction of the CU-time a grid of bm x bn tiles spends on useful
     // outputs (wave quantisation and ragged-edge padding count as waste).
@@ -108,67 +158,79 @@ mgemm_kernel_t choose(const Problem& p) {
     if (p.dtype == mgemm::F32) {
         const bool big = mgemm::f32_fast_supports(p, true), small = mgemm::f32_fast_supports(p, false);
         if (big && (!small || fill(256, 256, 1) >= fill(128, 128, 2) * 0.9))
-            return MGEMM_KERNEL_F32_FAST;
-        if (small) return MGEMM_KERNEL_F32_FAST_128;
+            return {MGEMM_KERNEL_F32_FAST, 1};
+        if (small) return {MGEMM_KERNEL_F32_FAST_128, 1};
         // NN operands that are not 16-byte aligned or a K that is not a
         // multiple of the slice: the same kernel with narrower loads.
-        if (mgemm::f32_unaligned_supports(p)) return MGEMM_KERNEL_F32_FAST_U;
-        return MGEMM_KERNEL_F32_MFMA;
+        if (mgemm::f32_unaligned_supports(p)) return {MGEMM_KERNEL_F32_FAST_U, 1};
+        return {MGEMM_KERNEL_F32_MFMA, 1};
     }
     // M <= 64 streams B once: 256-column blocks with K split over workgroups
     // read B in 512-byte row segments (about 5.1 TB/s in copy-only
     // measurements, against 4.2 TB/s for the 128-byte segments of the
     // whole-K kernel).
-    if (p.M <= 64 && mgemm::skinny_sk_supports(p)) return MGEMM_KERNEL_SKINNY_SK;
-    if (p.M <= 64 && mgemm::skinny_supports(p)) return MGEMM_KERNEL_SKINNY;
-    // 16-bit: score each variant by the fraction of CU-time its grid spends
-    // on useful outputs (wave quantisation and the padding of ragged edge
-    // tiles count as waste) times its measured per-CU speed relative to the
-    // register-staged kernel.  The four-wave direct-to-LDS kernel runs a full
-    // 256x256 tile about 1.4x as fast (1024 NN tiles: 2.12 vs 2.58 ms); its
-    // 256x192 form moves more bytes per flop and is preferred only where the
-    // narrower tile fills the CUs clearly better.
-    struct Cand { mgemm_kernel_t k; int bm, bn; double speed; };
-    const Cand cands[5] = {{MGEMM_KERNEL_H_DMA_256, 256, 256, 1.4},
-                           {MGEMM_KERNEL_H_DMA_192, 256, 192, 1.3},
-                           {MGEMM_KERNEL_H_256x256, 256, 256, 1.0},
-                           {MGEMM_KERNEL_H_256x192, 256, 192, 1.0},
-                           {MGEMM_KERNEL_H_128x128, 128, 128, 1.0}};
-    mgemm_kernel_t best = MGEMM_KERNEL_GENERAL;
-    double best_score = -1.0;
-    for (const Cand& c : cands) {
-        const bool ok = c.k == MGEMM_KERNEL_H_DMA_256   ? mgemm::h_dma_supports(p, 256)
-                        : c.k == MGEMM_KERNEL_H_DMA_192 ? mgemm::h_dma_supports(p, 192)
-                                                        : mgemm::h_mfma_supports(p, (int)c.k);
-        if (!ok) continue;
-        const double score = fill(c.bm, c.bn, 1) * c.speed;
-        if (score > best_score + 1e-9) { best_score = score; best = c.k; }
+    if (p.M <= 64 && mgemm::skinny_sk_supports(p))
+        return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
+    if (p.M <= 64 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
+    // 16-bit: the variant (and split of K) with the smallest predicted time.
+    Choice best{MGEMM_KERNEL_GENERAL, 1};
+    double best_t = 1e300;
+    for (int bn : {256, 192}) {
+        if (!mgemm::h_dma_supports(p, bn)) continue;
+        double t;
+        const int ks = auto_split(p, bn, false, ws, &t);
+        if (t < best_t) { best_t = t; best = {bn == 256 ? MGEMM_KERNEL_H_DMA_256 : MGEMM_KERNEL_H_DMA_192, ks}; }
+    }
+    // Register-staged kernels (any layout); two 128x128 workgroups share a CU
+    // and together run at 0.8 of the 256x256 rate (2048^3 BF16: 43.9 us).
+    struct Cand { mgemm_kernel_t k; int bm, bn, per_cu; double speed; };
+    const Cand regs[3] = {{MGEMM_KERNEL_H_256x256, 256, 256, 1, 1.0},
+                          {MGEMM_KERNEL_H_256x192, 256, 192, 1, 1.0},
+                          {MGEMM_KERNEL_H_128x128, 128, 128, 2, 0.8}};
+    for (const Cand& c : regs) {
+        if (!mgemm::h_mfma_supports(p, (int)c.k)) continue;
+        const double t = predict_us(p, c.bm, c.bn, c.bn, c.speed, c.per_cu, 1);
+        if (t < best_t) { best_t = t; best = {c.k, 1}; }
     }
     return best;
 }
 
-mgemm_status_t launch(mgemm_handle_t h, const Problem& p, mgemm_kernel_t k, hipStream_t s) {
-    hipError_t e;
+// Number of K ranges a forced variant runs with (0: it cannot run them).
+int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k, int requested) {
     switch (k) {
-    case MGEMM_KERNEL_SKINNY_SK: e = mgemm::launch_skinny_sk(p, h->ws, s); break;
+    case MGEMM_KERNEL_H_DMA_256:
+        return requested == 0 ? auto_split(p, 256, false, ws, nullptr)
+                              : mgemm::h_dma_splits(p, 256, false, requested, ws);
+    case MGEMM_KERNEL_H_DMA_192:
+        return requested == 0 ? auto_split(p, 192, false, ws, nullptr)
+                              : mgemm::h_dma_splits(p, 192, false, requested, ws);
+    case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_splits(p, ws, requested);
+    default: return requested <= 1 ? 1 : 0;
+    }
+}
+
+mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s) {
+    hipError_t e;
+    switch (c.k) {
+    case MGEMM_KERNEL_SKINNY_SK: e = mgemm::launch_skinny_sk(p, h->ws, c.ksplit, s); break;
     case MGEMM_KERNEL_GENERAL: e = mgemm::launch_general(p, s); break;
     case MGEMM_KERNEL_F32_MFMA: e = mgemm::launch_f32_mfma(p, s); break;
     case MGEMM_KERNEL_H_256x256:
     case MGEMM_KERNEL_H_256x192:
-    case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)k, s); break;
+    case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)c.k, s); break;
     case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
     case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
     case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
-    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, s); break;
-    case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, s); break;
+    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, c.ksplit, h->ws, s); break;
+    case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, c.ksplit, h->ws, s); break;
     case MGEMM_KERNEL_F32_FAST_U: e = mgemm::launch_f32_unaligned(p, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
-mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, mgemm_layout_t layoutA,
+mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
                         void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
@@ -179,6 +241,8 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, mgemm_layout_t 
     if (st != MGEMM_SUCCESS) return st;
     if (forced != MGEMM_KERNEL_AUTO && (forced <= 0 || forced >= MGEMM_KERNEL_COUNT))
         return MGEMM_ERR_INVALID_ARG;
+    if (ksplit < 0 || ksplit > MGEMM_MAX_KSPLIT || (forced == MGEMM_KERNEL_AUTO && ksplit != 0))
+        return MGEMM_ERR_INVALID_ARG;
     if (epilogue != MGEMM_EPILOGUE_NONE && epilogue != MGEMM_EPILOGUE_SILU)
         return MGEMM_ERR_INVALID_ARG;
     p.epilogue = epilogue == MGEMM_EPILOGUE_SILU ? mgemm::EPI_SILU : mgemm::EPI_NONE;
@@ -187,9 +251,15 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, mgemm_layout_t 
         hipError_t e = mgemm::launch_scale(p, stream);
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
-    mgemm_kernel_t k = forced == MGEMM_KERNEL_AUTO ? choose(p) : forced;
-    if (!variant_supports(p, k)) return MGEMM_ERR_UNSUPPORTED;
-    return launch(h, p, k, stream);
+    Choice c;
+    if (forced == MGEMM_KERNEL_AUTO) {
+        c = choose(p, h->ws);
+    } else {
+        if (!variant_supports(p, forced)) return MGEMM_ERR_UNSUPPORTED;
+        c = {forced, forced_splits(p, h->ws, forced, ksplit)};
+        if (c.ksplit < 1) return MGEMM_ERR_UNSUPPORTED;
+    }
+    return launch(h, p, c, stream);
 }
 
 }  // namespace
@@ -209,7 +279,7 @@ mgemm_status_t mgemm_create(mgemm_handle_t* out) {
     h->device = dev;
     h->num_cu = prop.multiProcessorCount;
     h->ws = mgemm::Workspace{nullptr, 0, nullptr, 0};
-    const int64_t part_bytes = (int64_t)32 << 20, ncounters = (int64_t)1 << 16;
+    const int64_t part_bytes = (int64_t)128 << 20, ncounters = (int64_t)1 << 16;
     void* part = nullptr;
     void* cnt = nullptr;
     if (hipMalloc(&part, (size_t)part_bytes) != hipSuccess ||
@@ -238,8 +308,8 @@ mgemm_status_t mgemm_run(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_
                          int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
                          const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
                          mgemm_dtype_t dtype, hipStream_t stream) {
-    return run_impl(h, MGEMM_KERNEL_AUTO, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                    ldc, dtype, MGEMM_EPILOGUE_NONE, stream);
+    return run_impl(h, MGEMM_KERNEL_AUTO, 0, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta,
+                    C, ldc, dtype, MGEMM_EPILOGUE_NONE, stream);
 }
 
 mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
@@ -248,7 +318,7 @@ mgemm_status_t mgemm_run_kernel(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_l
                                 int64_t ldb, float beta, void* C, int64_t ldc,
                                 mgemm_dtype_t dtype, hipStream_t stream) {
     if (kernel == MGEMM_KERNEL_AUTO) return MGEMM_ERR_INVALID_ARG;
-    return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run_impl(h, kernel, 0, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                     dtype, MGEMM_EPILOGUE_NONE, stream);
 }
 
@@ -257,13 +327,33 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
                             const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
                             void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
                             hipStream_t stream) {
-    return run_impl(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run_impl(h, kernel, 0, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                     dtype, epilogue, stream);
+}
+
+mgemm_status_t mgemm_run_variant(mgemm_handle_t h, const mgemm_variant_t* v,
+                                 mgemm_layout_t layoutA, mgemm_layout_t layoutB, int64_t M,
+                                 int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                                 mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                                 hipStream_t stream) {
+    const mgemm_kernel_t k = v ? (mgemm_kernel_t)v->kernel : MGEMM_KERNEL_AUTO;
+    const int ks = v ? v->ksplit : 0;
+    return run_impl(h, k, ks, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,
+                    epilogue, stream);
 }
 
 mgemm_status_t mgemm_run_gated(mgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* X,
                                int64_t ldx, const void* Wg, const void* Wu, int64_t ldw, void* Z,
                                int64_t ldz, mgemm_dtype_t dtype, hipStream_t stream) {
+    return mgemm_run_gated_ex(h, 0, M, N, K, X, ldx, Wg, Wu, ldw, Z, ldz, dtype, stream);
+}
+
+mgemm_status_t mgemm_run_gated_ex(mgemm_handle_t h, int32_t ksplit, int64_t M, int64_t N, int64_t K,
+                                  const void* X, int64_t ldx, const void* Wg, const void* Wu,
+                                  int64_t ldw, void* Z, int64_t ldz, mgemm_dtype_t dtype,
+                                  hipStream_t stream) {
+    if (ksplit < 0 || ksplit > MGEMM_MAX_KSPLIT) return MGEMM_ERR_INVALID_ARG;
     if (dtype != MGEMM_F16 && dtype != MGEMM_BF16) {
         if (!valid_dtype(dtype)) return MGEMM_ERR_INVALID_ARG;
     }
@@ -283,7 +373,10 @@ mgemm_status_t mgemm_run_gated(mgemm_handle_t h, int64_t M, int64_t N, int64_t K
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
     if (!mgemm::h_gated_supports(p)) return MGEMM_ERR_UNSUPPORTED;
-    hipError_t e = mgemm::launch_h_gated(p, stream);
+    const int ks = ksplit == 0 ? auto_split(p, 192, true, h->ws, nullptr)
+                               : mgemm::h_dma_splits(p, 192, true, ksplit, h->ws);
+    if (ks < 1) return MGEMM_ERR_UNSUPPORTED;
+    hipError_t e = mgemm::launch_h_gated(p, ks, h->ws, stream);
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
@@ -298,7 +391,28 @@ mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
                                      ldc, dtype, &p);
     if (st != MGEMM_SUCCESS) return st;
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.alpha == 0.f) *kernel_out = MGEMM_KERNEL_AUTO;
-    else *kernel_out = choose(p);
+    else *kernel_out = choose(p, h->ws).k;
+    return MGEMM_SUCCESS;
+}
+
+mgemm_status_t mgemm_select_variant(mgemm_handle_t h, mgemm_layout_t layoutA,
+                                    mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                    float alpha, const void* A, int64_t lda, const void* B,
+                                    int64_t ldb, float beta, void* C, int64_t ldc,
+                                    mgemm_dtype_t dtype, mgemm_variant_t* out) {
+    if (!out) return MGEMM_ERR_INVALID_ARG;
+    Problem p;
+    mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                     ldc, dtype, &p);
+    if (st != MGEMM_SUCCESS) return st;
+    if (p.M == 0 || p.N == 0 || p.K == 0 || p.alpha == 0.f) {
+        out->kernel = MGEMM_KERNEL_AUTO;
+        out->ksplit = 0;
+    } else {
+        const Choice c = choose(p, h->ws);
+        out->kernel = c.k;
+        out->ksplit = c.ksplit;
+    }
     return MGEMM_SUCCESS;
 }
 

@@ -79,15 +79,23 @@ typedef enum {
 
 typedef struct mgemm_handle_s* mgemm_handle_t;
 
+/* A kernel variant with its split of K (see mgemm_run_variant). */
+#define MGEMM_MAX_KSPLIT 32
+typedef struct mgemm_variant {
+    int32_t kernel;   /* an mgemm_kernel_t; MGEMM_KERNEL_AUTO = the library's choice */
+    int32_t ksplit;   /* K ranges: 0 = the library's choice, 1 = all of K in one
+                         workgroup per tile, 2 .. MGEMM_MAX_KSPLIT = at most that many */
+} mgemm_variant_t;
+
 /*
  * mgemm_create -- bind a handle to the CURRENT HIP device.
  *   out : receives the handle (owned by the caller, release with mgemm_destroy).
  * Returns MGEMM_ERR_UNSUPPORTED if the device is not gfx950, MGEMM_ERR_HIP if
  * the device cannot be queried or its workspace cannot be allocated,
  * MGEMM_ERR_INVALID_ARG if out is NULL.
- * The handle owns a device workspace (32 MiB of FP32 partial results plus
- * 64 Ki arrival counters, allocated and zeroed here) that the split-K kernel
- * uses: calls that run at the same time on different streams must use
+ * The handle owns a device workspace (128 MiB of FP32 partial results plus
+ * 64 Ki arrival counters, allocated and zeroed here) that the split-K forms
+ * use: calls that run at the same time on different streams must use
  * different handles; calls on one stream (or otherwise ordered) may share one.
  * The counters return to zero at the end of every call that uses them.
  */
@@ -162,6 +170,48 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
                             hipStream_t stream);
 
 /*
+ * mgemm_run_variant -- as mgemm_run_ex, with the variant given as a kernel and
+ * a split of K.
+ *   v : NULL or {MGEMM_KERNEL_AUTO, 0} lets the library choose both;
+ *       {kernel, 0} forces the kernel and lets the library choose its split;
+ *       {kernel, n} forces both.  A forced kernel with AUTO is invalid.
+ * Split K: K is cut into ranges of whole 32-element slices, one workgroup
+ * per output tile and range, and the ranges' FP32 partial sums are added in
+ * range order, never with atomics (the MTT S4000 write-up, section 21, found
+ * atomically accumulated split-K unusable; "Chapter 5: Operators and
+ * Runtime", section 5.2.4: the order of a floating-point sum changes its last
+ * bits), so a given variant gives the same bits on every run; different
+ * splits round differently (within the tolerance of the sum).
+ * Only MGEMM_KERNEL_H_DMA_256, MGEMM_KERNEL_H_DMA_192 and
+ * MGEMM_KERNEL_SKINNY_SK take ksplit > 1; the number of ranges used is
+ * ceil(S / ceil(S / ksplit)) for S = K / 32 slices.  The direct-to-LDS kernels
+ * then run in two launches on `stream` (partial products, then the sum and
+ * the epilogue); the partials live in the handle's workspace.
+ * Errors: as mgemm_run_ex; MGEMM_ERR_INVALID_ARG for ksplit < 0 or
+ * > MGEMM_MAX_KSPLIT, or a forced split with MGEMM_KERNEL_AUTO;
+ * MGEMM_ERR_UNSUPPORTED for ksplit > 1 on another kernel or partials that
+ * do not fit the workspace (nothing enqueued).
+ */
+mgemm_status_t mgemm_run_variant(mgemm_handle_t h, const mgemm_variant_t* v,
+                                 mgemm_layout_t layoutA, mgemm_layout_t layoutB, int64_t M,
+                                 int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                                 mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                                 hipStream_t stream);
+
+/*
+ * mgemm_select_variant -- the variant (kernel and number of K ranges)
+ * mgemm_run would launch; validation as mgemm_select_kernel.  out->kernel is
+ * MGEMM_KERNEL_AUTO (and out->ksplit 0) when nothing or only a scaling of C
+ * would be launched.
+ */
+mgemm_status_t mgemm_select_variant(mgemm_handle_t h, mgemm_layout_t layoutA,
+                                    mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                    float alpha, const void* A, int64_t lda, const void* B,
+                                    int64_t ldb, float beta, void* C, int64_t ldc,
+                                    mgemm_dtype_t dtype, mgemm_variant_t* out);
+
+/*
  * mgemm_run_gated -- the gated FFN pair Z = SiLU(X * W_g) (.) (X * W_u) in one
  * kernel ("Chapter 5: Operators and Runtime" (ai-infra-book), section 5.3.1:
  * G = X W_g, U = X W_u, Z = SiLU(G) multiplied elementwise by U; fused, the
@@ -184,6 +234,20 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
 mgemm_status_t mgemm_run_gated(mgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* X,
                                int64_t ldx, const void* Wg, const void* Wu, int64_t ldw, void* Z,
                                int64_t ldz, mgemm_dtype_t dtype, hipStream_t stream);
+
+/*
+ * mgemm_run_gated_ex -- mgemm_run_gated with a split of K: ksplit 0 lets the
+ * library choose, 1 keeps all of K in one workgroup per tile, 2 ..
+ * MGEMM_MAX_KSPLIT cuts K into at most that many ranges as mgemm_run_variant
+ * describes (G and U are both summed in range order before the epilogue).
+ * Errors: as mgemm_run_gated; MGEMM_ERR_INVALID_ARG for ksplit < 0 or
+ * > MGEMM_MAX_KSPLIT; MGEMM_ERR_UNSUPPORTED when the partials do not fit the
+ * workspace.
+ */
+mgemm_status_t mgemm_run_gated_ex(mgemm_handle_t h, int32_t ksplit, int64_t M, int64_t N, int64_t K,
+                                  const void* X, int64_t ldx, const void* Wg, const void* Wu,
+                                  int64_t ldw, void* Z, int64_t ldz, mgemm_dtype_t dtype,
+                                  hipStream_t stream);
 
 /*
  * mgemm_select_kernel -- the variant mgemm_run would launch for this problem

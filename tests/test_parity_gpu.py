@@ -271,12 +271,16 @@ def test_silu_k_zero_and_bad_epilogue(h):
 # ---------------------------------------------------------------------------
 # Gated pair Z = SiLU(X W_g) * (X W_u) (mgemm_run_gated)
 # ---------------------------------------------------------------------------
-def _run_gated(h, case, inputs):
+def _run_gated(h, case, inputs, ksplit=None):
     X, Wg, Wu = inputs
     Z = P.c_initial(case, None)
     dZ = Z.cuda()
-    mg.mgemm_run_gated(h, case.M, case.N, case.K, X.cuda(), case.lda, Wg.cuda(), Wu.cuda(),
-                       case.ldb, dZ, case.ldc, case.dtype)
+    args = (case.M, case.N, case.K, X.cuda(), case.lda, Wg.cuda(), Wu.cuda(), case.ldb, dZ,
+            case.ldc, case.dtype)
+    if ksplit is None:
+        mg.mgemm_run_gated(h, *args)
+    else:
+        mg.mgemm_run_gated_ex(h, ksplit, *args)
     torch.cuda.synchronize()
     return Z, dZ.cpu()
 
@@ -312,6 +316,116 @@ def test_gated_pair_unsupported_and_k_zero(h):
     mg.mgemm_run_gated(h, 16, 64, 0, B, 1, B, B, 64, Z, 64, "bf16")
     torch.cuda.synchronize()
     assert torch.count_nonzero(Z).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# Split K in the direct-to-LDS kernel (mgemm_run_variant / mgemm_run_gated_ex)
+# ---------------------------------------------------------------------------
+# Ragged M and N edges, K from 5 to 128 slices, beta != 0; requested splits
+# above the slice count are clamped.  Integer data: every split must give the
+# oracle's bits.
+WORKSPACE_BYTES = 128 << 20      # FP32 partials a handle holds (mgemm_create)
+SPLITK_SHAPES = [(300, 200, 640), (256, 192, 1024), (513, 776, 320), (37, 104, 160),
+                 (1024, 1536, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+def test_h_dma_split_k_bit_exact(h, M, N, K):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("hsplit", M, N, K, dtype, kindA="int", kindB="int", kindC="int",
+                      alpha=1.0, beta=-0.5, seeds=(M, N, K))
+        inputs = case.make()
+        for kernel in ("h_dma_256x256", "h_dma_256x192"):
+            bn = 256 if kernel.endswith("256") else 192
+            tiles = -(-M // 256) * -(-N // bn)
+            for ks in (1, 2, 3, 5, 8, 32):
+                say("h_dma split", dtype, (M, N, K), kernel, ks)
+                nk = K // 32
+                ranges = -(-nk // -(-nk // min(ks, nk)))
+                if tiles * ranges * 1024 * bn > WORKSPACE_BYTES:
+                    # The FP32 partials (256 x bn per tile and range) would
+                    # not fit the handle's workspace: refused, nothing runs.
+                    with pytest.raises(mg.MgemmError) as ei:
+                        P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks)
+                    assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
+                    continue
+                P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
+
+
+def test_h_dma_split_k_silu(h):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("hsplit_silu", 300, 520, 640, dtype, alpha=0.25, beta=-0.5, kindA="int",
+                      kindB="int", kindC="int", seeds=(3, 4, 5))
+        inputs = case.make()
+        for kernel, ks in (("h_dma_256x256", 4), ("h_dma_256x192", 7)):
+            say("h_dma split silu", dtype, kernel, ks)
+            out = P.run_gpu(h, case, kernel, inputs=inputs, epilogue="silu", ksplit=ks)
+            P.check_silu(case, *out, exact_gemm=True)
+
+
+def test_ffn_share_split_auto(h):
+    case = W.ffn_share_bf16()
+    name, ks = mg.mgemm_select_variant(h, case.layoutA, case.layoutB, case.M, case.N, case.K,
+                                       case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
+                                       case.ldc, case.dtype)
+    say("ffn share auto:", name, ks)
+    assert name.startswith("h_dma") and ks > 1
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 192, extra=8))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 160), (130, 520, 96), (37, 104, 160)])
+def test_gated_pair_split_k_integer(h, dtype, M, N, K):
+    # K stays small: G and U grow with K and their product must stay inside
+    # the FP16 range for most outputs.
+    case = W.Case("gated_split", M, N, K, dtype, kindA="int", kindB="int", seeds=(M, N, K),
+                  extra={"gated": True, "seed_u": K + 9})
+    inputs = W.gated_inputs(case)
+    for ks in (2, 3, 5, 32):
+        say("gated split", dtype, (M, N, K), ks)
+        Zin, Zout = _run_gated(h, case, inputs, ksplit=ks)
+        P.check_gated(case, *inputs, Zout, exact_gemm=True)
+        pad = P.padding_mask(case)
+        assert np.array_equal(W.storage_view(Zout)[pad], W.storage_view(Zin)[pad])
+
+
+def test_gated_share_sampled(h):
+    case = W.ffn_gated_share_bf16()
+    inputs = W.gated_inputs(case)
+    say("gated share auto")
+    _, Zout = _run_gated(h, case, inputs)
+    P.check_gated(case, *inputs, Zout, rows=P.sample_rows(case.M, 192, extra=8))
+
+
+def test_skinny_forced_splits_bit_exact(h):
+    for M, N, K in [(64, 12288, 4096), (5, 1000, 96)]:
+        case = W.Case("sk_forced", M, N, K, "bf16", kindA="int", kindB="int", kindC="int",
+                      alpha=1.0, beta=-0.5, seeds=(M, N, K))
+        inputs = case.make()
+        for ks in (1, 2, 7, 32):
+            say("skinny_sk forced", (M, N, K), ks)
+            P.check_bit_exact(case, *P.run_gpu(h, case, "skinny_sk", inputs=inputs, ksplit=ks))
+
+
+def test_split_k_argument_errors(h):
+    A = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    args = ("row", "row", 64, 64, 64, 1.0, A, 64, A, 64, 0.0, A, 64, "bf16")
+    for kernel, ks, want in (("h_dma_256x256", 33, mg.MGEMM_ERR_INVALID_ARG),
+                             ("h_dma_256x256", -1, mg.MGEMM_ERR_INVALID_ARG),
+                             ("auto", 2, mg.MGEMM_ERR_INVALID_ARG),
+                             ("h_mfma_128x128", 2, mg.MGEMM_ERR_UNSUPPORTED)):
+        with pytest.raises(mg.MgemmError) as ei:
+            mg.mgemm_run_variant(h, kernel, ks, *args)
+        assert ei.value.status == want, (kernel, ks)
+    # Partials larger than the workspace: refused before anything is launched.
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_variant(h, "h_dma_256x256", 32, "row", "row", 8192, 8192, 16384, 1.0, A,
+                             16384, A, 8192, 0.0, A, 8192, "bf16")
+    assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_gated_ex(h, 40, 64, 64, 64, A, 64, A, A, 64, A, 64, "bf16")
+    assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------------------
@@ -386,6 +500,14 @@ def test_deterministic_run_to_run(h):
         outs = [W.storage_view(P.run_gpu(h, case, inputs=inputs)[4]) for _ in range(3)]
         for o in outs[1:]:
             assert np.array_equal(o, outs[0]), case.name
+    # A split of K adds its ranges in a fixed order: the same bits every run.
+    case = W.Case("det_split", 1024, 1280, 4096, "bf16", kindA="normal", kindB="normal",
+                  seeds=(5, 6, 7))
+    inputs = case.make()
+    outs = [W.storage_view(P.run_gpu(h, case, "h_dma_256x192", inputs=inputs, ksplit=6)[4])
+            for _ in range(3)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), case.name
 
 
 def test_non_default_stream(h):

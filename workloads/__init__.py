@@ -153,6 +153,14 @@ def ffn_bf16(M: int = 1024) -> Case:
                 scaleA=1.0, scaleB=0.02, seeds=seeds)
 
 
+def ffn_share_bf16() -> Case:
+    """One GPU's share of the FFN projection when its 12288 output columns are
+    split over 8 GPUs: X[1024x4096] W[4096x1536], same distributions as
+    ffn_bf16() (its own matrices: W is drawn at the share's shape)."""
+    return Case("ffn_share_bf16_1024x1536x4096", 1024, 1536, 4096, "bf16", kindA="normal",
+                kindB="normal", scaleA=1.0, scaleB=0.02, seeds=(4101, 4102, 4103))
+
+
 def ffn_bf16_silu() -> Case:
     """The FFN projection with the fused activation, Y = SiLU(XW) (same inputs
     as ffn_bf16(); the epilogue is named in `extra`)."""
@@ -169,6 +177,14 @@ def ffn_gated_bf16(M: int = 1024) -> Case:
     c = ffn_bf16(M)
     c.name = "ffn_gated_bf16_m%d" % M
     c.extra = {"gated": True, "seed_u": 4004}
+    return c
+
+
+def ffn_gated_share_bf16() -> Case:
+    """The gated pair at one GPU's share (N = 12288 / 8 = 1536)."""
+    c = ffn_share_bf16()
+    c.name = "ffn_gated_share_bf16_1024x1536x4096"
+    c.extra = {"gated": True, "seed_u": 4104}
     return c
 
 
