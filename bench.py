@@ -166,6 +166,60 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
     }
 
 
+def measure_mix(h, steps=20):
+    """The FFN projection X[M x 4096] W[4096 x 12288] (BF16) over the row mix
+    of one group of ten calls: eight of 256 rows, one of 1536, one of 2048
+    ("Chapter 5: Operators and Runtime", section 5.5.3, Example 5-12).  Times
+    a group with the built-in model's choices, then with a dispatch table
+    tuned on the three shapes weighted 8:1:1 (a second handle)."""
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    from workloads import operand
+    K, N = 4096, 12288
+    rows = [256] * 8 + [1536, 2048]
+    X = operand("normal", 4201, max(rows), K, "row", K, "bf16").cuda()
+    Wt = operand("normal", 4202, K, N, "row", N, "bf16", 0.02).cuda()
+    C = torch.empty(max(rows) * N, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def group(hh):
+        for m in rows:
+            mg.mgemm_run(hh, "row", "row", m, N, K, 1.0, X, K, Wt, N, 0.0, C, N, "bf16",
+                         stream=stream)
+
+    def timed(hh):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.25:
+            group(hh)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            group(hh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    flops = sum(2.0 * m * N * K for m in rows)
+    choice = lambda hh, m: "%s/k%d" % mg.mgemm_select_variant(hh, "row", "row", m, N, K, 1.0, X, K,
+                                                              Wt, N, 0.0, C, N, "bf16")
+    model_ms = timed(h)
+    ht = mg.mgemm_create()
+    try:
+        t0 = time.perf_counter()
+        mg.mgemm_tune(ht, "bf16", "row", "row", [(256, N, K), (1536, N, K), (2048, N, K)], [8, 1, 1])
+        tune_s = time.perf_counter() - t0
+        tuned_ms = timed(ht)
+        picks = {m: (choice(h, m), choice(ht, m)) for m in (256, 1536, 2048)}
+    finally:
+        mg.mgemm_destroy(ht)
+    return {"rows_per_group": rows, "model_ms_per_group": round(model_ms, 5),
+            "tuned_ms_per_group": round(tuned_ms, 5), "tune_s": round(tune_s, 2),
+            "model_TFLOPs": round(flops / model_ms / 1e9, 1),
+            "tuned_TFLOPs": round(flops / tuned_ms / 1e9, 1),
+            "choices_model_vs_tuned": {str(k): v for k, v in picks.items()}}
+
+
 def cpu_baseline(case, out_dev, budget_s):
     """Time the oracle on a bounded row sample of the workload and check that
     sample against the GPU output."""
@@ -338,6 +392,8 @@ def main():
             others[name] = ent
             del rr
             torch.cuda.empty_cache()
+        log("workload: ffn_mix_bf16 (model vs tuned table)")
+        others["ffn_mix_bf16"] = measure_mix(h)
         line["workloads"] = others
     mg.mgemm_destroy(h)
     print(json.dumps(line), flush=True)

@@ -32,7 +32,9 @@ _DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
 
 EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
             "mgemm_run_variant", "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_select_kernel",
-            "mgemm_select_variant", "mgemm_status_string", "mgemm_kernel_name", "mgemm_num_cu"]
+            "mgemm_select_variant", "mgemm_tune", "mgemm_table_export", "mgemm_table_import",
+            "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_status_string",
+            "mgemm_kernel_name", "mgemm_num_cu"]
 
 
 class MgemmError(RuntimeError):
@@ -49,6 +51,12 @@ MGEMM_MAX_KSPLIT = 32
 class MgemmVariant(ctypes.Structure):
     """mgemm_variant_t: a kernel (mgemm_kernel_t) and its number of K ranges."""
     _fields_ = [("kernel", ctypes.c_int32), ("ksplit", ctypes.c_int32)]
+
+
+class MgemmTuneResult(ctypes.Structure):
+    """mgemm_tune_result_t."""
+    _fields_ = [("chosen", MgemmVariant), ("chosen_us", ctypes.c_float), ("model", MgemmVariant),
+                ("model_us", ctypes.c_float)]
 
 
 def load(path: str | None = None):
@@ -72,10 +80,20 @@ def load(path: str | None = None):
                                        i64, ci, vp]
     lib.mgemm_run_variant.argtypes = [vp, ctypes.POINTER(MgemmVariant)] + run_args[:-1] + [ci, vp]
     lib.mgemm_select_variant.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(MgemmVariant)]
+    pi64, pdbl = ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)
+    lib.mgemm_tune.argtypes = [vp, ci, ci, ci, ctypes.c_int32, pi64, pi64, pi64, pdbl,
+                               ctypes.POINTER(MgemmTuneResult), vp]
+    lib.mgemm_table_export.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t,
+                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.mgemm_table_import.argtypes = [vp, ctypes.c_char_p]
+    lib.mgemm_table_clear.argtypes = [vp]
+    lib.mgemm_weighted_choice.argtypes = [ctypes.c_int32, ctypes.c_int32, pdbl, pdbl]
+    lib.mgemm_weighted_choice.restype = ctypes.c_int32
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
     for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
                  "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
-                 "mgemm_select_variant", "mgemm_select_kernel"):
+                 "mgemm_select_variant", "mgemm_select_kernel", "mgemm_tune", "mgemm_table_export",
+                 "mgemm_table_import", "mgemm_table_clear"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
@@ -202,6 +220,61 @@ def mgemm_select_variant(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, be
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_select_variant")
     return load().mgemm_kernel_name(out.kernel).decode(), int(out.ksplit)
+
+
+def mgemm_tune(h, dtype, layoutA, layoutB, shapes, calls=None, stream=None) -> list:
+    """Measure every variant on each (M, N, K) and fill the handle's dispatch
+    table (blocking).  Returns, per shape, the fastest variant and the model's
+    choice with their measured times."""
+    n = len(shapes)
+    arr = lambda vals, t: (t * n)(*vals)
+    Ms = arr([int(s[0]) for s in shapes], ctypes.c_int64)
+    Ns = arr([int(s[1]) for s in shapes], ctypes.c_int64)
+    Ks = arr([int(s[2]) for s in shapes], ctypes.c_int64)
+    cw = None if calls is None else arr([float(c) for c in calls], ctypes.c_double)
+    res = (MgemmTuneResult * n)()
+    st = load().mgemm_tune(h, _enum(dtype, _DTYPE), _enum(layoutA, _LAYOUT), _enum(layoutB, _LAYOUT),
+                           n, Ms, Ns, Ks, cw, res, _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_tune")
+    name = lambda v: (load().mgemm_kernel_name(v.kernel).decode(), int(v.ksplit))
+    return [{"shape": tuple(shapes[i]), "chosen": name(r.chosen), "chosen_us": r.chosen_us,
+             "model": name(r.model), "model_us": r.model_us} for i, r in enumerate(res)]
+
+
+def mgemm_table_export(h) -> str:
+    """The handle's dispatch table as text."""
+    n = ctypes.c_size_t()
+    st = load().mgemm_table_export(h, None, 0, ctypes.byref(n))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_table_export")
+    buf = ctypes.create_string_buffer(n.value + 1)
+    st = load().mgemm_table_export(h, buf, n.value + 1, ctypes.byref(n))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_table_export")
+    return buf.value.decode()
+
+
+def mgemm_table_import(h, text: str) -> None:
+    st = load().mgemm_table_import(h, text.encode())
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_table_import")
+
+
+def mgemm_table_clear(h) -> None:
+    st = load().mgemm_table_clear(h)
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_table_clear")
+
+
+def mgemm_weighted_choice(times, calls=None) -> int:
+    """Index of the variant (column of `times`, one row per shape) with the
+    smallest call-weighted total time; -1 if none runs every called shape."""
+    rows = [list(map(float, r)) for r in times]
+    ns, nv = len(rows), len(rows[0]) if rows else 0
+    flat = (ctypes.c_double * (ns * nv))(*[t for r in rows for t in r])
+    cw = None if calls is None else (ctypes.c_double * ns)(*map(float, calls))
+    return int(load().mgemm_weighted_choice(ns, nv, flat, cw))
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

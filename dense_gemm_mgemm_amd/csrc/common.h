@@ -262,6 +262,8 @@ bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s);
 bool h_dma_supports(const Problem& p, int bn);
+// n elements of dtype at p get small exact values (a hash of the index and seed).
+hipError_t launch_fill_pattern(void* p, int64_t n, int dtype, uint32_t seed, hipStream_t s);
 bool skinny_supports(const Problem& p);
 
 }  // namespace mgemm

@@ -6,22 +6,15 @@
 #include <new>
 #include <string.h>
 
-#include "../../include/mgemm.h"
-#include "common.h"
+#include "host.h"
 
-struct mgemm_handle_s {
-    int device;
-    int num_cu;
-    mgemm::Workspace ws;     // device memory owned by the handle
-};
+namespace mgemm_host {
 
 namespace {
-
-using mgemm::Problem;
-
 inline bool valid_layout(mgemm_layout_t l) { return l == MGEMM_ROW_MAJOR || l == MGEMM_COL_MAJOR; }
 inline bool valid_dtype(mgemm_dtype_t d) { return d == MGEMM_F32 || d == MGEMM_F16 || d == MGEMM_BF16; }
 inline int64_t max1(int64_t x) { return x > 1 ? x : 1; }
+}  // namespace
 
 // Checks the rules of mgemm_run and builds the canonical problem.
 mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
@@ -94,12 +87,6 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     }
 }
 
-// A kernel and its number of K ranges (1: no split).
-struct Choice {
-    mgemm_kernel_t k;
-    int ksplit;
-};
-
 // Predicted time (microseconds) of a 16-bit MFMA kernel on this problem:
 // waves of workgroups times the time of one workgroup (per 32-wide K slice of
 // a bm x bn tile SLICE_US * bm*bn/256^2 / speed, times the workgroups sharing
@@ -144,8 +131,8 @@ int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, 
     return best;
 }
 
-// Kernel choice for a canonical problem.
-Choice choose(const Problem& p, const mgemm::Workspace& ws) {
+// Kernel choice of the built-in model for a canonical problem.
+Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
     // Fraction of the CU-time a grid of bm x bn tiles spends on useful
     // outputs (wave quantisation and ragged-edge padding count as waste).
@@ -195,6 +182,10 @@ Choice choose(const Problem& p, const mgemm::Workspace& ws) {
     return best;
 }
 
+bool splittable(mgemm_kernel_t k) {
+    return k == MGEMM_KERNEL_H_DMA_256 || k == MGEMM_KERNEL_H_DMA_192 || k == MGEMM_KERNEL_SKINNY_SK;
+}
+
 // Number of K ranges a forced variant runs with (0: it cannot run them).
 int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k, int requested) {
     switch (k) {
@@ -207,6 +198,23 @@ int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k
     case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_splits(p, ws, requested);
     default: return requested <= 1 ? 1 : 0;
     }
+}
+
+// A table entry for the problem (exact shape first, then its bucket) if its
+// variant can run it; otherwise the model.
+Choice choose(mgemm_handle_t h, const Problem& p) {
+    const auto& tab = h->table.entries;
+    if (!tab.empty()) {
+        for (const TableKey& key : {exact_key(p), bucket_key(p)}) {
+            auto it = tab.find(key);
+            if (it == tab.end()) continue;
+            const mgemm_kernel_t k = (mgemm_kernel_t)it->second.kernel;
+            if (!variant_supports(p, k)) continue;
+            const int ks = forced_splits(p, h->ws, k, it->second.ksplit);
+            if (ks >= 1) return {k, ks};
+        }
+    }
+    return model_choice(p, h->ws);
 }
 
 mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s) {
@@ -229,6 +237,8 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t 
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
+
+namespace {
 
 mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
@@ -253,7 +263,7 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mge
     }
     Choice c;
     if (forced == MGEMM_KERNEL_AUTO) {
-        c = choose(p, h->ws);
+        c = choose(h, p);
     } else {
         if (!variant_supports(p, forced)) return MGEMM_ERR_UNSUPPORTED;
         c = {forced, forced_splits(p, h->ws, forced, ksplit)};
@@ -263,6 +273,9 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mge
 }
 
 }  // namespace
+}  // namespace mgemm_host
+
+using namespace mgemm_host;
 
 extern "C" {
 
@@ -391,7 +404,7 @@ mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
                                      ldc, dtype, &p);
     if (st != MGEMM_SUCCESS) return st;
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.alpha == 0.f) *kernel_out = MGEMM_KERNEL_AUTO;
-    else *kernel_out = choose(p, h->ws).k;
+    else *kernel_out = choose(h, p).k;
     return MGEMM_SUCCESS;
 }
 
@@ -409,7 +422,7 @@ mgemm_status_t mgemm_select_variant(mgemm_handle_t h, mgemm_layout_t layoutA,
         out->kernel = MGEMM_KERNEL_AUTO;
         out->ksplit = 0;
     } else {
-        const Choice c = choose(p, h->ws);
+        const Choice c = choose(h, p);
         out->kernel = c.k;
         out->ksplit = c.ksplit;
     }

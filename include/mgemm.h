@@ -22,6 +22,7 @@
 #ifndef MGEMM_H_
 #define MGEMM_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -262,6 +263,86 @@ mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
                                    float alpha, const void* A, int64_t lda, const void* B,
                                    int64_t ldb, float beta, void* C, int64_t ldc,
                                    mgemm_dtype_t dtype, mgemm_kernel_t* kernel_out);
+
+/*
+ * Dispatch table tuned by measurement ("Chapter 5: Operators and Runtime"
+ * (ai-infra-book), section 5.4.5: rule out what cannot run, then time the
+ * remaining candidates on representative shapes and keep the cheapest;
+ * Example 5-9: when one choice must serve several shapes, the cheapest is the
+ * one with the smallest total time weighted by each shape's call count;
+ * section 5.5.3: similar shapes share a choice through buckets).
+ *
+ * The handle holds a table consulted by mgemm_run, mgemm_run_ex,
+ * mgemm_run_variant with MGEMM_KERNEL_AUTO, and mgemm_select_*:
+ *   1. an exact entry for the problem's canonical shape (after the
+ *      column-major transpose identity), dtype and operand layouts;
+ *   2. else a bucket entry: M, N and K each rounded up to a power of two;
+ *   3. else the built-in time model.
+ * An entry whose variant cannot run the call (e.g. operands less aligned
+ * than when it was tuned) falls through to the next step.  Entries never
+ * change results beyond the choice of variant; every variant is
+ * parity-tested.  The table must not be changed while another call uses the
+ * handle.
+ */
+typedef struct mgemm_tune_result {
+    mgemm_variant_t chosen;   /* fastest measured variant (kernel, ranges requested) */
+    float chosen_us;          /* its mean time per call, microseconds */
+    mgemm_variant_t model;    /* what the built-in model picks (ranges used) */
+    float model_us;           /* its measured mean time per call */
+} mgemm_tune_result_t;
+
+/*
+ * mgemm_tune -- measure every variant that can run each of the n shapes
+ * (M[i] x N[i] x K[i], this dtype and these layouts, alpha = 1, beta = 0) on
+ * `stream`, add an exact table entry per shape with the fastest, and one
+ * entry per bucket with the variant of smallest sum of calls[i] * time over
+ * the bucket's shapes (calls NULL: one call each).  Split-capable kernels
+ * are measured at splits 1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24 and 32.
+ * Operands are allocated on the device inside this call (hipMalloc) and
+ * filled with small exact values; the call blocks until the measurements are
+ * done and releases them.  results: NULL or n entries, filled per shape.
+ * Errors: MGEMM_ERR_INVALID_ARG for n < 1, a NULL array, a size < 1 or a
+ * negative call count; MGEMM_ERR_UNSUPPORTED if no variant runs a shape;
+ * MGEMM_ERR_HIP for an allocation or launch failure.
+ */
+mgemm_status_t mgemm_tune(mgemm_handle_t h, mgemm_dtype_t dtype, mgemm_layout_t layoutA,
+                          mgemm_layout_t layoutB, int32_t n, const int64_t* M, const int64_t* N,
+                          const int64_t* K, const double* calls, mgemm_tune_result_t* results,
+                          hipStream_t stream);
+
+/*
+ * mgemm_table_export -- the handle's table as text, one entry per line:
+ *     exact  <dtype> <a_kc> <b_kc> <M> <N> <K> <kernel name> <ksplit> <us>
+ *     bucket <dtype> <a_kc> <b_kc> <log2 M> <log2 N> <log2 K> <kernel name> <ksplit> <us>
+ * (canonical problem: a_kc/b_kc = 1 when A'/B' rows are K-contiguous; us =
+ * measured time, for a bucket the call-weighted total).  Writes at most cap
+ * bytes including the terminating NUL; *len receives the full length
+ * without the NUL (call with buf NULL, cap 0 to size a buffer).
+ * MGEMM_ERR_INVALID_ARG if len is NULL or the text does not fit.
+ */
+mgemm_status_t mgemm_table_export(mgemm_handle_t h, char* buf, size_t cap, size_t* len);
+
+/*
+ * mgemm_table_import -- add the entries of text in mgemm_table_export's
+ * format (replacing entries with the same key).  All-or-nothing:
+ * MGEMM_ERR_INVALID_ARG for a malformed line or an unknown kernel name, and
+ * then the table is unchanged.
+ */
+mgemm_status_t mgemm_table_import(mgemm_handle_t h, const char* text);
+
+/* mgemm_table_clear -- remove every entry (the model alone decides again). */
+mgemm_status_t mgemm_table_clear(mgemm_handle_t h);
+
+/*
+ * mgemm_weighted_choice -- index of the variant with the smallest
+ * sum over shapes of calls[s] * times[s * n_variants + v] (Example 5-9 of
+ * section 5.4.5); a variant with a non-finite or negative time for any shape
+ * with calls > 0 is out.  Ties go to the lower index.  calls NULL counts one
+ * call per shape.  Returns -1 if no variant qualifies or an argument is
+ * invalid.  Host-only; needs no device.
+ */
+int32_t mgemm_weighted_choice(int32_t n_shapes, int32_t n_variants, const double* times,
+                              const double* calls);
 
 /* Static strings; never NULL (unknown values give "unknown"). */
 const char* mgemm_status_string(mgemm_status_t s);
