@@ -12,6 +12,7 @@ import subprocess
 import sys
 import textwrap
 
+import numpy as np
 import pytest
 
 import oracle
@@ -116,3 +117,80 @@ def test_planted_swiglu_mistake_is_caught(mutant, monkeypatch):
     monkeypatch.setattr(oracle, "swiglu", mutant)
     with pytest.raises(AssertionError):
         check_swiglu()
+
+
+# ---------------------------------------------------------------------------
+# FP8 oracle (oracle/fp8.py): plausible slips swapped in for its functions.
+# ---------------------------------------------------------------------------
+from oracle import fp8 as _fp8   # noqa: E402
+
+
+def _quantize_blockwise(x):
+    # Scale from the first 128 elements only (Example 5-7's wrong order).
+    x = np.asarray(x, np.float64)
+    head = x[:, :128]
+    q, s = _REAL_QUANTIZE(head)
+    rest = x[:, 128:]
+    if rest.shape[1] == 0:
+        return q, s
+    t = (rest.astype(np.float32) * np.float32(448)) / np.maximum(np.abs(head).max(axis=1), 1e-30).astype(np.float32)[:, None]
+    return np.concatenate([q, _fp8.e4m3_encode(np.clip(t, -448, 448))], axis=1), s
+
+
+def _quantize_multiply(x):
+    x = np.asarray(x, np.float64)
+    x32 = x.astype(np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    s = (amax / np.float32(448)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = x32 * s[:, None]                       # multiplies by the scale instead of dividing
+    return _fp8.e4m3_encode(t), s
+
+
+def _encode_half_away(t):
+    t = np.asarray(t, np.float64)
+    vals = _fp8.e4m3_values()[:0x7F]
+    a = np.minimum(np.abs(t), 448.0)
+    lo = np.clip(np.searchsorted(vals, a, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    pick = (vals[hi] - a) <= (a - vals[lo])        # ties go up
+    mag = np.where(pick, hi, lo).astype(np.uint8)
+    code = mag | np.where(np.signbit(t), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(t), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def _values_bias8():
+    v = _REAL_VALUES()
+    return np.where(np.isnan(v), v, v / 2.0)       # exponent bias 8 instead of 7
+
+
+def _gemm_sb_per_row(M, N, K, alpha, qa, lda, sa, qb, ldb, sb, beta=0.0, c0=None):
+    sb2 = np.resize(np.asarray(sa, np.float32), N)  # row scales used for the columns too
+    return _REAL_GEMM(M, N, K, alpha, qa, lda, sa, qb, ldb, sb2, beta, c0)
+
+
+def _gemm_qb_transposed(M, N, K, alpha, qa, lda, sa, qb, ldb, sb, beta=0.0, c0=None):
+    qb = np.asarray(qb, np.uint8)
+    B = _fp8.e4m3_decode(qb[: N * ldb].reshape(N, ldb)[:, :K])
+    Bt = np.resize(B.T.ravel(), N * K).reshape(N, K)   # read as K x N
+    return _REAL_GEMM(M, N, K, alpha, qa, lda, sa, _fp8.e4m3_encode(Bt).ravel(), K, sb, beta, c0)
+
+
+_REAL_QUANTIZE, _REAL_VALUES, _REAL_GEMM = _fp8.quantize_rows, _fp8.e4m3_values, _fp8.fp8_gemm
+
+FP8_MUTANTS = [("quantize_rows", _quantize_blockwise), ("quantize_rows", _quantize_multiply),
+               ("e4m3_encode", _encode_half_away), ("e4m3_values", _values_bias8),
+               ("fp8_gemm", _gemm_sb_per_row), ("fp8_gemm", _gemm_qb_transposed)]
+
+
+@pytest.mark.parametrize("attr,mutant", FP8_MUTANTS, ids=lambda m: getattr(m, "__name__", m))
+def test_planted_fp8_mistake_is_caught(attr, mutant, monkeypatch):
+    from tests.test_oracle_fp8 import FP8_PINS
+    monkeypatch.setattr(_fp8, attr, mutant)
+    failed = []
+    for check in FP8_PINS:
+        try:
+            check()
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, "mutant %s passed every FP8 pin" % mutant.__name__
