@@ -22,7 +22,8 @@ MGEMM_ROW_MAJOR, MGEMM_COL_MAJOR = 0, 1
 MGEMM_F32, MGEMM_F16, MGEMM_BF16 = 0, 1, 2
 KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
            "skinny", "h_pp_256x256", "f32_fast", "f32_fast_128",
-           "h_dma_256x256", "skinny_sk", "h_dma_256x192", "f32_fast_u"]
+           "h_dma_256x256", "skinny_sk", "h_dma_256x192", "f32_fast_u",
+           "f8_mfma_256x256", "f8_general"]
 MGEMM_KERNEL_AUTO = 0
 MGEMM_EPILOGUE_NONE, MGEMM_EPILOGUE_SILU = 0, 1
 _EPILOGUE = {"none": MGEMM_EPILOGUE_NONE, "silu": MGEMM_EPILOGUE_SILU}
@@ -33,7 +34,8 @@ _DTYPE = {"f32": MGEMM_F32, "f16": MGEMM_F16, "bf16": MGEMM_BF16}
 EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
             "mgemm_run_variant", "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_select_kernel",
             "mgemm_select_variant", "mgemm_tune", "mgemm_table_export", "mgemm_table_import",
-            "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_status_string",
+            "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_quantize_fp8", "mgemm_run_fp8",
+            "mgemm_status_string",
             "mgemm_kernel_name", "mgemm_num_cu"]
 
 
@@ -89,11 +91,15 @@ def load(path: str | None = None):
     lib.mgemm_table_clear.argtypes = [vp]
     lib.mgemm_weighted_choice.argtypes = [ctypes.c_int32, ctypes.c_int32, pdbl, pdbl]
     lib.mgemm_weighted_choice.restype = ctypes.c_int32
+    lib.mgemm_quantize_fp8.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, vp, vp]
+    lib.mgemm_run_fp8.argtypes = [vp, ci, i64, i64, i64, f32, vp, i64, vp, vp, i64, vp, f32, vp,
+                                  i64, ci, vp]
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
     for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
                  "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
                  "mgemm_select_variant", "mgemm_select_kernel", "mgemm_tune", "mgemm_table_export",
-                 "mgemm_table_import", "mgemm_table_clear"):
+                 "mgemm_table_import", "mgemm_table_clear", "mgemm_quantize_fp8",
+                 "mgemm_run_fp8"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
@@ -275,6 +281,25 @@ def mgemm_weighted_choice(times, calls=None) -> int:
     flat = (ctypes.c_double * (ns * nv))(*[t for r in rows for t in r])
     cw = None if calls is None else (ctypes.c_double * ns)(*map(float, calls))
     return int(load().mgemm_weighted_choice(ns, nv, flat, cw))
+
+
+def mgemm_quantize_fp8(h, M, K, X, ldx, xtype, Q, ldq, scales, stream=None) -> None:
+    """Per-row E4M3 quantisation of X (M x K) into codes Q and FP32 scales."""
+    st = load().mgemm_quantize_fp8(h, int(M), int(K), _ptr(X), int(ldx), _enum(xtype, _DTYPE),
+                                   _ptr(Q), int(ldq), _ptr(scales), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_quantize_fp8")
+
+
+def mgemm_run_fp8(h, kernel, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, ctype,
+                  stream=None) -> None:
+    """C = alpha * sa[m] * sb[n] * sum_k A[m,k] B[n,k] + beta * C on E4M3 codes."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    st = load().mgemm_run_fp8(h, k, int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                              _ptr(sa), _ptr(B), int(ldb), _ptr(sb), float(beta), _ptr(C),
+                              int(ldc), _enum(ctype, _DTYPE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_fp8(%s)" % kernel)
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

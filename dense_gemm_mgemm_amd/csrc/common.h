@@ -262,6 +262,15 @@ bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s);
 bool h_dma_supports(const Problem& p, int bn);
+// FP8 E4M3: per-row quantisation of an M x K matrix of xtype (codes Q with
+// row stride ldq, FP32 dequantisation scales), and the FP8 GEMM on codes:
+// p.A = A codes (M x K, stride lda), p.B = B codes one output column per row
+// (N x K, stride ldb), p.dtype = C's type; sa/sb = the row scales of A and B.
+hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx, int xtype, void* Q,
+                               int64_t ldq, float* scales, hipStream_t s);
+bool f8_mfma_supports(const Problem& p);
+bool f8_general_supports(const Problem& p);
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, bool mfma, hipStream_t s);
 // n elements of dtype at p get small exact values (a hash of the index and seed).
 hipError_t launch_fill_pattern(void* p, int64_t n, int dtype, uint32_t seed, hipStream_t s);
 bool skinny_supports(const Problem& p);

@@ -1,0 +1,439 @@
+// FP8 (E4M3FN) path for gfx950: per-row quantisation and the FP8 GEMM.
+//
+// Format ("Chapter 5: Operators and Runtime", section 5.4.3, Example 5-7):
+// sign, 4 exponent bits (bias 7), 3 mantissa bits; largest finite value 448,
+// no infinity, 0x7F/0xFF are NaN.
+//
+// Quantisation (Example 5-7): a row's scale comes from the largest magnitude
+// of the whole row, found before any element is quantised: one wave per row
+// reads the row once for the maximum, then again (from L2) to quantise.
+// Element x becomes t = (x * 448) / amax (x * 448 is exact in FP32, the
+// division correctly rounded), rounded to the nearest E4M3 value with ties
+// to the even mantissa; the row's dequantisation scale amax / 448 is stored
+// as FP32.  A separate kernel rather than a fused one because each output
+// tile would otherwise re-read the wide input (section 5.4.4, Example 5-8:
+// with 128x128 tiles 444 vs 620 MiB; with 256-wide tiles the fused form still
+// reads the 16-bit input once per column block).
+//
+// GEMM (section 5.4.4, Example 5-8): C = alpha * sa[m] * sb[n] * sum_k
+// qa[m,k] qb[n,k] + beta * C with both code matrices K-contiguous (qb holds
+// the weights one output column per row).  The scales factor out of the K
+// sum, so the contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// block scales and the row/column scales are applied in the epilogue.  The
+// tile loop is the four-slot direct-to-LDS ring of k_h_dma.hip with both
+// operands staged like its A: 256x256 output tiles, four waves of 128x128,
+// K = 64 bytes per slice (a 64-byte row per operand row, 16 KiB per operand
+// per slot), one MFMA K-step per slice, fragments read one slice ahead, one
+// copy or fragment read after each MFMA.
+// Restrictions of the MFMA kernel (host-checked): K % 64 == 0, lda and ldb
+// multiples of 16, 16-byte aligned code buffers; k_f8_general takes the rest.
+#include "common.h"
+
+namespace mgemm {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// E4M3 encode / decode
+// ---------------------------------------------------------------------------
+// Nearest E4M3 code of t (ties to the even mantissa; magnitudes >= 448
+// saturate to 448; NaN -> 0x7F; the sign of zero is kept).
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+    const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+    const float a = fabsf(t);
+    if (!(a == a)) return 0x7Fu;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0x1p-6f) {
+        // Subnormals are multiples of 2^-9: scale exactly, round to an
+        // integer 0..8 (8 is the smallest normal, code 0x08).
+        return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+    }
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);          // round the mantissa to 3 bits, ties to even
+    const uint32_t e = (b >> 23) - 127u + 7u;  // 1..15 (a < 448 cannot round past 448)
+    return sign | (e << 3) | ((b >> 20) & 7u);
+}
+
+// Value of an E4M3 code (exact in FP32).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+    else if (e == 0u) v = (float)m * 0x1p-9f;
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row quantisation: one wave per row, four rows per workgroup.
+// ---------------------------------------------------------------------------
+template <int XT>
+__device__ __forceinline__ float load_x(const void* x, int64_t i) {
+    if constexpr (XT == F32) return ((const float*)x)[i];
+    else if constexpr (XT == F16) return f16_bits_to_f32(((const uint16_t*)x)[i]);
+    else return bf16_bits_to_f32(((const uint16_t*)x)[i]);
+}
+
+// Largest magnitude, NaN if either is NaN.
+__device__ __forceinline__ float amax2(float a, float b) {
+    return (a != a || b != b) ? __uint_as_float(0x7FC00000u) : fmaxf(a, b);
+}
+
+template <int XT, bool VEC>
+__global__ __launch_bounds__(256) void k_quant_rows(int64_t M, int64_t K, const void* X, int64_t ldx,
+                                                    uint8_t* Q, int64_t ldq, float* scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    constexpr int ES = XT == F32 ? 4 : 2;
+    constexpr int V = 16 / ES;                    // elements per 16-byte load
+    const unsigned char* xr = (const unsigned char*)X + row * ldx * ES;
+    auto vec_at = [&](int64_t k, float (&v)[V]) {
+        const i32x4 w = *(const i32x4*)(xr + k * ES);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            if constexpr (XT == F32) v[e] = __int_as_float(w[e]);
+            else {
+                const uint16_t h = (uint16_t)((uint32_t)w[e / 2] >> (16 * (e & 1)));
+                v[e] = XT == F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+            }
+        }
+    };
+    // Pass 1: the row's largest magnitude.
+    float m = 0.0f;
+    if constexpr (VEC) {
+        for (int64_t k = (int64_t)lane * V; k < K; k += 64 * V) {
+            float v[V];
+            vec_at(k, v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) m = amax2(m, fabsf(v[e]));
+        }
+    } else {
+        for (int64_t k = lane; k < K; k += 64) m = amax2(m, fabsf(load_x<XT>(xr, k)));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = amax2(m, __shfl_xor(m, off, 64));
+    if (lane == 0) scales[row] = m / 448.0f;
+    // Pass 2: codes.  A zero row keeps its (signed) zeros.
+    uint8_t* qr = Q + row * ldq;
+    auto code = [&](float x) {
+        const float t = m == 0.0f ? x : (x * 448.0f) / m;
+        return e4m3_code(t);
+    };
+    if constexpr (VEC) {
+        for (int64_t k = (int64_t)lane * V; k < K; k += 64 * V) {
+            float v[V];
+            vec_at(k, v);
+            uint32_t w[V / 4];
+#pragma unroll
+            for (int g = 0; g < V / 4; ++g)
+                w[g] = code(v[4 * g]) | (code(v[4 * g + 1]) << 8) | (code(v[4 * g + 2]) << 16) |
+                       (code(v[4 * g + 3]) << 24);
+            if constexpr (V == 8) *(uint2*)(qr + k) = make_uint2(w[0], w[1]);
+            else *(uint32_t*)(qr + k) = w[0];
+        }
+    } else {
+        for (int64_t k = lane; k < K; k += 64) qr[k] = (uint8_t)code(load_x<XT>(xr, k));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 GEMM on the matrix cores
+// ---------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int SLOTS = 4, AHEAD = SLOTS - 1;
+constexpr int ROW = BK;                          // bytes per operand row per slice
+constexpr int OP_BYTES = BM * ROW;               // 16 KiB per operand per slot
+constexpr int SLOT_BYTES = 2 * OP_BYTES;
+constexpr int OP_COPIES = 4;                     // 1 KiB copies per wave per operand per slice
+constexpr int COPIES = 2 * OP_COPIES;
+constexpr int TM = 4, TN = 4;                    // 32x32 blocks per wave (128x128)
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Wait until at most n slices of COPIES copies each are still in flight.
+__device__ __forceinline__ void wait_slices(int n) {
+    if (n <= 0) wait_vm<0>();
+    else if (n == 1) wait_vm<COPIES>();
+    else wait_vm<2 * COPIES>();
+}
+// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l).  Inline
+// asm: the compiler would otherwise drain every copy in flight before any LDS
+// read it cannot prove disjoint.
+__device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void fence_sched() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void slice_barrier() {
+    fence_sched();
+    __builtin_amdgcn_s_barrier();
+    fence_sched();
+}
+
+struct Frags {
+    i32x4 a[TM][2];
+    i32x4 b[TN][2];
+};
+
+__device__ __forceinline__ f32x16 mfma8(const i32x4 (&x)[2], const i32x4 (&y)[2], f32x16 c) {
+    const i32x8 xa = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 ya = __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    // Both operands E4M3 (format 0), unit block scales (E8M0 127 = 2^0).
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, c, 0, 0, 0, 127, 0, 127);
+}
+
+struct F8Args {
+    const float* sa;      // M scales of A's rows
+    const float* sb;      // N scales of B's rows (output columns)
+};
+
+template <int CT>
+__device__ __forceinline__ void store4(void* C, int64_t ldc, int64_t m, int64_t n, int nlim_n,
+                                       bool vec_ok, float beta, float (&v)[4]) {
+    if constexpr (CT == F32) {
+        float* c = (float*)C + m * ldc + n;
+        const bool full = vec_ok && nlim_n >= 4;
+        if (beta != 0.f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nlim_n) v[e] = fmaf(beta, c[e], v[e]);
+        }
+        if (full) *(f32x4*)c = f32x4{v[0], v[1], v[2], v[3]};
+        else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < nlim_n) c[e] = v[e];
+        }
+    } else {
+        store_out4<CT, EPI_NONE>((uint16_t*)C + m * ldc, (int)n, (int)n + nlim_n, vec_ok, beta, v);
+    }
+}
+
+template <int CT>
+__global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    int tmi, tni;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const uint8_t* __restrict__ A = (const uint8_t*)p.A;
+    const uint8_t* __restrict__ B = (const uint8_t*)p.B;
+
+    // Copies of this wave: rows [64w, 64w+64) of each operand tile, four
+    // copies of 16 rows (lane l: row 16i + l/4, 16-byte chunk l%4 stored at
+    // the swizzled chunk position).  Rows past the edge repeat the last row.
+    const uint8_t* src[COPIES];
+    int dst[COPIES];
+#pragma unroll
+    for (int i = 0; i < OP_COPIES; ++i) {
+        const int r = 64 * wave + 16 * i + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
+        const int ra = r < mlim ? r : mlim - 1, rb = r < nlim ? r : nlim - 1;
+        src[i] = A + (m0 + ra) * p.lda + 16 * c;
+        src[OP_COPIES + i] = B + (n0 + rb) * p.ldb + 16 * c;
+        dst[i] = (64 * wave + 16 * i) * ROW;
+        dst[OP_COPIES + i] = OP_BYTES + (64 * wave + 16 * i) * ROW;
+    }
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    auto copy = [&](int s, int i) {
+        copy_to_lds(src[i] + (int64_t)s * BK, lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES + dst[i]);
+    };
+    // Fragment offsets: lane l holds 32 K-consecutive bytes (chunks
+    // 2*(l/32) and 2*(l/32)+1) of row l%32 of its 32-row block.
+    int a_off[TM][2], b_off[TN][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = 2 * (lane >> 5) + h;
+            const int ra = 128 * wm + 32 * t + (lane & 31);
+            const int rb = 128 * wn + 32 * t + (lane & 31);
+            a_off[t][h] = ra * ROW + ((c ^ swz(ra)) << 4);
+            b_off[t][h] = OP_BYTES + rb * ROW + ((c ^ swz(rb)) << 4);
+        }
+    // Read r (0..15) of a slice: A0, B0..B3, A1..A3, two 16-byte halves each.
+    auto read = [&](Frags& fr, int s, int r) {
+        const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
+        const int item = r >> 1, h = r & 1;
+        if (item == 0) fr.a[0][h] = *(const i32x4*)(base + a_off[0][h]);
+        else if (item <= TN) fr.b[item - 1][h] = *(const i32x4*)(base + b_off[item - 1][h]);
+        else fr.a[item - TN][h] = *(const i32x4*)(base + a_off[item - TN][h]);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+    // One slice: the 16 MFMAs on `use`, each followed by one fragment read
+    // of slice rs into `nxt` (when do_read) and, after every other MFMA, one
+    // copy of slice cs (when do_copy).
+    auto step = [&](const Frags& use, Frags& nxt, bool do_read, int rs, bool do_copy, int cs) {
+#pragma unroll
+        for (int i = 0; i < TM * TN; ++i) {
+            const int tm = i / TN, tn = i % TN;
+            acc[tm][tn] = mfma8(use.b[tn], use.a[tm], acc[tm][tn]);
+            if (do_copy && (i & 1) == 0) copy(cs, i >> 1);
+            if (do_read) read(nxt, rs, i);
+            fence_sched();
+        }
+    };
+
+    const int nk = (int)(p.K / BK);
+    const int npro = nk < AHEAD ? nk : AHEAD;
+    for (int s = 0; s < npro; ++s)
+        for (int i = 0; i < COPIES; ++i) copy(s, i);
+    wait_slices(npro - 1);
+    slice_barrier();
+    Frags f0, f1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read(f0, 0, r);
+
+    // Pairs of slices (the fragment buffers alternate); every slice waits
+    // for this wave's copies of the next slice, then a barrier makes them
+    // visible to all waves and frees the slot of the slice before.
+    int j = 0;
+    for (; j + 1 + AHEAD < nk; j += 2) {
+        wait_slices(AHEAD - 2);
+        slice_barrier();
+        step(f0, f1, true, j + 1, true, j + AHEAD);
+        wait_slices(AHEAD - 2);
+        slice_barrier();
+        step(f1, f0, true, j + 2, true, j + 1 + AHEAD);
+    }
+    for (; j < nk; j += 2) {        // the last slices: copies only while any remain
+        int left = nk - j - 2;
+        if (j + 1 < nk) {
+            wait_slices(left < AHEAD - 2 ? left : AHEAD - 2);
+            slice_barrier();
+        }
+        step(f0, f1, j + 1 < nk, j + 1, j + AHEAD < nk, j + AHEAD);
+        if (j + 1 >= nk) break;
+        left = nk - j - 3;
+        if (j + 2 < nk) {
+            wait_slices(left < AHEAD - 2 ? left : AHEAD - 2);
+            slice_barrier();
+        }
+        step(f1, f0, j + 2 < nk, j + 2, j + 1 + AHEAD < nk, j + 1 + AHEAD);
+    }
+
+    // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
+    const int fr = lane & 31, nq = 4 * (lane >> 5);
+    const int es = CT == F32 ? 4 : 2;
+    const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & (4 * es - 1)) == 0);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int mi = 128 * wm + 32 * tm + fr;
+        if (mi >= mlim) continue;
+        const float sa = f.sa[m0 + mi];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ni = 128 * wn + 32 * tn + 8 * q + nq;
+                if (ni >= nlim) continue;
+                const int nn = nlim - ni < 4 ? nlim - ni : 4;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sb = e < nn ? f.sb[n0 + ni + e] : 0.0f;
+                    v[e] = p.alpha * ((acc[tm][tn][4 * q + e] * sa) * sb);
+                }
+                store4<CT>(p.C, p.ldc, m0 + mi, n0 + ni, nn, vec_ok, p.beta, v);
+            }
+    }
+}
+
+// Any K, alignment and leading dimension: one thread per output, codes
+// decoded one by one, FP32 accumulation in K order.
+template <int CT>
+__global__ __launch_bounds__(256) void k_f8_general(Problem p, F8Args f) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.M * p.N) return;
+    const int64_t m = idx / p.N, n = idx % p.N;
+    const uint8_t* a = (const uint8_t*)p.A + m * p.lda;
+    const uint8_t* b = (const uint8_t*)p.B + n * p.ldb;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < p.K; ++k) acc = fmaf(e4m3_value(a[k]), e4m3_value(b[k]), acc);
+    float v[4] = {p.alpha * ((acc * f.sa[m]) * f.sb[n]), 0.f, 0.f, 0.f};
+    store4<CT>(p.C, p.ldc, m, n, 1, false, p.beta, v);
+}
+
+template <int XT>
+hipError_t launch_quant_xt(int64_t M, int64_t K, const void* X, int64_t ldx, uint8_t* Q, int64_t ldq,
+                           float* scales, hipStream_t s) {
+    constexpr int ES = XT == F32 ? 4 : 2, V = 16 / ES;
+    const bool vec = K % V == 0 && (ldx * ES) % 16 == 0 && ((uintptr_t)X & 15) == 0 &&
+                     ldq % V == 0 && ((uintptr_t)Q & (V - 1)) == 0;
+    const dim3 grid((unsigned)((M + 3) / 4));
+    if (vec) hipLaunchKernelGGL((k_quant_rows<XT, true>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+    else hipLaunchKernelGGL((k_quant_rows<XT, false>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+    return hipGetLastError();
+}
+
+template <int CT>
+hipError_t launch_f8_ct(const Problem& p, const F8Args& f, bool mfma, hipStream_t s) {
+    if (mfma) {
+        auto kern = k_f8_dma<CT>;
+        const size_t lds = (size_t)SLOTS * SLOT_BYTES;
+        static bool attr_set = false;     // benign race: every caller sets the same value
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p, f);
+    } else {
+        const int64_t n = p.M * p.N;
+        hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, f);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx, int xtype, void* Q,
+                               int64_t ldq, float* scales, hipStream_t s) {
+    if (xtype == F32) return launch_quant_xt<F32>(M, K, X, ldx, (uint8_t*)Q, ldq, scales, s);
+    if (xtype == F16) return launch_quant_xt<F16>(M, K, X, ldx, (uint8_t*)Q, ldq, scales, s);
+    return launch_quant_xt<BF16>(M, K, X, ldx, (uint8_t*)Q, ldq, scales, s);
+}
+
+bool f8_mfma_supports(const Problem& p) {
+    if (p.K <= 0 || p.K % BK != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0) return false;
+    if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    return tiles > 0 && tiles <= 0x7fffffff;
+}
+
+bool f8_general_supports(const Problem& p) { return (p.M * p.N + 255) / 256 <= 0x7fffffff; }
+
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, bool mfma, hipStream_t s) {
+    const F8Args f{sa, sb};
+    if (p.dtype == F32) return launch_f8_ct<F32>(p, f, mfma, s);
+    if (p.dtype == F16) return launch_f8_ct<F16>(p, f, mfma, s);
+    return launch_f8_ct<BF16>(p, f, mfma, s);
+}
+
+}  // namespace mgemm

@@ -393,6 +393,64 @@ mgemm_status_t mgemm_run_gated_ex(mgemm_handle_t h, int32_t ksplit, int64_t M, i
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
+mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const void* X,
+                                  int64_t ldx, mgemm_dtype_t xtype, void* Q, int64_t ldq,
+                                  float* scales, hipStream_t stream) {
+    if (!h || M < 0 || K < 0 || !valid_dtype(xtype)) return MGEMM_ERR_INVALID_ARG;
+    if (ldx < (K > 1 ? K : 1) || ldq < (K > 1 ? K : 1)) return MGEMM_ERR_INVALID_ARG;
+    const int64_t lim = (int64_t)1 << 62;
+    if (M > lim / ldx || M > lim / ldq) return MGEMM_ERR_INVALID_ARG;
+    if (M == 0) return MGEMM_SUCCESS;
+    if (!scales || (K > 0 && (!X || !Q))) return MGEMM_ERR_INVALID_ARG;
+    if ((M + 3) / 4 > 0x7fffffff) return MGEMM_ERR_INVALID_ARG;
+    hipError_t e = mgemm::launch_quantize_fp8(M, K, X, ldx, (int)xtype, Q, ldq, scales, stream);
+    return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+}
+
+mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M, int64_t N,
+                             int64_t K, float alpha, const void* A, int64_t lda, const float* sa,
+                             const void* B, int64_t ldb, const float* sb, float beta, void* C,
+                             int64_t ldc, mgemm_dtype_t ctype, hipStream_t stream) {
+    if (!h || M < 0 || N < 0 || K < 0 || !valid_dtype(ctype)) return MGEMM_ERR_INVALID_ARG;
+    if (kernel != MGEMM_KERNEL_AUTO && kernel != MGEMM_KERNEL_F8_MFMA &&
+        kernel != MGEMM_KERNEL_F8_GENERAL)
+        return MGEMM_ERR_INVALID_ARG;
+    if (lda < max1(K) || ldb < max1(K) || ldc < max1(N)) return MGEMM_ERR_INVALID_ARG;
+    const int64_t lim = (int64_t)1 << 62;
+    if (M > lim / lda || N > lim / ldb || M > lim / ldc) return MGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MGEMM_SUCCESS;
+    if (!C) return MGEMM_ERR_INVALID_ARG;
+    Problem p;
+    p.M = M; p.N = N; p.K = K;
+    p.A = A; p.lda = lda; p.a_kc = 1;
+    p.B = B; p.ldb = ldb; p.b_kc = 1;
+    p.C = C; p.ldc = ldc;
+    p.alpha = alpha; p.beta = beta;
+    p.dtype = (int)ctype;
+    p.num_cu = h->num_cu;
+    p.epilogue = mgemm::EPI_NONE;
+    p.B2 = nullptr;
+    p.ldb2 = 0;
+    if (K == 0 || alpha == 0.f) {
+        hipError_t e = mgemm::launch_scale(p, stream);
+        return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+    }
+    if (!A || !B || !sa || !sb) return MGEMM_ERR_INVALID_ARG;
+    bool mfma;
+    if (kernel == MGEMM_KERNEL_F8_MFMA) {
+        if (!mgemm::f8_mfma_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+        mfma = true;
+    } else if (kernel == MGEMM_KERNEL_F8_GENERAL) {
+        if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+        mfma = false;
+    } else {
+        mfma = mgemm::f8_mfma_supports(p);
+        if (!mfma && !mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+    }
+    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, mfma, stream);
+    return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+}
+
 mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
                                    mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
                                    float alpha, const void* A, int64_t lda, const void* B,
@@ -456,6 +514,8 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_DMA_192: return "h_dma_256x192";
     case MGEMM_KERNEL_F32_FAST_U: return "f32_fast_u";
     case MGEMM_KERNEL_SKINNY_SK: return "skinny_sk";
+    case MGEMM_KERNEL_F8_MFMA: return "f8_mfma_256x256";
+    case MGEMM_KERNEL_F8_GENERAL: return "f8_general";
     default: return "unknown";
     }
 }

@@ -69,7 +69,9 @@ typedef enum {
     MGEMM_KERNEL_SKINNY_SK = 11, /* FP16/BF16, M <= 64, 256-column blocks, K split over workgroups */
     MGEMM_KERNEL_H_DMA_192 = 12, /* FP16/BF16 NN, 256x192 tiles, 4 waves of 128x96, direct-to-LDS ring */
     MGEMM_KERNEL_F32_FAST_U = 13, /* FP32 NN, any alignment and K: 256x256x32 tiles, narrower loads */
-    MGEMM_KERNEL_COUNT = 14
+    MGEMM_KERNEL_F8_MFMA = 14,   /* FP8 codes (mgemm_run_fp8 only): 256x256 tiles, f8f6f4 MFMA */
+    MGEMM_KERNEL_F8_GENERAL = 15, /* FP8 codes (mgemm_run_fp8 only): any K/alignment, VALU */
+    MGEMM_KERNEL_COUNT = 16
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */
@@ -343,6 +345,57 @@ mgemm_status_t mgemm_table_clear(mgemm_handle_t h);
  */
 int32_t mgemm_weighted_choice(int32_t n_shapes, int32_t n_variants, const double* times,
                               const double* calls);
+
+/*
+ * FP8 E4M3 with per-row scales ("Chapter 5: Operators and Runtime"
+ * (ai-infra-book): section 5.4.3, Example 5-7, the E4M3FN format and a scale
+ * taken from the largest magnitude of the whole row before quantising;
+ * section 5.4.4, Example 5-8, FP8 activations with per-row scales times FP8
+ * weights).  E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits, largest
+ * finite 448, no infinity, codes 0x7F and 0xFF are NaN.
+ *
+ * mgemm_quantize_fp8 -- per-row quantisation of X (M x K, row-major, element
+ * type xtype = F32, F16 or BF16, leading dimension ldx >= max(1, K)) into
+ * codes Q (M x K bytes, row stride ldq >= max(1, K)) and FP32 dequantisation
+ * scales (M floats): for each row, amax = largest |x| (NaN if the row holds
+ * a NaN), scales[row] = amax / 448 and
+ *     Q[row][k] = E4M3( (x * 448) / amax )
+ * computed in FP32 (x * 448 exact, the division correctly rounded), rounded
+ * to the nearest E4M3 value with ties to the even mantissa; magnitudes of 448
+ * and above give 448, NaN gives 0x7F, the sign of zero is kept.  A row of
+ * zeros gets scale 0 and keeps its signed zeros.  So X ~ decode(Q) * scales.
+ * Device pointers; asynchronous on `stream`.
+ * Errors: MGEMM_ERR_INVALID_ARG for negative sizes, a leading dimension or
+ * row stride below K, an unknown xtype or a NULL pointer with M, K > 0.
+ */
+mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const void* X,
+                                  int64_t ldx, mgemm_dtype_t xtype, void* Q, int64_t ldq,
+                                  float* scales, hipStream_t stream);
+
+/*
+ * mgemm_run_fp8 -- C = alpha * (diag(sa) A) (diag(sb) B)^T + beta * C on FP8
+ * codes, i.e. per output
+ *     C[m][n] = round(alpha * sa[m] * sb[n] * sum_k A[m][k] * B[n][k] + beta * C[m][n])
+ *   A  : M x K codes, row-major (row stride lda >= max(1, K)), sa: M scales;
+ *   B  : N x K codes, one row per output column (the weight matrix as
+ *        out_features x in_features; row stride ldb >= max(1, K)), sb: N scales;
+ *   C  : M x N, row-major, ldc >= max(1, N), element type ctype (F32, F16,
+ *        BF16); beta == 0 never reads C.
+ *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA (K % 64 == 0, lda and
+ *        ldb multiples of 16, 16-byte aligned A and B) or
+ *        MGEMM_KERNEL_F8_GENERAL (anything).
+ * Products of codes are exact; the K sum accumulates in FP32 and the scales
+ * are applied to it once: v = alpha * ((acc * sa[m]) * sb[n]).
+ * M == 0 or N == 0 does nothing; K == 0 or alpha == 0 gives C = beta * C.
+ * Asynchronous on `stream`.
+ * Errors: MGEMM_ERR_INVALID_ARG (sizes, strides, NULL pointers, ctype,
+ * kernel not an FP8 kernel); MGEMM_ERR_UNSUPPORTED when a forced kernel
+ * cannot run the problem; MGEMM_ERR_HIP for a failed launch.
+ */
+mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M, int64_t N,
+                             int64_t K, float alpha, const void* A, int64_t lda, const float* sa,
+                             const void* B, int64_t ldb, const float* sb, float beta, void* C,
+                             int64_t ldc, mgemm_dtype_t ctype, hipStream_t stream);
 
 /* Static strings; never NULL (unknown values give "unknown"). */
 const char* mgemm_status_string(mgemm_status_t s);

@@ -188,6 +188,24 @@ def ffn_gated_share_bf16() -> Case:
     return c
 
 
+def fp8_ffn_bf16() -> Case:
+    """FP8 form of the FFN projection: X[1024x4096] BF16 ~ N(0,1) quantised per
+    row each call; the weights W ~ N(0, 0.02^2), stored as 12288 rows of 4096
+    (one row per output column, i.e. B column-major) and quantised per row
+    once; BF16 output."""
+    return Case("fp8_ffn_1024x12288x4096", 1024, 12288, 4096, "bf16", layoutB="col",
+                kindA="normal", kindB="normal", scaleA=1.0, scaleB=0.02,
+                seeds=(4301, 4302, 4303), extra={"fp8": True})
+
+
+def fp8_quant_example() -> Case:
+    """The shapes of the separate-versus-fused quantisation example: FP16
+    A[4096x4096] ~ N(0,1), FP8 weights for 1536 output columns, FP16 output."""
+    return Case("fp8_4096x1536x4096", 4096, 1536, 4096, "f16", layoutB="col", kindA="normal",
+                kindB="normal", scaleA=1.0, scaleB=0.02, seeds=(4311, 4312, 4313),
+                extra={"fp8": True})
+
+
 def gated_inputs(case: Case):
     """(X, W_g, W_u) CPU tensors of a gated-pair case."""
     X, Wg, _ = case.make()
