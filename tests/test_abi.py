@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "mgemm.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mgemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mgemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_is_built():
