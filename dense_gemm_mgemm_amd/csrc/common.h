@@ -268,9 +268,10 @@ bool h_dma_supports(const Problem& p, int bn);
 // (N x K, stride ldb), p.dtype = C's type; sa/sb = the row scales of A and B.
 hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx, int xtype, void* Q,
                                int64_t ldq, float* scales, hipStream_t s);
-bool f8_mfma_supports(const Problem& p);
+bool f8_mfma_supports(const Problem& p, int bn);          // bn = 256 or 192
 bool f8_general_supports(const Problem& p);
-hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, bool mfma, hipStream_t s);
+// bn: the MFMA kernel's tile width (256 or 192), 0 for the scalar kernel.
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, hipStream_t s);
 // n elements of dtype at p get small exact values (a hash of the index and seed).
 hipError_t launch_fill_pattern(void* p, int64_t n, int dtype, uint32_t seed, hipStream_t s);
 bool skinny_supports(const Problem& p);

@@ -5,12 +5,14 @@
 // no infinity, 0x7F/0xFF are NaN.
 //
 // Quantisation (Example 5-7): a row's scale comes from the largest magnitude
-// of the whole row, found before any element is quantised: one wave per row
-// reads the row once for the maximum, then again (from L2) to quantise.
-// Element x becomes t = (x * 448) / amax (x * 448 is exact in FP32, the
-// division correctly rounded), rounded to the nearest E4M3 value with ties
-// to the even mantissa; the row's dequantisation scale amax / 448 is stored
-// as FP32.  A separate kernel rather than a fused one because each output
+// of the whole row, found before any element is quantised.  Rows of up to
+// 16384 16-bit (8192 FP32) elements with aligned 16-byte chunks: one workgroup
+// per row holds the row in registers; otherwise one wave per row reads the
+// row once for the maximum and again (from L2) to quantise.
+// Element x is scaled by the row's factor, t = x * r with r = 448 / amax
+// (both FP32, r correctly rounded once per row), and rounded to the nearest
+// E4M3 value with ties to the even mantissa; the row's dequantisation scale
+// amax / 448 is stored as FP32.  A separate kernel rather than a fused one because each output
 // tile would otherwise re-read the wide input (section 5.4.4, Example 5-8:
 // with 128x128 tiles 444 vs 620 MiB; with 256-wide tiles the fused form still
 // reads the 16-bit input once per column block).
@@ -23,8 +25,11 @@
 // tile loop is the four-slot direct-to-LDS ring of k_h_dma.hip with both
 // operands staged like its A: 256x256 output tiles, four waves of 128x128,
 // K = 64 bytes per slice (a 64-byte row per operand row, 16 KiB per operand
-// per slot), one MFMA K-step per slice, fragments read one slice ahead, one
-// copy or fragment read after each MFMA.
+// per slot), one MFMA K-step per slice, fragments read one slice ahead, the
+// copies and fragment reads spread evenly between the MFMAs.  BN = 192 (four
+// waves of 128x96) exists for grids that a 256-wide tile fills badly: the
+// 1024x12288 FFN projection is 192 tiles of 256x256 on 256 CUs but 256 of
+// 256x192.
 // Restrictions of the MFMA kernel (host-checked): K % 64 == 0, lda and ldb
 // multiples of 16, 16-byte aligned code buffers; k_f8_general takes the rest.
 #include "common.h"
@@ -56,6 +61,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float t) {
     b += 0x7FFFFu + ((b >> 20) & 1u);          // round the mantissa to 3 bits, ties to even
     const uint32_t e = (b >> 23) - 127u + 7u;  // 1..15 (a < 448 cannot round past 448)
     return sign | (e << 3) | ((b >> 20) & 7u);
+}
+
+// Four codes packed little-endian into a word.  gfx950 converts FP32 pairs
+// to E4M3 in hardware (v_cvt_pk_fp8_f32, round to nearest even); the inputs
+// are clamped to +-448 first (infinities saturate like e4m3_code) and the
+// code of a NaN is set to 0x7F afterwards.  The parity tests check every code
+// against the oracle's encoder.
+#ifndef MGEMM_F8_HW_CVT
+#define MGEMM_F8_HW_CVT 1
+#endif
+__device__ __forceinline__ uint32_t e4m3_word(float a, float b, float c, float d) {
+#if MGEMM_F8_HW_CVT
+    auto clamp = [](float t) { return fminf(fmaxf(t, -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
+    uint32_t u = (uint32_t)w;
+    if (a != a) u = (u & 0xFFFFFF00u) | 0x7Fu;
+    if (b != b) u = (u & 0xFFFF00FFu) | 0x7F00u;
+    if (c != c) u = (u & 0xFF00FFFFu) | 0x7F0000u;
+    if (d != d) u = (u & 0x00FFFFFFu) | 0x7F000000u;
+    return u;
+#else
+    return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
+#endif
 }
 
 // Value of an E4M3 code (exact in FP32).
@@ -120,10 +149,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(int64_t M, int64_t K, const 
     if (lane == 0) scales[row] = m / 448.0f;
     // Pass 2: codes.  A zero row keeps its (signed) zeros.
     uint8_t* qr = Q + row * ldq;
-    auto code = [&](float x) {
-        const float t = m == 0.0f ? x : (x * 448.0f) / m;
-        return e4m3_code(t);
-    };
+    const float r = 448.0f / m;
+    auto sc = [&](float x) { return m == 0.0f ? x : x * r; };       // scaled value
     if constexpr (VEC) {
         for (int64_t k = (int64_t)lane * V; k < K; k += 64 * V) {
             float v[V];
@@ -131,27 +158,94 @@ __global__ __launch_bounds__(256) void k_quant_rows(int64_t M, int64_t K, const 
             uint32_t w[V / 4];
 #pragma unroll
             for (int g = 0; g < V / 4; ++g)
-                w[g] = code(v[4 * g]) | (code(v[4 * g + 1]) << 8) | (code(v[4 * g + 2]) << 16) |
-                       (code(v[4 * g + 3]) << 24);
+                w[g] = e4m3_word(sc(v[4 * g]), sc(v[4 * g + 1]), sc(v[4 * g + 2]), sc(v[4 * g + 3]));
             if constexpr (V == 8) *(uint2*)(qr + k) = make_uint2(w[0], w[1]);
             else *(uint32_t*)(qr + k) = w[0];
         }
     } else {
-        for (int64_t k = lane; k < K; k += 64) qr[k] = (uint8_t)code(load_x<XT>(xr, k));
+        for (int64_t k = lane; k < K; k += 64) qr[k] = (uint8_t)e4m3_code(sc(load_x<XT>(xr, k)));
+    }
+}
+
+// One workgroup per row with the row held in registers: thread t loads the
+// 16-byte chunks t, t + 256, ... (up to R of them, all issued at once), the
+// four waves combine their maxima through LDS, and the codes are formed from
+// the registers, so the row crosses HBM once and each thread waits for one
+// round of loads (rows of up to 16384 16-bit or 8192 FP32 elements).
+template <int XT, int R>
+__global__ __launch_bounds__(256) void k_quant_rows_reg(int64_t M, int64_t K, const void* X,
+                                                        int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                        float* scales) {
+    constexpr int ES = XT == F32 ? 4 : 2;
+    constexpr int V = 16 / ES;
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t row = blockIdx.x;
+    const int64_t chunks = K / V;
+    const unsigned char* xr = (const unsigned char*)X + row * ldx * ES;
+    float v[R][V];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t c = tid + 256 * i;
+        if (c < chunks) {
+            const i32x4 w = *(const i32x4*)(xr + c * 16);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                if constexpr (XT == F32) v[i][e] = __int_as_float(w[e]);
+                else {
+                    const uint16_t hb = (uint16_t)((uint32_t)w[e / 2] >> (16 * (e & 1)));
+                    v[i][e] = XT == F16 ? f16_bits_to_f32(hb) : bf16_bits_to_f32(hb);
+                }
+                m = amax2(m, fabsf(v[i][e]));
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = amax2(m, __shfl_xor(m, off, 64));
+    if (lane == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    m = amax2(amax2(wmax[0], wmax[1]), amax2(wmax[2], wmax[3]));
+    if (tid == 0) scales[row] = m / 448.0f;
+    const float r = 448.0f / m;
+    uint8_t* qr = Q + row * ldq;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t c = tid + 256 * i;
+        if (c < chunks) {
+            uint32_t w[V / 4];
+#pragma unroll
+            for (int g = 0; g < V / 4; ++g) {
+                float t[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) t[b] = m == 0.0f ? v[i][4 * g + b] : v[i][4 * g + b] * r;
+                w[g] = e4m3_word(t[0], t[1], t[2], t[3]);
+            }
+            if constexpr (V == 8) *(uint2*)(qr + c * V) = make_uint2(w[0], w[1]);
+            else *(uint32_t*)(qr + c * V) = w[0];
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // FP8 GEMM on the matrix cores
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int BM = 256, BK = 64, NT = 256;
 constexpr int SLOTS = 4, AHEAD = SLOTS - 1;
 constexpr int ROW = BK;                          // bytes per operand row per slice
-constexpr int OP_BYTES = BM * ROW;               // 16 KiB per operand per slot
-constexpr int SLOT_BYTES = 2 * OP_BYTES;
-constexpr int OP_COPIES = 4;                     // 1 KiB copies per wave per operand per slice
-constexpr int COPIES = 2 * OP_COPIES;
-constexpr int TM = 4, TN = 4;                    // 32x32 blocks per wave (128x128)
+constexpr int A_BYTES = BM * ROW;                // 16 KiB of A per slot
+constexpr int A_COPIES = 4;                      // 1 KiB copies of A per wave per slice
+constexpr int TM = 4;                            // 32-row blocks per wave (128 rows)
+
+template <int BN>
+struct F8Cfg {
+    static_assert(BN == 256 || BN == 192, "tile width");
+    static constexpr int B_COPIES = BN / 64;     // 1 KiB copies of B per wave per slice
+    static constexpr int COPIES = A_COPIES + B_COPIES;
+    static constexpr int SLOT_BYTES = A_BYTES + BN * ROW;
+    static constexpr int TN = BN / 64;           // 32-column blocks per wave (BN/2 columns)
+    static constexpr int READS = 2 * (TM + TN);  // 16-byte fragment reads per slice
+};
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
@@ -160,11 +254,12 @@ __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Wait until at most n slices of COPIES copies each are still in flight.
+// Wait until at most n slices of L copies each are still in flight.
+template <int L>
 __device__ __forceinline__ void wait_slices(int n) {
     if (n <= 0) wait_vm<0>();
-    else if (n == 1) wait_vm<COPIES>();
-    else wait_vm<2 * COPIES>();
+    else if (n == 1) wait_vm<L>();
+    else wait_vm<2 * L>();
 }
 // Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l).  Inline
 // asm: the compiler would otherwise drain every copy in flight before any LDS
@@ -183,6 +278,7 @@ __device__ __forceinline__ void slice_barrier() {
     fence_sched();
 }
 
+template <int TN>
 struct Frags {
     i32x4 a[TM][2];
     i32x4 b[TN][2];
@@ -222,8 +318,11 @@ __device__ __forceinline__ void store4(void* C, int64_t ldc, int64_t m, int64_t 
     }
 }
 
-template <int CT>
+template <int CT, int BN>
 __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
+    using G = F8Cfg<BN>;
+    constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
+    using Fr = Frags<TN>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,20 +336,27 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     const uint8_t* __restrict__ A = (const uint8_t*)p.A;
     const uint8_t* __restrict__ B = (const uint8_t*)p.B;
 
-    // Copies of this wave: rows [64w, 64w+64) of each operand tile, four
-    // copies of 16 rows (lane l: row 16i + l/4, 16-byte chunk l%4 stored at
-    // the swizzled chunk position).  Rows past the edge repeat the last row.
+    // Copies of this wave: rows [64w, 64w+64) of the A tile and
+    // [BN/4*w, BN/4*(w+1)) of the B tile, 16 rows per copy (lane l: row
+    // 16i + l/4, 16-byte chunk l%4 stored at the swizzled chunk position).
+    // Rows past the edge repeat the last row.
     const uint8_t* src[COPIES];
     int dst[COPIES];
 #pragma unroll
-    for (int i = 0; i < OP_COPIES; ++i) {
+    for (int i = 0; i < A_COPIES; ++i) {
         const int r = 64 * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
-        const int ra = r < mlim ? r : mlim - 1, rb = r < nlim ? r : nlim - 1;
+        const int ra = r < mlim ? r : mlim - 1;
         src[i] = A + (m0 + ra) * p.lda + 16 * c;
-        src[OP_COPIES + i] = B + (n0 + rb) * p.ldb + 16 * c;
         dst[i] = (64 * wave + 16 * i) * ROW;
-        dst[OP_COPIES + i] = OP_BYTES + (64 * wave + 16 * i) * ROW;
+    }
+#pragma unroll
+    for (int i = 0; i < G::B_COPIES; ++i) {
+        const int r = BN / 4 * wave + 16 * i + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
+        const int rb = r < nlim ? r : nlim - 1;
+        src[A_COPIES + i] = B + (n0 + rb) * p.ldb + 16 * c;
+        dst[A_COPIES + i] = A_BYTES + (BN / 4 * wave + 16 * i) * ROW;
     }
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
@@ -260,17 +366,21 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     // 2*(l/32) and 2*(l/32)+1) of row l%32 of its 32-row block.
     int a_off[TM][2], b_off[TN][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int h = 0; h < 2; ++h) {
+        const int c = 2 * (lane >> 5) + h;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = 2 * (lane >> 5) + h;
+        for (int t = 0; t < TM; ++t) {
             const int ra = 128 * wm + 32 * t + (lane & 31);
-            const int rb = 128 * wn + 32 * t + (lane & 31);
             a_off[t][h] = ra * ROW + ((c ^ swz(ra)) << 4);
-            b_off[t][h] = OP_BYTES + rb * ROW + ((c ^ swz(rb)) << 4);
         }
-    // Read r (0..15) of a slice: A0, B0..B3, A1..A3, two 16-byte halves each.
-    auto read = [&](Frags& fr, int s, int r) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int rb = BN / 2 * wn + 32 * t + (lane & 31);
+            b_off[t][h] = A_BYTES + rb * ROW + ((c ^ swz(rb)) << 4);
+        }
+    }
+    // Read r of a slice: A0, B0..B(TN-1), A1..A3, two 16-byte halves each.
+    auto read = [&](Fr& fr, int s, int r) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
         const int item = r >> 1, h = r & 1;
         if (item == 0) fr.a[0][h] = *(const i32x4*)(base + a_off[0][h]);
@@ -284,16 +394,24 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    // One slice: the 16 MFMAs on `use`, each followed by one fragment read
-    // of slice rs into `nxt` (when do_read) and, after every other MFMA, one
-    // copy of slice cs (when do_copy).
-    auto step = [&](const Frags& use, Frags& nxt, bool do_read, int rs, bool do_copy, int cs) {
+    // One slice: the TM*TN MFMAs on `use`; read r of slice rs into `nxt`
+    // follows MFMA r*NM/READS and copy c of slice cs follows MFMA c*NM/COPIES.
+    constexpr int NM = TM * TN, NR = G::READS;
+    auto step = [&](const Fr& use, Fr& nxt, bool do_read, int rs, bool do_copy, int cs) {
 #pragma unroll
-        for (int i = 0; i < TM * TN; ++i) {
+        for (int i = 0; i < NM; ++i) {
             const int tm = i / TN, tn = i % TN;
             acc[tm][tn] = mfma8(use.b[tn], use.a[tm], acc[tm][tn]);
-            if (do_copy && (i & 1) == 0) copy(cs, i >> 1);
-            if (do_read) read(nxt, rs, i);
+            if (do_copy) {
+#pragma unroll
+                for (int c = 0; c < COPIES; ++c)
+                    if (c * NM / COPIES == i) copy(cs, c);
+            }
+            if (do_read) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    if (r * NM / NR == i) read(nxt, rs, r);
+            }
             fence_sched();
         }
     };
@@ -302,35 +420,35 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     const int npro = nk < AHEAD ? nk : AHEAD;
     for (int s = 0; s < npro; ++s)
         for (int i = 0; i < COPIES; ++i) copy(s, i);
-    wait_slices(npro - 1);
+    wait_slices<COPIES>(npro - 1);
     slice_barrier();
-    Frags f0, f1;
+    Fr f0, f1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) read(f0, 0, r);
+    for (int r = 0; r < NR; ++r) read(f0, 0, r);
 
     // Pairs of slices (the fragment buffers alternate); every slice waits
     // for this wave's copies of the next slice, then a barrier makes them
     // visible to all waves and frees the slot of the slice before.
     int j = 0;
     for (; j + 1 + AHEAD < nk; j += 2) {
-        wait_slices(AHEAD - 2);
+        wait_slices<COPIES>(AHEAD - 2);
         slice_barrier();
         step(f0, f1, true, j + 1, true, j + AHEAD);
-        wait_slices(AHEAD - 2);
+        wait_slices<COPIES>(AHEAD - 2);
         slice_barrier();
         step(f1, f0, true, j + 2, true, j + 1 + AHEAD);
     }
     for (; j < nk; j += 2) {        // the last slices: copies only while any remain
         int left = nk - j - 2;
         if (j + 1 < nk) {
-            wait_slices(left < AHEAD - 2 ? left : AHEAD - 2);
+            wait_slices<COPIES>(left < AHEAD - 2 ? left : AHEAD - 2);
             slice_barrier();
         }
         step(f0, f1, j + 1 < nk, j + 1, j + AHEAD < nk, j + AHEAD);
         if (j + 1 >= nk) break;
         left = nk - j - 3;
         if (j + 2 < nk) {
-            wait_slices(left < AHEAD - 2 ? left : AHEAD - 2);
+            wait_slices<COPIES>(left < AHEAD - 2 ? left : AHEAD - 2);
             slice_barrier();
         }
         step(f1, f0, j + 2 < nk, j + 2, j + 1 + AHEAD < nk, j + 1 + AHEAD);
@@ -349,7 +467,7 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int ni = 128 * wn + 32 * tn + 8 * q + nq;
+                const int ni = BN / 2 * wn + 32 * tn + 8 * q + nq;
                 if (ni >= nlim) continue;
                 const int nn = nlim - ni < 4 ? nlim - ni : 4;
                 float v[4];
@@ -384,30 +502,48 @@ hipError_t launch_quant_xt(int64_t M, int64_t K, const void* X, int64_t ldx, uin
     constexpr int ES = XT == F32 ? 4 : 2, V = 16 / ES;
     const bool vec = K % V == 0 && (ldx * ES) % 16 == 0 && ((uintptr_t)X & 15) == 0 &&
                      ldq % V == 0 && ((uintptr_t)Q & (V - 1)) == 0;
+    const int64_t per_thread = (K / V + 255) / 256;       // 16-byte chunks per thread
+    if (vec && per_thread <= 8 && M <= 0x7fffffff) {
+        const dim3 grid((unsigned)M);
+        if (per_thread <= 1)
+            hipLaunchKernelGGL((k_quant_rows_reg<XT, 1>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+        else if (per_thread <= 2)
+            hipLaunchKernelGGL((k_quant_rows_reg<XT, 2>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+        else if (per_thread <= 4)
+            hipLaunchKernelGGL((k_quant_rows_reg<XT, 4>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+        else
+            hipLaunchKernelGGL((k_quant_rows_reg<XT, 8>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((M + 3) / 4));
     if (vec) hipLaunchKernelGGL((k_quant_rows<XT, true>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
     else hipLaunchKernelGGL((k_quant_rows<XT, false>), grid, dim3(256), 0, s, M, K, X, ldx, Q, ldq, scales);
     return hipGetLastError();
 }
 
-template <int CT>
-hipError_t launch_f8_ct(const Problem& p, const F8Args& f, bool mfma, hipStream_t s) {
-    if (mfma) {
-        auto kern = k_f8_dma<CT>;
-        const size_t lds = (size_t)SLOTS * SLOT_BYTES;
-        static bool attr_set = false;     // benign race: every caller sets the same value
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
-        const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p, f);
-    } else {
-        const int64_t n = p.M * p.N;
-        hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, f);
+template <int CT, int BN>
+hipError_t launch_f8_dma(const Problem& p, const F8Args& f, hipStream_t s) {
+    auto kern = k_f8_dma<CT, BN>;
+    const size_t lds = (size_t)SLOTS * F8Cfg<BN>::SLOT_BYTES;
+    static bool attr_set = false;     // benign race: every caller sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
     }
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p, f);
+    return hipGetLastError();
+}
+
+// bn: 256 or 192 for the MFMA kernel, 0 for the scalar kernel.
+template <int CT>
+hipError_t launch_f8_ct(const Problem& p, const F8Args& f, int bn, hipStream_t s) {
+    if (bn == 256) return launch_f8_dma<CT, 256>(p, f, s);
+    if (bn == 192) return launch_f8_dma<CT, 192>(p, f, s);
+    const int64_t n = p.M * p.N;
+    hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, f);
     return hipGetLastError();
 }
 
@@ -420,20 +556,21 @@ hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx,
     return launch_quant_xt<BF16>(M, K, X, ldx, (uint8_t*)Q, ldq, scales, s);
 }
 
-bool f8_mfma_supports(const Problem& p) {
+bool f8_mfma_supports(const Problem& p, int bn) {
+    if (bn != 256 && bn != 192) return false;
     if (p.K <= 0 || p.K % BK != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
     return tiles > 0 && tiles <= 0x7fffffff;
 }
 
 bool f8_general_supports(const Problem& p) { return (p.M * p.N + 255) / 256 <= 0x7fffffff; }
 
-hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, bool mfma, hipStream_t s) {
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, hipStream_t s) {
     const F8Args f{sa, sb};
-    if (p.dtype == F32) return launch_f8_ct<F32>(p, f, mfma, s);
-    if (p.dtype == F16) return launch_f8_ct<F16>(p, f, mfma, s);
-    return launch_f8_ct<BF16>(p, f, mfma, s);
+    if (p.dtype == F32) return launch_f8_ct<F32>(p, f, bn, s);
+    if (p.dtype == F16) return launch_f8_ct<F16>(p, f, bn, s);
+    return launch_f8_ct<BF16>(p, f, bn, s);
 }
 
 }  // namespace mgemm

@@ -413,7 +413,7 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M,
                              int64_t ldc, mgemm_dtype_t ctype, hipStream_t stream) {
     if (!h || M < 0 || N < 0 || K < 0 || !valid_dtype(ctype)) return MGEMM_ERR_INVALID_ARG;
     if (kernel != MGEMM_KERNEL_AUTO && kernel != MGEMM_KERNEL_F8_MFMA &&
-        kernel != MGEMM_KERNEL_F8_GENERAL)
+        kernel != MGEMM_KERNEL_F8_MFMA_192 && kernel != MGEMM_KERNEL_F8_GENERAL)
         return MGEMM_ERR_INVALID_ARG;
     if (lda < max1(K) || ldb < max1(K) || ldc < max1(N)) return MGEMM_ERR_INVALID_ARG;
     const int64_t lim = (int64_t)1 << 62;
@@ -436,18 +436,30 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M,
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
     if (!A || !B || !sa || !sb) return MGEMM_ERR_INVALID_ARG;
-    bool mfma;
-    if (kernel == MGEMM_KERNEL_F8_MFMA) {
-        if (!mgemm::f8_mfma_supports(p)) return MGEMM_ERR_UNSUPPORTED;
-        mfma = true;
+    int bn = -1;                     // MFMA tile width, 0 = scalar kernel
+    if (kernel == MGEMM_KERNEL_F8_MFMA || kernel == MGEMM_KERNEL_F8_MFMA_192) {
+        bn = kernel == MGEMM_KERNEL_F8_MFMA ? 256 : 192;
+        if (!mgemm::f8_mfma_supports(p, bn)) return MGEMM_ERR_UNSUPPORTED;
     } else if (kernel == MGEMM_KERNEL_F8_GENERAL) {
         if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
-        mfma = false;
+        bn = 0;
     } else {
-        mfma = mgemm::f8_mfma_supports(p);
-        if (!mfma && !mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+        // The width with the fewest tile-columns of CU time (waves of tiles
+        // times the tile width); ties keep the wider tile.
+        const int64_t slots = h->num_cu > 0 ? h->num_cu : 256;
+        int64_t best = -1;
+        for (int w : {256, 192}) {
+            if (!mgemm::f8_mfma_supports(p, w)) continue;
+            const int64_t tiles = ((M + 255) / 256) * ((N + w - 1) / w);
+            const int64_t cost = (tiles + slots - 1) / slots * w;
+            if (best < 0 || cost < best) { best = cost; bn = w; }
+        }
+        if (bn < 0) {
+            if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+            bn = 0;
+        }
     }
-    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, mfma, stream);
+    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, bn, stream);
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
@@ -516,6 +528,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_SKINNY_SK: return "skinny_sk";
     case MGEMM_KERNEL_F8_MFMA: return "f8_mfma_256x256";
     case MGEMM_KERNEL_F8_GENERAL: return "f8_general";
+    case MGEMM_KERNEL_F8_MFMA_192: return "f8_mfma_256x192";
     default: return "unknown";
     }
 }

@@ -71,7 +71,8 @@ typedef enum {
     MGEMM_KERNEL_F32_FAST_U = 13, /* FP32 NN, any alignment and K: 256x256x32 tiles, narrower loads */
     MGEMM_KERNEL_F8_MFMA = 14,   /* FP8 codes (mgemm_run_fp8 only): 256x256 tiles, f8f6f4 MFMA */
     MGEMM_KERNEL_F8_GENERAL = 15, /* FP8 codes (mgemm_run_fp8 only): any K/alignment, VALU */
-    MGEMM_KERNEL_COUNT = 16
+    MGEMM_KERNEL_F8_MFMA_192 = 16, /* FP8 codes (mgemm_run_fp8 only): 256x192 tiles, f8f6f4 MFMA */
+    MGEMM_KERNEL_COUNT = 17
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */
@@ -381,9 +382,10 @@ mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const 
  *        out_features x in_features; row stride ldb >= max(1, K)), sb: N scales;
  *   C  : M x N, row-major, ldc >= max(1, N), element type ctype (F32, F16,
  *        BF16); beta == 0 never reads C.
- *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA (K % 64 == 0, lda and
- *        ldb multiples of 16, 16-byte aligned A and B) or
- *        MGEMM_KERNEL_F8_GENERAL (anything).
+ *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA or
+ *        MGEMM_KERNEL_F8_MFMA_192 (K % 64 == 0, lda and ldb multiples of 16,
+ *        16-byte aligned A and B) or MGEMM_KERNEL_F8_GENERAL (anything).
+ *        AUTO takes the MFMA tile width whose grid fills the CUs better.
  * Products of codes are exact; the K sum accumulates in FP32 and the scales
  * are applied to it once: v = alpha * ((acc * sa[m]) * sb[n]).
  * M == 0 or N == 0 does nothing; K == 0 or alpha == 0 gives C = beta * C.

@@ -22,12 +22,13 @@ What it computes ("Chapter 5: Operators and Runtime", ai-infra-book):
 
 Readings where the pages are silent (each also listed in the design notes):
 * Rounding to E4M3 is to nearest, ties to the even mantissa; magnitudes
-  above 448 saturate to 448 (they cannot arise from x * 448 / amax).
-* The scaled value t = (x * 448) / amax and the stored scale amax / 448 are
-  formed in FP32 (x * 448 is exact in FP32 for FP16/BF16/FP32 inputs with at
-  most 21 significant bits; the division is correctly rounded), because the
-  quantised code is an integer decision that both sides must take in the
-  same precision.
+  above 448 saturate to 448 (the row's largest element can land a rounding
+  above 448 after scaling).
+* Each element is scaled by the row's factor 448 / amax (Example 5-7 scales
+  the 1 "by 448/10"): r = 448 / amax is formed once per row in FP32
+  (correctly rounded), then t = x * r in FP32 (one rounding), and the stored
+  scale is amax / 448 in FP32; FP32 because the quantised code is an
+  integer decision that both sides must take in the same precision.
 * A row of zeros has scale 0 and codes of signed zero; a row holding a NaN
   has a NaN scale and NaN codes (0x7F) everywhere; a row holding +-inf (and
   no NaN) has an infinite scale, codes 0x7F for the infinite elements and
@@ -95,8 +96,9 @@ def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
     with np.errstate(invalid="ignore"):
         amax = np.max(np.abs(x32), axis=1)                       # NaN if the row holds one
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    with np.errstate(invalid="ignore", divide="ignore"):
-        t = (x32 * np.float32(E4M3_MAX)) / amax[:, None]          # float32 ops throughout
+    with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+        r = (np.float32(E4M3_MAX) / amax).astype(np.float32)      # per-row factor, float32
+        t = x32 * r[:, None]                                      # float32 product
     t = np.where((amax == 0)[:, None], x32, t)                    # a zero row keeps its zeros
     return e4m3_encode(t), scale
 
