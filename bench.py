@@ -67,7 +67,8 @@ def workload_table():
     t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
          "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu(),
          "ffn_gated_bf16": W.ffn_gated_bf16(), "ffn_share_bf16": W.ffn_share_bf16(),
-         "ffn_gated_share_bf16": W.ffn_gated_share_bf16()}
+         "ffn_gated_share_bf16": W.ffn_gated_share_bf16(), "fp8_ffn": W.fp8_ffn_bf16(),
+         "fp8_4096x1536x4096": W.fp8_quant_example()}
     for s in W.HGEMM_SHAPES:
         c = W.hgemm_colmajor(*s)
         t[c.name] = c
@@ -83,9 +84,16 @@ def algorithmic(case):
     if case.extra.get("gated"):     # two products sharing X; one output
         flops = 2 * cm.gemm_flops(case.M, case.N, case.K)
         return flops, es * (case.M * case.K + 2 * case.K * case.N + case.M * case.N)
+    if case.extra.get("fp8"):       # quantise X (read X, write codes), then the FP8 product
+        M, N, K = case.M, case.N, case.K
+        return cm.gemm_flops(M, N, K), es * M * K + 2 * M * K + N * K + es * M * N
     flops = cm.gemm_flops(case.M, case.N, case.K)
     nbytes = cm.min_bytes(case.M, case.N, case.K, es) + (es * case.M * case.N if case.beta else 0)
     return flops, nbytes
+
+
+def peak_key(case) -> str:
+    return "fp8" if case.extra.get("fp8") else case.dtype
 
 
 def is_hbm_bound(case) -> bool:
@@ -102,7 +110,25 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
 
     stream = torch.cuda.current_stream()
     epilogue = case.extra.get("epilogue", "none")
-    if case.extra.get("gated"):
+    if case.extra.get("fp8"):
+        # One step: quantise X per row, then the FP8 product with the weights
+        # (quantised once, before timing).
+        A, B, C0 = case.make()
+        M, N, K = case.M, case.N, case.K
+        dX, dW = A.cuda(), B.cuda()
+        qx = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+        qw = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+        sx = torch.empty(M, dtype=torch.float32, device="cuda")
+        sw = torch.empty(N, dtype=torch.float32, device="cuda")
+        mg.mgemm_quantize_fp8(h, N, K, dW, case.ldb, case.dtype, qw, K, sw, stream=stream)
+        dC = [c_initial(case, None).cuda()]
+        kname = "fp8_quant+fp8_gemm"
+
+        def launch(i):
+            mg.mgemm_quantize_fp8(h, M, K, dX, case.lda, case.dtype, qx, K, sx, stream=stream)
+            mg.mgemm_run_fp8(h, "auto", M, N, K, case.alpha, qx, K, sx, qw, K, sw, 0.0, dC[0],
+                             case.ldc, case.dtype, stream=stream)
+    elif case.extra.get("gated"):
         import workloads as W
         X, Wg, Wu = W.gated_inputs(case)
         A, B, C0 = X, (Wg, Wu), None
@@ -229,6 +255,8 @@ def cpu_baseline(case, out_dev, budget_s):
     from workloads import storage_view
 
     A, B, C0 = case.inputs
+    if case.extra.get("fp8"):
+        return cpu_baseline_fp8(case, out_dev, budget_s)
     gated = bool(case.extra.get("gated"))
     a = storage_view(A)
     bs = [storage_view(x) for x in (B if gated else (B,))]
@@ -272,6 +300,49 @@ def cpu_baseline(case, out_dev, budget_s):
                  len(rows_done), case.M, flops / 1e9, t_total)},
             {"rows": len(rows_done), "max_err": rep["max_err"], "tol": rep["tol"],
              "ok": rep["ok"]})
+
+
+def cpu_baseline_fp8(case, out_dev, budget_s):
+    """The FP8 oracle on a row sample: quantise the sampled rows of X, multiply
+    by the weight codes (quantised once, not timed, like the GPU's), and check
+    the sample against the GPU output within the FP32-accumulation bound."""
+    import numpy as np
+    import oracle
+    from oracle import fp8 as f8
+    from tests import parity as P
+    from workloads import storage_view
+
+    A, B, _ = case.inputs
+    M, N, K = case.M, case.N, case.K
+    X = oracle.decode(case.dtype, storage_view(A)).reshape(M, case.lda)[:, :K]
+    Wv = oracle.decode(case.dtype, storage_view(B)).reshape(N, case.ldb)[:, :K]
+    qw, sw = f8.quantize_rows(Wv)
+    rng = np.random.default_rng(0)
+    nrows = max(1, min(M, 8))
+    while True:
+        rows = np.sort(rng.choice(M, size=nrows, replace=False)) if nrows < M else np.arange(M)
+        t0 = time.perf_counter()
+        qx, sx = f8.quantize_rows(X[rows])
+        exact = f8.fp8_gemm(len(rows), N, K, case.alpha, qx.ravel(), K, sx, qw.ravel(), K, sw)
+        dt = time.perf_counter() - t0
+        if nrows >= M or dt * 2 > budget_s:
+            break
+        nrows = int(min(M, max(nrows * 2, nrows * budget_s / max(dt, 1e-3) * 0.8)))
+    got = oracle.decode(case.dtype, storage_view(out_dev.cpu())).reshape(-1, case.ldc)[rows, :N]
+    tol = P.tol_f32_rel(K) * float(np.max(np.abs(exact))) + \
+        P._ulp(case.dtype, oracle.round_to(case.dtype, exact)) / 2
+    err = np.abs(got - exact)
+    flops = 2.0 * len(rows) * N * K
+    try:                                  # threads of numpy's BLAS (the matmul step)
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                     # threadpoolctl missing or unreadable
+        cores = 1
+    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+             "sample": "%d of %d rows of C: FP8 quantisation + product (%.1f GFLOP in %.1f s, "
+                       "numpy FP64)" % (len(rows), M, flops / 1e9, dt)},
+            {"rows": len(rows), "max_err": float(np.max(err)), "tol": float(np.max(tol)),
+             "ok": bool(np.all(err <= tol))})
 
 
 def traffic_for(kernel, workload):
@@ -338,7 +409,7 @@ def main():
         achieved, peak, unit, bound = nbytes / per_launch_s / 1e9, cm.PEAK_HBM_GBS, "GB/s", "hbm"
         value, vunit = nbytes / (r["ms_per_step"] * 1e-3) / 1e9, "GB/s"
     else:
-        achieved, peak = flops / per_launch_s / 1e12, cm.PEAK_TFLOPS[case.dtype]
+        achieved, peak = flops / per_launch_s / 1e12, cm.PEAK_TFLOPS[peak_key(case)]
         unit, bound = "TFLOP/s", "mfma"
         value, vunit = flops / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
     traffic = traffic_for(r["kernel"], case.name)
@@ -388,7 +459,7 @@ def main():
                 ent.update(GBs=round(b2 / s / 1e9, 1), frac_hbm=round(b2 / s / 1e9 / cm.PEAK_HBM_GBS, 4))
             else:
                 tf = f2 / s / 1e12
-                ent.update(TFLOPs=round(tf, 2), frac_peak=round(tf / cm.PEAK_TFLOPS[c.dtype], 4))
+                ent.update(TFLOPs=round(tf, 2), frac_peak=round(tf / cm.PEAK_TFLOPS[peak_key(c)], 4))
             others[name] = ent
             del rr
             torch.cuda.empty_cache()

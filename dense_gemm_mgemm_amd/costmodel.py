@@ -9,7 +9,7 @@ from __future__ import annotations
 import math
 
 # MI355X published peaks (dense, no sparsity).
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "f64": 78.6}
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "f32": 157.3, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
 N_CU = 256
 N_XCD = 8
