@@ -232,6 +232,21 @@ template <> struct Elem<BF16> {
     static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
 };
 
+// Raises a kernel's dynamic LDS limit once per device (the attribute is held
+// per device).  done[] is the caller's per-kernel flag array; two threads
+// that race on a first call both set the same value, which is harmless.
+constexpr int MAX_DEVICES = 64;
+inline hipError_t set_lds_limit_once(const void* kern, int lds, bool (&done)[MAX_DEVICES]) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool track = dev >= 0 && dev < MAX_DEVICES;
+    if (track && done[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && track) done[dev] = true;
+    return e;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers (each kernel file defines its own).  They return a HIP error of
 // the launch; shape/alignment eligibility is checked by the *_supports calls.

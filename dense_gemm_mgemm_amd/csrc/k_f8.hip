@@ -230,8 +230,11 @@ __global__ __launch_bounds__(256) void k_quant_rows_reg(int64_t M, int64_t K, co
 // ---------------------------------------------------------------------------
 // FP8 GEMM on the matrix cores
 // ---------------------------------------------------------------------------
+#ifndef MGEMM_F8_SLOTS
+#define MGEMM_F8_SLOTS 4
+#endif
 constexpr int BM = 256, BK = 64, NT = 256;
-constexpr int SLOTS = 4, AHEAD = SLOTS - 1;
+constexpr int SLOTS = MGEMM_F8_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
 constexpr int ROW = BK;                          // bytes per operand row per slice
 constexpr int A_BYTES = BM * ROW;                // 16 KiB of A per slot
 constexpr int A_COPIES = 4;                      // 1 KiB copies of A per wave per slice
@@ -257,9 +260,11 @@ __device__ __forceinline__ void wait_vm() {
 // Wait until at most n slices of L copies each are still in flight.
 template <int L>
 __device__ __forceinline__ void wait_slices(int n) {
+    static_assert(3 * L < 64, "vmcnt range");
     if (n <= 0) wait_vm<0>();
     else if (n == 1) wait_vm<L>();
-    else wait_vm<2 * L>();
+    else if (n == 2) wait_vm<2 * L>();
+    else wait_vm<3 * L>();
 }
 // Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l).  Inline
 // asm: the compiler would otherwise drain every copy in flight before any LDS
@@ -525,13 +530,9 @@ template <int CT, int BN>
 hipError_t launch_f8_dma(const Problem& p, const F8Args& f, hipStream_t s) {
     auto kern = k_f8_dma<CT, BN>;
     const size_t lds = (size_t)SLOTS * F8Cfg<BN>::SLOT_BYTES;
-    static bool attr_set = false;     // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[MAX_DEVICES] = {};
+    if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
+        return e;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p, f);
     return hipGetLastError();

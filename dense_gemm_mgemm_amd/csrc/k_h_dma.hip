@@ -456,13 +456,9 @@ template <int DT, int BN, bool DUAL, int EPI>
 hipError_t launch_epi(const Problem& p, const HSplit& sp, hipStream_t s) {
     auto kern = k_h_dma<DT, BN, DUAL, EPI>;
     const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
-    static bool attr_set = false;     // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[MAX_DEVICES] = {};
+    if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
+        return e;
     constexpr int OUT = Cfg<BN, DUAL>::OUT;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + OUT - 1) / OUT);
     hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * sp.ksplit)), dim3(NT), lds, s, p, sp);

@@ -285,13 +285,9 @@ template <int DT, int BM, int BN, bool AKC, bool BKC>
 hipError_t launch_one(const Problem& p, hipStream_t s) {
     auto kern = k_h_mfma<DT, BM, BN, AKC, BKC>;
     const size_t lds = (size_t)2 * (BM + BN) * LDS_ROW * sizeof(uint16_t);
-    static bool attr_set = false;   // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[MAX_DEVICES] = {};
+    if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
+        return e;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p);
     return hipGetLastError();

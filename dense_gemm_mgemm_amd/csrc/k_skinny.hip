@@ -244,13 +244,9 @@ hipError_t launch_cfg(const Problem& p, hipStream_t s) {
     auto kern = k_skinny<DT, MT, BN>;
     constexpr int SLOT = KS * BN * 2 + MT * KS * 2;
     const size_t lds = (size_t)NW * SLOTS * SLOT;
-    static bool attr_set = false;     // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[MAX_DEVICES] = {};
+    if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
+        return e;
     const int64_t blocks = (p.N + BN - 1) / BN;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), lds, s, p);
     return hipGetLastError();

@@ -369,13 +369,9 @@ template <int DT, int MT>
 hipError_t launch_cfg(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
     auto kern = k_skinny_sk<DT, MT>;
     const size_t lds = (size_t)SLOTS * (W_BYTES + MT * KS * 2);
-    static bool attr_set = false;     // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool attr_set[MAX_DEVICES] = {};
+    if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds, s, p, sa);
     return hipGetLastError();
 }
