@@ -92,8 +92,8 @@ def load(path: str | None = None):
     lib.mgemm_weighted_choice.argtypes = [ctypes.c_int32, ctypes.c_int32, pdbl, pdbl]
     lib.mgemm_weighted_choice.restype = ctypes.c_int32
     lib.mgemm_quantize_fp8.argtypes = [vp, i64, i64, vp, i64, ci, vp, i64, vp, vp]
-    lib.mgemm_run_fp8.argtypes = [vp, ci, i64, i64, i64, f32, vp, i64, vp, vp, i64, vp, f32, vp,
-                                  i64, ci, vp]
+    lib.mgemm_run_fp8.argtypes = [vp, ci, ctypes.c_int32, i64, i64, i64, f32, vp, i64, vp, vp, i64,
+                                  vp, f32, vp, i64, ci, vp]
     lib.mgemm_select_kernel.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(ci)]
     for name in ("mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "mgemm_run_ex",
                  "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
@@ -292,14 +292,15 @@ def mgemm_quantize_fp8(h, M, K, X, ldx, xtype, Q, ldq, scales, stream=None) -> N
 
 
 def mgemm_run_fp8(h, kernel, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, ctype,
-                  stream=None) -> None:
-    """C = alpha * sa[m] * sb[n] * sum_k A[m,k] B[n,k] + beta * C on E4M3 codes."""
+                  stream=None, ksplit=0) -> None:
+    """C = alpha * sa[m] * sb[n] * sum_k A[m,k] B[n,k] + beta * C on E4M3 codes
+    (ksplit: 0 = the library's choice, 1 = no split, n = at most n K ranges)."""
     k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
-    st = load().mgemm_run_fp8(h, k, int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
-                              _ptr(sa), _ptr(B), int(ldb), _ptr(sb), float(beta), _ptr(C),
-                              int(ldc), _enum(ctype, _DTYPE), _stream(stream))
+    st = load().mgemm_run_fp8(h, k, int(ksplit), int(M), int(N), int(K), float(alpha), _ptr(A),
+                              int(lda), _ptr(sa), _ptr(B), int(ldb), _ptr(sb), float(beta),
+                              _ptr(C), int(ldc), _enum(ctype, _DTYPE), _stream(stream))
     if st != MGEMM_SUCCESS:
-        raise MgemmError(st, "mgemm_run_fp8(%s)" % kernel)
+        raise MgemmError(st, "mgemm_run_fp8(%s, %d)" % (kernel, ksplit))
 
 
 def mgemm_select_kernel(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

@@ -286,7 +286,12 @@ hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx,
 bool f8_mfma_supports(const Problem& p, int bn);          // bn = 256 or 192
 bool f8_general_supports(const Problem& p);
 // bn: the MFMA kernel's tile width (256 or 192), 0 for the scalar kernel.
-hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, hipStream_t s);
+// ksplit > 1 (MFMA kernel only) cuts K into ranges of whole 64-slices (two
+// launches, partials in ws); f8_splits turns a request into the number of
+// ranges used (0 when the partials do not fit the workspace).
+int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws);
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, int ksplit,
+                          const Workspace& ws, hipStream_t s);
 // n elements of dtype at p get small exact values (a hash of the index and seed).
 hipError_t launch_fill_pattern(void* p, int64_t n, int dtype, uint32_t seed, hipStream_t s);
 bool skinny_supports(const Problem& p);

@@ -299,6 +299,9 @@ __device__ __forceinline__ f32x16 mfma8(const i32x4 (&x)[2], const i32x4 (&y)[2]
 struct F8Args {
     const float* sa;      // M scales of A's rows
     const float* sb;      // N scales of B's rows (output columns)
+    float* part;          // split K: [tile][range][chunk][thread] f32x4 partial sums
+    int ksplit;           // K ranges (1: no split)
+    int nks;              // 64-slices per range (the last range may hold fewer)
 };
 
 template <int CT>
@@ -383,7 +386,7 @@ __device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[TM][BN / 64], co
     }
 }
 
-template <int CT, int BN>
+template <int CT, int BN, bool PARTIAL>
 __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     using G = F8Cfg<BN>;
     constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
@@ -393,13 +396,19 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    // Position range * tiles + tile in an order where each XCD's workgroups
+    // are consecutive (as in k_h_dma.hip's split of K).
+    const int ntiles = tiles_m * tiles_n;
+    const int pos = xcd_linear(blockIdx.x, gridDim.x);
+    const int split = pos / ntiles;
     int tmi, tni;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+    tile_from_linear(pos - split * ntiles, tiles_m, tiles_n, 8, tmi, tni);
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-    const uint8_t* __restrict__ A = (const uint8_t*)p.A;
-    const uint8_t* __restrict__ B = (const uint8_t*)p.B;
+    const int64_t k0 = (int64_t)split * f.nks * BK;         // first K of this range
+    const uint8_t* __restrict__ A = (const uint8_t*)p.A + k0;
+    const uint8_t* __restrict__ B = (const uint8_t*)p.B + k0;
 
     // Copies of this wave: rows [64w, 64w+64) of the A tile and
     // [BN/4*w, BN/4*(w+1)) of the B tile, 16 rows per copy (lane l: row
@@ -481,7 +490,8 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         }
     };
 
-    const int nk = (int)(p.K / BK);
+    const int nk_all = (int)(p.K / BK);
+    const int nk = nk_all - split * f.nks < f.nks ? nk_all - split * f.nks : f.nks;
     const int npro = nk < AHEAD ? nk : AHEAD;
     for (int s = 0; s < npro; ++s)
         for (int i = 0; i < COPIES; ++i) copy(s, i);
@@ -520,7 +530,62 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     }
 
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
+    if constexpr (PARTIAL) {
+        // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3].
+        float* dst = f.part + ((int64_t)(tmi * tiles_n + tni) * f.ksplit + split) *
+                                  (int64_t)(NT * TM * TN * 16) + 4 * tid;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& a = acc[tm][tn];
+                    const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    *(f32x4*)(dst + (int64_t)((tm * TN + tn) * 4 + q) * NT * 4) = v;
+                }
+        return;
+    }
     f8_epilogue<CT, BN>(acc, p, f.sa, f.sb, p.C, lane, wm, wn, m0, n0, mlim, nlim);
+}
+
+// Second split-K phase: one thread per 16-byte chunk of a tile's
+// accumulators sums the K ranges in range order, then scales and stores the
+// four outputs as the one-phase epilogue would.
+template <int CT, int BN>
+__global__ __launch_bounds__(NT) void k_f8_reduce(Problem p, F8Args f) {
+    constexpr int TN = BN / 64, CH = TM * TN * 4;
+    constexpr int64_t TILE_FLOATS = (int64_t)NT * TM * TN * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_n = (int)((p.N + BN - 1) / BN);
+    const int t = blockIdx.x / CH, c = blockIdx.x % CH;
+    const int tm = c / (TN * 4), tn = (c / 4) % TN, q = c % 4;
+    const int64_t m0 = (int64_t)(t / tiles_n) * BM, n0 = (int64_t)(t % tiles_n) * BN;
+    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const int mi = 128 * wm + 32 * tm + (lane & 31);
+    const int ni = BN / 2 * wn + 32 * tn + 8 * q + 4 * (lane >> 5);
+    if (mi >= mlim || ni >= nlim) return;
+    const float* src = f.part + (int64_t)t * f.ksplit * TILE_FLOATS + (int64_t)c * NT * 4 + 4 * tid;
+    f32x4 a = *(const f32x4*)src;
+    int s = 1;
+    for (; s + 4 <= f.ksplit; s += 4) {
+        const f32x4 b0 = *(const f32x4*)(src + s * TILE_FLOATS);
+        const f32x4 b1 = *(const f32x4*)(src + (s + 1) * TILE_FLOATS);
+        const f32x4 b2 = *(const f32x4*)(src + (s + 2) * TILE_FLOATS);
+        const f32x4 b3 = *(const f32x4*)(src + (s + 3) * TILE_FLOATS);
+        a = (((a + b0) + b1) + b2) + b3;
+    }
+    for (; s < f.ksplit; ++s) a = a + *(const f32x4*)(src + s * TILE_FLOATS);
+    const int nn = nlim - ni < 4 ? nlim - ni : 4;
+    const float sam = f.sa[m0 + mi];
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p.alpha * ((a[e] * sam) * (e < nn ? f.sb[n0 + ni + e] : 0.0f));
+    const int es = CT == F32 ? 4 : 2;
+    const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & (4 * es - 1)) == 0);
+    store4<CT>(p.C, p.ldc, m0 + mi, n0 + ni, nn, vec_ok, p.beta, v);
 }
 
 // Any K, alignment and leading dimension: one thread per output, codes
@@ -563,23 +628,30 @@ hipError_t launch_quant_xt(int64_t M, int64_t K, const void* X, int64_t ldx, uin
     return hipGetLastError();
 }
 
-template <int CT, int BN>
+template <int CT, int BN, bool PARTIAL>
 hipError_t launch_f8_dma(const Problem& p, const F8Args& f, hipStream_t s) {
-    auto kern = k_f8_dma<CT, BN>;
+    auto kern = k_f8_dma<CT, BN, PARTIAL>;
     const size_t lds = (size_t)SLOTS * F8Cfg<BN>::SLOT_BYTES;
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
         return e;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NT), lds, s, p, f);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * f.ksplit)), dim3(NT), lds, s, p, f);
+    if constexpr (PARTIAL) {
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        constexpr int CH = TM * (BN / 64) * 4;
+        hipLaunchKernelGGL((k_f8_reduce<CT, BN>), dim3((unsigned)(tiles * CH)), dim3(NT), 0, s, p, f);
+    }
     return hipGetLastError();
 }
 
 // bn: 256 or 192 for the MFMA kernel, 0 for the scalar kernel.
 template <int CT>
 hipError_t launch_f8_ct(const Problem& p, const F8Args& f, int bn, hipStream_t s) {
-    if (bn == 256) return launch_f8_dma<CT, 256>(p, f, s);
-    if (bn == 192) return launch_f8_dma<CT, 192>(p, f, s);
+    if (bn == 256)
+        return f.ksplit > 1 ? launch_f8_dma<CT, 256, true>(p, f, s) : launch_f8_dma<CT, 256, false>(p, f, s);
+    if (bn == 192)
+        return f.ksplit > 1 ? launch_f8_dma<CT, 192, true>(p, f, s) : launch_f8_dma<CT, 192, false>(p, f, s);
     const int64_t n = p.M * p.N;
     hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, f);
     return hipGetLastError();
@@ -604,8 +676,25 @@ bool f8_mfma_supports(const Problem& p, int bn) {
 
 bool f8_general_supports(const Problem& p) { return (p.M * p.N + 255) / 256 <= 0x7fffffff; }
 
-hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, hipStream_t s) {
-    const F8Args f{sa, sb};
+int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
+    const int64_t nk = p.K / BK;
+    if (requested <= 1 || nk < 2) return 1;
+    int64_t ks = requested < nk ? requested : nk;
+    const int64_t nks = (nk + ks - 1) / ks;                 // whole 64-slices per range
+    ks = (nk + nks - 1) / nks;
+    if (ws.part == nullptr || tiles * ks * (int64_t)BM * bn * 4 > ws.part_bytes) return 0;
+    return (int)ks;
+}
+
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, int ksplit,
+                          const Workspace& ws, hipStream_t s) {
+    F8Args f{sa, sb, (float*)ws.part, 1, (int)(p.K / BK)};
+    if (bn != 0 && ksplit > 1) {
+        const int nk = (int)(p.K / BK);
+        f.nks = (nk + ksplit - 1) / ksplit;
+        f.ksplit = (nk + f.nks - 1) / f.nks;
+    }
     if (p.dtype == F32) return launch_f8_ct<F32>(p, f, bn, s);
     if (p.dtype == F16) return launch_f8_ct<F16>(p, f, bn, s);
     return launch_f8_ct<BF16>(p, f, bn, s);

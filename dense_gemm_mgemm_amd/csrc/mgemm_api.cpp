@@ -407,11 +407,14 @@ mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const 
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
-mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M, int64_t N,
-                             int64_t K, float alpha, const void* A, int64_t lda, const float* sa,
-                             const void* B, int64_t ldb, const float* sb, float beta, void* C,
-                             int64_t ldc, mgemm_dtype_t ctype, hipStream_t stream) {
+mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ksplit, int64_t M,
+                             int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                             const float* sa, const void* B, int64_t ldb, const float* sb,
+                             float beta, void* C, int64_t ldc, mgemm_dtype_t ctype,
+                             hipStream_t stream) {
     if (!h || M < 0 || N < 0 || K < 0 || !valid_dtype(ctype)) return MGEMM_ERR_INVALID_ARG;
+    if (ksplit < 0 || ksplit > MGEMM_MAX_KSPLIT || (kernel == MGEMM_KERNEL_AUTO && ksplit != 0))
+        return MGEMM_ERR_INVALID_ARG;
     if (kernel != MGEMM_KERNEL_AUTO && kernel != MGEMM_KERNEL_F8_MFMA &&
         kernel != MGEMM_KERNEL_F8_MFMA_192 && kernel != MGEMM_KERNEL_F8_GENERAL)
         return MGEMM_ERR_INVALID_ARG;
@@ -436,30 +439,48 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M,
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
     if (!A || !B || !sa || !sb) return MGEMM_ERR_INVALID_ARG;
-    int bn = -1;                     // MFMA tile width, 0 = scalar kernel
+    // The MFMA kernel's time per (width, split) by the 16-bit time model: a
+    // 64-wide FP8 slice moves the bytes of a 32-wide 16-bit slice and measured
+    // the same time per slice (0.59 us for 256x192 tiles at 1024x12288).
+    Problem q = p;
+    q.K = p.K / 2;
+    auto best_split = [&](int w, double* t_out) {
+        int best = 1;
+        double bt = 1e300;
+        for (int req = 1, last = 0; req <= MGEMM_MAX_KSPLIT; ++req) {
+            const int ks = mgemm::f8_splits(p, w, req, h->ws);
+            if (ks <= last) continue;
+            last = ks;
+            const double t = predict_us(q, 256, w, w, w == 256 ? 1.4 : 1.3, 1, ks);
+            if (t < bt) { bt = t; best = ks; }
+        }
+        if (t_out) *t_out = bt;
+        return best;
+    };
+    int bn = -1, ks = 1;                 // MFMA tile width (0 = scalar kernel), K ranges
     if (kernel == MGEMM_KERNEL_F8_MFMA || kernel == MGEMM_KERNEL_F8_MFMA_192) {
         bn = kernel == MGEMM_KERNEL_F8_MFMA ? 256 : 192;
         if (!mgemm::f8_mfma_supports(p, bn)) return MGEMM_ERR_UNSUPPORTED;
+        ks = ksplit == 0 ? best_split(bn, nullptr) : mgemm::f8_splits(p, bn, ksplit, h->ws);
+        if (ks < 1) return MGEMM_ERR_UNSUPPORTED;
     } else if (kernel == MGEMM_KERNEL_F8_GENERAL) {
         if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
+        if (ksplit > 1) return MGEMM_ERR_UNSUPPORTED;
         bn = 0;
     } else {
-        // The width with the fewest tile-columns of CU time (waves of tiles
-        // times the tile width); ties keep the wider tile.
-        const int64_t slots = h->num_cu > 0 ? h->num_cu : 256;
-        int64_t best = -1;
+        double best_t = 1e300;
         for (int w : {256, 192}) {
             if (!mgemm::f8_mfma_supports(p, w)) continue;
-            const int64_t tiles = ((M + 255) / 256) * ((N + w - 1) / w);
-            const int64_t cost = (tiles + slots - 1) / slots * w;
-            if (best < 0 || cost < best) { best = cost; bn = w; }
+            double t;
+            const int k2 = best_split(w, &t);
+            if (t < best_t) { best_t = t; bn = w; ks = k2; }
         }
         if (bn < 0) {
             if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
             bn = 0;
         }
     }
-    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, bn, stream);
+    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, bn, ks, h->ws, stream);
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 

@@ -385,19 +385,26 @@ mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const 
  *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA or
  *        MGEMM_KERNEL_F8_MFMA_192 (K % 64 == 0, lda and ldb multiples of 16,
  *        16-byte aligned A and B) or MGEMM_KERNEL_F8_GENERAL (anything).
- *        AUTO takes the MFMA tile width whose grid fills the CUs better.
+ *        AUTO takes the MFMA tile width and split of K with the smallest
+ *        predicted time.
+ *   ksplit : 0 = the library's choice, 1 = no split, 2 .. MGEMM_MAX_KSPLIT =
+ *        at most that many K ranges of whole 64-element slices (MFMA kernels
+ *        only), summed in range order by a second launch as mgemm_run_variant
+ *        describes; a forced split with MGEMM_KERNEL_AUTO is invalid.
  * Products of codes are exact; the K sum accumulates in FP32 and the scales
  * are applied to it once: v = alpha * ((acc * sa[m]) * sb[n]).
  * M == 0 or N == 0 does nothing; K == 0 or alpha == 0 gives C = beta * C.
  * Asynchronous on `stream`.
  * Errors: MGEMM_ERR_INVALID_ARG (sizes, strides, NULL pointers, ctype,
- * kernel not an FP8 kernel); MGEMM_ERR_UNSUPPORTED when a forced kernel
- * cannot run the problem; MGEMM_ERR_HIP for a failed launch.
+ * kernel not an FP8 kernel, ksplit out of range); MGEMM_ERR_UNSUPPORTED when
+ * a forced kernel or split cannot run the problem (partials larger than the
+ * workspace); MGEMM_ERR_HIP for a failed launch.
  */
-mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int64_t M, int64_t N,
-                             int64_t K, float alpha, const void* A, int64_t lda, const float* sa,
-                             const void* B, int64_t ldb, const float* sb, float beta, void* C,
-                             int64_t ldc, mgemm_dtype_t ctype, hipStream_t stream);
+mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ksplit, int64_t M,
+                             int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                             const float* sa, const void* B, int64_t ldb, const float* sb,
+                             float beta, void* C, int64_t ldc, mgemm_dtype_t ctype,
+                             hipStream_t stream);
 
 /* Static strings; never NULL (unknown values give "unknown"). */
 const char* mgemm_status_string(mgemm_status_t s);

@@ -126,7 +126,8 @@ def test_fp8_gemm_integer_bit_exact(h, M, N, K, ctype):
     exact = fp8.fp8_gemm(M, N, K, alpha, pa.ravel(), lda, sa, pb.ravel(), ldb, sb, beta, c0[:, :N])
     want = oracle.encode(ctype, exact)
     ran = 0
-    for kernel in ("auto", "f8_mfma_256x256", "f8_mfma_256x192", "f8_general"):
+    for kernel, ks in (("auto", 0), ("f8_mfma_256x256", 1), ("f8_mfma_256x256", 3),
+                       ("f8_mfma_256x192", 0), ("f8_mfma_256x192", 32), ("f8_general", 1)):
         dA = torch.from_numpy(pa.ravel()).cuda()
         dB = torch.from_numpy(pb.ravel()).cuda()
         dsa, dsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
@@ -134,18 +135,18 @@ def test_fp8_gemm_integer_bit_exact(h, M, N, K, ctype):
         dC = torch.from_numpy(c0_bits.view(host_view).copy().ravel()).cuda()
         try:
             mg.mgemm_run_fp8(h, kernel, M, N, K, alpha, dA, lda, dsa, dB, ldb, dsb, beta, dC, ldc,
-                             ctype)
+                             ctype, ksplit=ks)
         except mg.MgemmError as e:
             assert e.status == mg.MGEMM_ERR_UNSUPPORTED and kernel.startswith("f8_mfma") and K % 64
             continue
         torch.cuda.synchronize()
         got = dC.cpu().numpy().view(c0_bits.dtype).reshape(M, ldc)
-        say("fp8 gemm", (M, N, K), ctype, kernel)
+        say("fp8 gemm", (M, N, K), ctype, kernel, ks)
         bad = np.argwhere(got[:, :N] != want)
         assert bad.size == 0, (kernel, bad[:5], got[tuple(bad[0])], want[tuple(bad[0])])
         assert np.array_equal(got[:, N:], c0_bits[:, N:])   # ldc padding untouched
         ran += 1
-    assert ran >= (4 if K % 64 == 0 else 2)
+    assert ran >= (6 if K % 64 == 0 else 2)
 
 
 def fp8_inputs(case):
@@ -211,6 +212,18 @@ def test_fp8_deterministic_and_errors(h):
         with pytest.raises(mg.MgemmError) as ei:
             mg.mgemm_run_fp8(h, kernel, *args)
         assert ei.value.status == want
+    for kernel, ks, want in (("auto", 2, mg.MGEMM_ERR_INVALID_ARG),
+                             ("f8_mfma_256x256", 33, mg.MGEMM_ERR_INVALID_ARG),
+                             ("f8_general", 2, mg.MGEMM_ERR_UNSUPPORTED)):
+        with pytest.raises(mg.MgemmError) as ei:
+            mg.mgemm_run_fp8(h, kernel, M, N, K, 1.0, qa, K, sa, qb, K, sb, 0.0, C, N, "bf16",
+                             ksplit=ks)
+        assert ei.value.status == want, (kernel, ks)
+    # A split forced on the 8k problem needs more partials than the workspace holds.
+    with pytest.raises(mg.MgemmError) as ei:
+        mg.mgemm_run_fp8(h, "f8_mfma_256x256", 8192, 8192, 16384, 1.0, qa, 16384, sa, qb, 16384,
+                         sb, 0.0, C, 8192, "bf16", ksplit=8)
+    assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
     with pytest.raises(mg.MgemmError) as ei:       # lda below K
         mg.mgemm_run_fp8(h, "auto", M, N, K, 1.0, qa, K - 1, sa, qb, K, sb, 0.0, C, N, "bf16")
     assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG
