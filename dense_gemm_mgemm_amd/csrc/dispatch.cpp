@@ -57,13 +57,18 @@ int kernel_of(const char* s) {
 
 // Mean time of one call of variant c (microseconds): two warm-up calls, one
 // call to size the runs, then the best of two runs of 3..50 calls (about
-// 2 ms each).  +inf if a launch fails.
-double time_choice(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s, hipEvent_t e0,
-                   hipEvent_t e1) {
+// 2 ms each).  Consecutive calls use the operand sets in turn (probs[i % n]),
+// so memory-bound shapes are timed streaming from HBM rather than from the
+// 256 MiB last-level cache.  +inf if a launch fails.
+double time_choice(mgemm_handle_t h, const std::vector<Problem>& probs, Choice c, hipStream_t s,
+                   hipEvent_t e0, hipEvent_t e1) {
+    const size_t np = probs.size();
+    size_t next = 0;
+    auto run = [&]() { return launch(h, probs[next++ % np], c, s) == MGEMM_SUCCESS; };
     for (int i = 0; i < 2; ++i)
-        if (launch(h, p, c, s) != MGEMM_SUCCESS) return INFINITY;
+        if (!run()) return INFINITY;
     float ms = 0.f;
-    if (hipEventRecord(e0, s) != hipSuccess || launch(h, p, c, s) != MGEMM_SUCCESS ||
+    if (hipEventRecord(e0, s) != hipSuccess || !run() ||
         hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
         hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
         return INFINITY;
@@ -73,7 +78,7 @@ double time_choice(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s, 
     for (int round = 0; round < 2; ++round) {
         if (hipEventRecord(e0, s) != hipSuccess) return INFINITY;
         for (int i = 0; i < reps; ++i)
-            if (launch(h, p, c, s) != MGEMM_SUCCESS) return INFINITY;
+            if (!run()) return INFINITY;
         if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
             hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
             return INFINITY;
@@ -87,8 +92,8 @@ double time_choice(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s, 
 const int TUNE_SPLITS[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32};
 
 struct DeviceBuffers {
-    void* a = nullptr;
-    void* b = nullptr;
+    void* a = nullptr;    // `sets` consecutive copies of the largest A
+    void* b = nullptr;    // and of the largest B
     void* c = nullptr;
     ~DeviceBuffers() {
         if (a) (void)hipFree(a);
@@ -96,6 +101,14 @@ struct DeviceBuffers {
         if (c) (void)hipFree(c);
     }
 };
+
+// Operand sets for the timing runs: enough copies that the largest A and B
+// together exceed twice the 256 MiB last-level cache, at most 64.
+int operand_sets(size_t ab_bytes) {
+    const size_t want = (size_t)512 << 20;
+    size_t n = ab_bytes ? (want + ab_bytes - 1) / ab_bytes : 1;
+    return (int)(n < 1 ? 1 : (n > 64 ? 64 : n));
+}
 
 struct Events {
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -158,14 +171,18 @@ mgemm_status_t mgemm_tune(mgemm_handle_t h, mgemm_dtype_t dtype, mgemm_layout_t 
         nc = M[i] * N[i] > nc ? M[i] * N[i] : nc;
     }
     const size_t es = dtype == MGEMM_F32 ? 4 : 2;
+    // Round A and B up to 256-byte multiples so every set stays aligned.
+    const size_t a_bytes = ((size_t)na * es + 255) & ~(size_t)255;
+    const size_t b_bytes = ((size_t)nb * es + 255) & ~(size_t)255;
+    const int sets = operand_sets(a_bytes + b_bytes);
     DeviceBuffers buf;
     Events ev;
-    if (hipMalloc(&buf.a, (size_t)na * es) != hipSuccess || hipMalloc(&buf.b, (size_t)nb * es) != hipSuccess ||
+    if (hipMalloc(&buf.a, a_bytes * sets) != hipSuccess || hipMalloc(&buf.b, b_bytes * sets) != hipSuccess ||
         hipMalloc(&buf.c, (size_t)nc * es) != hipSuccess || hipEventCreate(&ev.e0) != hipSuccess ||
         hipEventCreate(&ev.e1) != hipSuccess)
         return MGEMM_ERR_HIP;
-    if (mgemm::launch_fill_pattern(buf.a, na, (int)dtype, 1u, stream) != hipSuccess ||
-        mgemm::launch_fill_pattern(buf.b, nb, (int)dtype, 2u, stream) != hipSuccess ||
+    if (mgemm::launch_fill_pattern(buf.a, (int64_t)(a_bytes * sets / es), (int)dtype, 1u, stream) != hipSuccess ||
+        mgemm::launch_fill_pattern(buf.b, (int64_t)(b_bytes * sets / es), (int)dtype, 2u, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return MGEMM_ERR_HIP;
 
@@ -185,17 +202,22 @@ mgemm_status_t mgemm_tune(mgemm_handle_t h, mgemm_dtype_t dtype, mgemm_layout_t 
 
     for (int i = 0; i < n; ++i) {
         const int64_t lda = rowA ? K[i] : M[i], ldb = rowB ? N[i] : K[i], ldc = rowA ? N[i] : M[i];
+        std::vector<Problem> set_probs(sets);
+        for (int r = 0; r < sets; ++r) {
+            mgemm_status_t st = make_problem(h, layoutA, layoutB, M[i], N[i], K[i], 1.0f,
+                                             (char*)buf.a + a_bytes * r, lda, (char*)buf.b + b_bytes * r,
+                                             ldb, 0.0f, buf.c, ldc, dtype, &set_probs[r]);
+            if (st != MGEMM_SUCCESS) return st;
+        }
         Problem& p = probs[i];
-        mgemm_status_t st = make_problem(h, layoutA, layoutB, M[i], N[i], K[i], 1.0f, buf.a, lda,
-                                         buf.b, ldb, 0.0f, buf.c, ldc, dtype, &p);
-        if (st != MGEMM_SUCCESS) return st;
+        p = set_probs[0];
         // Each (kernel, ranges actually used) is timed once per shape.
         std::map<std::pair<int, int>, double> seen;
         auto measure = [&](Choice c) {
             auto key = std::make_pair((int)c.k, c.ksplit);
             auto it = seen.find(key);
             if (it != seen.end()) return it->second;
-            const double t = time_choice(h, p, c, stream, ev.e0, ev.e1);
+            const double t = time_choice(h, set_probs, c, stream, ev.e0, ev.e1);
             seen[key] = t;
             return t;
         };

@@ -323,27 +323,42 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
                 *row = tot;
             }
         } else {
-            // More ranges: per row, rounds of SPC ranges in flight.
-            constexpr int SPC = 4;
-            for (int m = w; m < M; m += 4) {
-                f32x4* row = (f32x4*)(red + m * RED_LD + n);
-                const f32x4 mine = *row;
-                f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int sp0 = 0; sp0 < sa.ksplit; sp0 += SPC) {
-                    f32x4 v[SPC];
+            // More ranges: groups of RG rows, rounds of SPC ranges; the
+            // RG*SPC loads of a round are in flight together, and each row
+            // keeps its sum in range order.
+            constexpr int SPC = 4, RG = 4;
+            for (int m0r = w; m0r < M; m0r += 4 * RG) {
+                f32x4 mine[RG], tot[RG];
 #pragma unroll
-                    for (int c = 0; c < SPC; ++c) {
-                        const int sp = sp0 + c;
-                        v[c] = (sp < sa.ksplit && sp != split) ? load_coherent(ws, part_off(sp, m)) : mine;
-                    }
-#pragma unroll
-                    for (int c = 0; c < SPC; ++c) {
-                        const int sp = sp0 + c;
-                        if (sp == 0) tot = v[c];
-                        else if (sp < sa.ksplit) tot = tot + v[c];
-                    }
+                for (int g = 0; g < RG; ++g) {
+                    const int m = m0r + 4 * g;
+                    mine[g] = m < M ? *(const f32x4*)(red + m * RED_LD + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    tot[g] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                *row = tot;
+                for (int sp0 = 0; sp0 < sa.ksplit; sp0 += SPC) {
+                    f32x4 v[RG][SPC];
+#pragma unroll
+                    for (int g = 0; g < RG; ++g)
+#pragma unroll
+                        for (int c = 0; c < SPC; ++c) {
+                            const int m = m0r + 4 * g, sp = sp0 + c;
+                            v[g][c] = (m < M && sp < sa.ksplit && sp != split)
+                                          ? load_coherent(ws, part_off(sp, m)) : mine[g];
+                        }
+#pragma unroll
+                    for (int g = 0; g < RG; ++g)
+#pragma unroll
+                        for (int c = 0; c < SPC; ++c) {
+                            const int sp = sp0 + c;
+                            if (sp == 0) tot[g] = v[g][c];
+                            else if (sp < sa.ksplit) tot[g] = tot[g] + v[g][c];
+                        }
+                }
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const int m = m0r + 4 * g;
+                    if (m < M) *(f32x4*)(red + m * RED_LD + n) = tot[g];
+                }
             }
         }
     }
@@ -405,10 +420,12 @@ int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested) {
     int64_t ks;
     if (requested <= 0) {
         // About three workgroups for every four CUs (the copy-only
-        // measurements peak there), at most 16 ranges and never an empty one.
+        // measurements peak there), at most 16 ranges, each of at least 8
+        // steps (K = 256; shorter ranges spend more on the partial exchange
+        // than they save: 64x6144x1024 took 27 us at 8 ranges of 4 steps).
         ks = (3 * slots / 4 + blocks - 1) / blocks;
         if (ks > 16) ks = 16;
-        if (ks > nk) ks = nk;
+        if (ks > nk / 8) ks = nk / 8;
         if (ks < 1) ks = 1;
         if (ks > 1 && (!room || ks * per_range > ws.part_bytes)) ks = 1;
     } else {

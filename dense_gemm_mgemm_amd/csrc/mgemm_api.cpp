@@ -148,15 +148,27 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
             return {MGEMM_KERNEL_F32_FAST, 1};
         if (small) return {MGEMM_KERNEL_F32_FAST_128, 1};
         // NN operands that are not 16-byte aligned or a K that is not a
-        // multiple of the slice: the same kernel with narrower loads.
-        if (mgemm::f32_unaligned_supports(p)) return {MGEMM_KERNEL_F32_FAST_U, 1};
+        // multiple of the slice: the same kernel with narrower loads.  It has
+        // only 256x256 tiles; a grid of them that leaves more than half of the
+        // CUs idle runs faster on the 128x128 masked kernel (1000^3: 125 vs
+        // 260 us).
+        if (mgemm::f32_unaligned_supports(p)) {
+            const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+            if (tiles * 2 <= slots && mgemm::f32_mfma_supports(p)) return {MGEMM_KERNEL_F32_MFMA, 1};
+            return {MGEMM_KERNEL_F32_FAST_U, 1};
+        }
         return {MGEMM_KERNEL_F32_MFMA, 1};
     }
     // M <= 64 streams B once: 256-column blocks with K split over workgroups
     // read B in 512-byte row segments (about 5.1 TB/s in copy-only
     // measurements, against 4.2 TB/s for the 128-byte segments of the
     // whole-K kernel).
-    if (p.M <= 64 && mgemm::skinny_sk_supports(p))
+    // Short K is the exception: with few steps per range the exchange of
+    // partial rows costs more than the wider segments save, most of all for
+    // 64-row blocks (BF16, K = 2048, M = 64: 17.4 us whole-K against 19.1 us
+    // at the best split; K = 1024: 9.4 against 15.7).
+    const bool short_k = p.K <= 1024 || (p.M > 32 && p.K <= 2048);
+    if (p.M <= 64 && mgemm::skinny_sk_supports(p) && !(short_k && mgemm::skinny_supports(p)))
         return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
     if (p.M <= 64 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
     // 16-bit: the variant (and split of K) with the smallest predicted time.

@@ -120,3 +120,23 @@ def test_tune_argument_errors(h):
                 st = mg.load().mgemm_tune(h, 2, 0, 0, 0, None, None, None, None, None, None)
                 raise mg.MgemmError(st, "mgemm_tune")
         assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG
+
+
+def test_tune_other_dtypes_and_layouts(h):
+    # FP32 (aligned and ragged), column-major FP16 and skinny BF16 shapes: the
+    # tuner measures whatever can run each one, the table steers mgemm_run,
+    # and the results stay exact on integer data.
+    cases = [("f32", "row", "row", [(1000, 1000, 1000), (512, 512, 2048)]),
+             ("f16", "col", "col", [(512, 1024, 2048)]),
+             ("bf16", "row", "row", [(16, 12288, 4096), (64, 6144, 1024)])]
+    for dtype, la, lb, shapes in cases:
+        res = mg.mgemm_tune(h, dtype, la, lb, shapes)
+        for r in res:
+            say("tuned", dtype, la, lb, r)
+            assert r["chosen_us"] > 0 and r["chosen_us"] <= r["model_us"] * 1.10, r
+        for (M, N, K) in shapes:
+            case = W.Case("tuned_int", M, N, K, dtype, layoutA=la, layoutB=lb, kindA="int",
+                          kindB="int", seeds=(M, N, K))
+            P.check_bit_exact(case, *P.run_gpu(h, case))
+    text = mg.mgemm_table_export(h)
+    assert "exact f32" in text and "exact f16" in text and "exact bf16" in text
