@@ -100,6 +100,30 @@ def is_hbm_bound(case) -> bool:
     return case.dtype != "f32" and case.M <= 64
 
 
+_SLEEP_CYCLES_PER_S = None
+
+
+def hold_stream(stream, seconds):
+    """Keep `stream` busy for about `seconds` (at most 50 ms) with torch's
+    bounded spin kernel, so that launches enqueued behind it reach the GPU
+    back to back instead of at the host's enqueue pace.  The spin's rate is
+    measured once."""
+    import torch
+    global _SLEEP_CYCLES_PER_S
+    if not hasattr(torch.cuda, "_sleep"):
+        return
+    with torch.cuda.stream(stream):
+        if _SLEEP_CYCLES_PER_S is None:
+            torch.cuda._sleep(100_000)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.cuda._sleep(2_000_000)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            _SLEEP_CYCLES_PER_S = 2_000_000 / max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+        torch.cuda._sleep(int(min(seconds, 0.05) * _SLEEP_CYCLES_PER_S))
+
+
 def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
     """Time `steps` launches after `warmup` untimed ones (continued until
     `warm_s` seconds have passed, so short kernels run at a settled clock);
@@ -172,21 +196,39 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Host time to enqueue one step, from 16 steps.
     torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    for i in range(16):
+        launch(i)
+    host_s = (time.perf_counter() - t_host) / 16
+    torch.cuda.synchronize()
+    # The timed region: `steps` launches back to back between two events.  A
+    # kernel shorter than the host's enqueue time would otherwise be timed
+    # with the GPU waiting for the host between steps, so the stream is held
+    # until all of them are enqueued.  Average launch duration = region / steps.
+    hold_stream(stream, 1.25 * host_s * steps + 1e-4)
     wall0 = time.perf_counter()
     t_all0.record(stream)
+    for i in range(steps):
+        launch(i)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_all0.elapsed_time(t_all1)
+    # Spread of single launches, from a second pass with an event pair around
+    # each (each pair adds a few microseconds of its own).
+    hold_stream(stream, 1.5 * host_s * steps + 1e-4)
     for i in range(steps):
         ev[i][0].record(stream)
         launch(i)
         ev[i][1].record(stream)
-    t_all1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     per = sorted(a.elapsed_time(b) for a, b in ev)
-    total_ms = t_all0.elapsed_time(t_all1)
     return {
         "kernel": kname, "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
-        "launch_ms_mean": sum(per) / len(per), "launch_ms_median": per[len(per) // 2],
+        "host_ms_per_step": host_s * 1e3, "launch_ms_mean": total_ms / steps,
+        "launch_ms_single_median": per[len(per) // 2],
         "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
         "inputs": (A, B, C0), "out": dC[(steps - 1) % len(dC)],
     }
@@ -219,6 +261,11 @@ def measure_mix(h, steps=20):
             group(hh)
             torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        group(hh)
+        host_s = time.perf_counter() - t1
+        torch.cuda.synchronize()
+        hold_stream(stream, 1.25 * host_s * steps + 1e-4)
         e0.record(stream)
         for _ in range(steps):
             group(hh)
@@ -432,8 +479,8 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_per_launch": flops if not hbm else nbytes,
                      "launch_ms_mean": round(r["launch_ms_mean"], 5),
-                     "launch_ms_p10": round(r["launch_ms_p10"], 5),
-                     "launch_ms_p90": round(r["launch_ms_p90"], 5)},
+                     "single_launch_ms_p10": round(r["launch_ms_p10"], 5),
+                     "single_launch_ms_p90": round(r["launch_ms_p90"], 5)},
         "cpu_baseline": None,
         "src_hash": src_hash(),
     }
