@@ -44,6 +44,24 @@ struct Workspace {
     int64_t ncounters;
 };
 
+// Exchange of FP32 partial results between workgroups of one launch (split
+// K and stream-K).  Device-coherent 16-byte store and load: buffer accesses
+// with the device-scope cache policy (sc1), so the store writes through this
+// XCD's L2 and the load does not hit a stale line there.  A partial written on
+// one XCD and counted with a device-scope atomic is thus read correctly on
+// another, with no whole-L2 write-back or invalidation.  The compiler sees
+// both (it resolves the store's register hazards and keeps many loads in
+// flight); offsets past the buffer's size read as zero and drop stores.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int CPOL_DEVICE = 16;   // sc1
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws, off, 0, CPOL_DEVICE);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, off, 0, CPOL_DEVICE));
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup -> output tile.
 //
@@ -259,6 +277,10 @@ hipError_t launch_f32_fast(const Problem& p, bool big, hipStream_t s);
 bool f32_fast_supports(const Problem& p, bool big);
 bool f32_unaligned_supports(const Problem& p);
 hipError_t launch_f32_unaligned(const Problem& p, hipStream_t s);
+// Stream-K form of the f32_fast_u kernel (same support); it needs two partial
+// tiles per CU and one counter per tile in the workspace.
+bool f32_sk_fits(const Problem& p, const Workspace& ws);
+hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s);
 hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s);
 bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);

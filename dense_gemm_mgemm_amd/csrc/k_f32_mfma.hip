@@ -212,8 +212,24 @@ __device__ __forceinline__ void set_lane(typename VecT<V>::T& v, int e, float x)
     else v[e] = x;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int OCC, int VA, int VB, bool TAIL>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
+// Stream-K form (SK): the grid has one workgroup per CU, and the T = tiles * nk
+// (tile, K slice) pairs, tile-major in the M-grouped tile order, are dealt out
+// in equal contiguous shares: workgroup g takes pairs [g*T/G, (g+1)*T/G).  A
+// share covers the end of one tile, whole tiles and the start of another; a
+// whole tile is stored as usual.  Each piece of a split tile is published as
+// an FP32 partial in the workspace, the contributors count their arrivals on
+// the tile's counter, and the last to arrive sums the pieces in K order
+// (contributor order) and stores C.  No workgroup ever waits for another.
+// Shares are numbered XCD-major (the workgroups on one XCD take consecutive
+// shares, hence neighbouring tiles that share A and B panels in its L2).
+struct SKArgs {
+    float* part;        // [G][2] partial tiles of BM*BN floats in register order
+    int part_bytes;     // bytes of `part` (bounds the buffer accesses)
+    unsigned* cnt;      // [tiles] arrival counters, zero between calls
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int OCC, int VA, int VB, bool TAIL, bool SK>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArgs sk) {
     typedef typename VecT<VA>::T TA;
     typedef typename VecT<VB>::T TB;
     constexpr int NT = 64 * WM * WN;
@@ -228,18 +244,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
 
     __shared__ __align__(16) float As[2][BM * AROW];
     __shared__ __align__(16) float Bs[2][BK * BROW];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    __shared__ int last_arrival;
 
     const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-    int tmi, tni;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
-    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
-    const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
-    const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    const int64_t nfull = p.K / BK, nk = (p.K + BK - 1) / BK;
 
     const float* __restrict__ A = (const float*)p.A;
     const float* __restrict__ B = (const float*)p.B;
@@ -250,146 +258,248 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p) {
     constexpr int AK = BK / VA, A_RS = NT / AK;
     constexpr int BNV = BN / VB, B_RS = NT / BNV;
     static_assert(NT % AK == 0 && NT % BNV == 0, "loads must tile the slice");
-    const int a_mi0 = tid / AK, a_kc = (tid % AK) * VA;
-    const int b_ki0 = tid / BNV, b_nc = (tid % BNV) * VB;
-    const int b_nn = b_nc + VB <= nlim ? b_nc : nlim - VB;
-    const float* a_base = A + m0 * p.lda + a_kc;
-    const float* b_base = B + (int64_t)b_ki0 * p.ldb + n0 + b_nn;
-    auto a_ptr = [&](int r) {
-        const int mi = a_mi0 + r * A_RS;
-        return a_base + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda;
-    };
-    auto b_ptr = [&](int r) { return b_base + (int64_t)(r * B_RS) * p.ldb; };
-
-    TA ra[LA];
-    TB rb[LB];
-    // With 16-byte loads on both operands the per-load pointers are computed
-    // once (they fit in the registers of a 16-wave workgroup and save the
-    // address arithmetic in the loop); with narrower loads there are too
-    // many, and the slice bases pass through an empty asm so that the
-    // compiler forms each load address here instead of keeping LA + LB
-    // loop-invariant 64-bit pointers live across the K loop.
-    constexpr bool WIDE = VA == 4 && VB == 4;
-    const float* a_src[WIDE ? LA : 1];
-    const float* b_src[WIDE ? LB : 1];
-    if constexpr (WIDE) {
-#pragma unroll
-        for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
-#pragma unroll
-        for (int r = 0; r < LB; ++r) b_src[r] = b_ptr(r);
-    }
-    auto fetch = [&](int64_t kt) {
-        if constexpr (WIDE) {
-#pragma unroll
-            for (int r = 0; r < LA; ++r) ra[r] = *(const TA*)(a_src[r] + kt * BK);
-#pragma unroll
-            for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(b_src[r] + kt * BK * p.ldb);
-        } else {
-            const float* ab = a_base + kt * BK;
-            const float* bb = b_base + kt * BK * p.ldb;
-            asm volatile("" : "+v"(ab), "+v"(bb));
-#pragma unroll
-            for (int r = 0; r < LA; ++r) {
-                const int mi = a_mi0 + r * A_RS;
-                ra[r] = *(const TA*)(ab + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda);
-            }
-#pragma unroll
-            for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(bb + (int64_t)(r * B_RS) * p.ldb);
-        }
-    };
-    // The partial last slice: element by element, zero where k >= K (the
-    // address is clamped to k = K-1 so that nothing past the operands is read).
-    auto fetch_tail = [&](int64_t kt) {
-        const int64_t kb = kt * BK;
-#pragma unroll
-        for (int r = 0; r < LA; ++r)
-#pragma unroll
-            for (int e = 0; e < VA; ++e) {
-                const int64_t k = kb + a_kc + e;
-                const float x = a_ptr(r)[(k < p.K ? k : p.K - 1) - a_kc];
-                set_lane<VA>(ra[r], e, k < p.K ? x : 0.f);
-            }
-#pragma unroll
-        for (int r = 0; r < LB; ++r) {
-            const int64_t k = kb + b_ki0 + r * B_RS;
-            const float* row = b_base + ((k < p.K ? k : p.K - 1) - b_ki0) * p.ldb;
-#pragma unroll
-            for (int e = 0; e < VB; ++e) set_lane<VB>(rb[r], e, k < p.K ? row[e] : 0.f);
-        }
-    };
-    auto stash = [&](int slot) {
-#pragma unroll
-        for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
-#pragma unroll
-        for (int r = 0; r < LB; ++r) *(TB*)(&Bs[slot][(b_ki0 + r * B_RS) * BROW + b_nc]) = rb[r];
-    };
 
     f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
-    const int64_t nfull = p.K / BK, nk = (p.K + BK - 1) / BK;
-    auto load = [&](int64_t kt) {
-        if constexpr (TAIL) {
-            if (kt < nfull) fetch(kt);
-            else fetch_tail(kt);
-        } else {
-            fetch(kt);          // K % BK == 0 (host-checked)
-        }
+    // Thread-chunk c of the accumulators: 4 consecutive values of one MFMA
+    // block (the unit of the partial exchange).
+    constexpr int NCH = TM * TN * 4;
+    auto chunk = [&](int c) -> f32x4 {
+        const f32x16& v = acc[c / (TN * 4)][(c / 4) % TN];
+        const int e = 4 * (c % 4);
+        return f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
     };
-    const int lrow = lane >> 5, lcol = lane & 31;
-    load(0);
-    stash(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) load(kt + 1);
-        const float* as = &As[cur][(wm * WTM + lcol) * AROW + lrow * HALF];
-        const float* bs = &Bs[cur][(lrow * HALF) * BROW + wn * WTN + lcol];
-#pragma unroll
-        for (int s0 = 0; s0 < HALF; s0 += 4) {
-            f32x4v a4[TM];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) a4[i] = *(const f32x4v*)(as + i * 32 * AROW + s0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                float b[TN];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) b[j] = bs[(s0 + s) * BROW + j * 32];
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[i][s], b[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        if (kt + 1 < nk) stash(cur ^ 1);
-        __syncthreads();
-    }
+    auto set_chunk = [&](int c, f32x4 x) {
+        f32x16& v = acc[c / (TN * 4)][(c / 4) % TN];
+        const int e = 4 * (c % 4);
+        v[e] = x[0]; v[e + 1] = x[1]; v[e + 2] = x[2]; v[e + 3] = x[3];
+    };
 
-    float* C = (float*)p.C;
-    with_epilogue(p.epilogue, [&](auto E) {
-        constexpr int EPI = decltype(E)::value;
+    // Slices [k0, k1) of tile (tmi, tni) into acc; if they are all of K, the
+    // epilogue stores C, otherwise (stream-K only) the piece is exchanged.
+    // Everything derived from the thread id is formed here, from `tid` as
+    // passed in: the stream-K loop passes it through an empty asm on every
+    // tile, so that these values are not hoisted out of that loop and kept
+    // live (with the accumulators) across it.
+    auto tile_pass = [&](int tid, int tmi, int tni, int64_t k0, int64_t k1, int64_t t, int64_t g,
+                         int64_t T, int64_t G) {
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        const int a_mi0 = tid / AK, a_kc = (tid % AK) * VA;
+        const int b_ki0 = tid / BNV, b_nc = (tid % BNV) * VB;
+        const int lrow = lane >> 5, lcol = lane & 31;
+        const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+        const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+        const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+        const int b_nn = b_nc + VB <= nlim ? b_nc : nlim - VB;
+        const float* a_base = A + m0 * p.lda + a_kc;
+        const float* b_base = B + (int64_t)b_ki0 * p.ldb + n0 + b_nn;
+        auto a_ptr = [&](int r) {
+            const int mi = a_mi0 + r * A_RS;
+            return a_base + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda;
+        };
+        auto b_ptr = [&](int r) { return b_base + (int64_t)(r * B_RS) * p.ldb; };
+
+        TA ra[LA];
+        TB rb[LB];
+        // With 16-byte loads on both operands the per-load pointers are
+        // computed once (they fit in the registers of a 16-wave workgroup and
+        // save the address arithmetic in the loop); with narrower loads there
+        // are too many, and the slice bases pass through an empty asm so that
+        // the compiler forms each load address here instead of keeping LA + LB
+        // loop-invariant 64-bit pointers live across the K loop.
+        constexpr bool WIDE = VA == 4 && VB == 4;
+        const float* a_src[WIDE ? LA : 1];
+        const float* b_src[WIDE ? LB : 1];
+        if constexpr (WIDE) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int ni = wn * WTN + j * 32 + lcol;
+            for (int r = 0; r < LB; ++r) b_src[r] = b_ptr(r);
+        }
+        auto fetch = [&](int64_t kt) {
+            if constexpr (WIDE) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int mi = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
-                    if (mi < mlim && ni < nlim) {
-                        const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
-                        float v = p.alpha * acc[i][j][r];
-                        if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
-                        C[idx] = epilogue_op<F32, EPI>(v);
+                for (int r = 0; r < LA; ++r) ra[r] = *(const TA*)(a_src[r] + kt * BK);
+#pragma unroll
+                for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(b_src[r] + kt * BK * p.ldb);
+            } else {
+                const float* ab = a_base + kt * BK;
+                const float* bb = b_base + kt * BK * p.ldb;
+                asm volatile("" : "+v"(ab), "+v"(bb));
+#pragma unroll
+                for (int r = 0; r < LA; ++r) {
+                    const int mi = a_mi0 + r * A_RS;
+                    ra[r] = *(const TA*)(ab + (int64_t)(mi < mlim ? mi : mlim - 1) * p.lda);
+                }
+#pragma unroll
+                for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(bb + (int64_t)(r * B_RS) * p.ldb);
+            }
+        };
+        // The partial last slice: element by element, zero where k >= K (the
+        // address is clamped to k = K-1 so that nothing past the operands is read).
+        auto fetch_tail = [&](int64_t kt) {
+            const int64_t kb = kt * BK;
+#pragma unroll
+            for (int r = 0; r < LA; ++r)
+#pragma unroll
+                for (int e = 0; e < VA; ++e) {
+                    const int64_t k = kb + a_kc + e;
+                    const float x = a_ptr(r)[(k < p.K ? k : p.K - 1) - a_kc];
+                    set_lane<VA>(ra[r], e, k < p.K ? x : 0.f);
+                }
+#pragma unroll
+            for (int r = 0; r < LB; ++r) {
+                const int64_t k = kb + b_ki0 + r * B_RS;
+                const float* row = b_base + ((k < p.K ? k : p.K - 1) - b_ki0) * p.ldb;
+#pragma unroll
+                for (int e = 0; e < VB; ++e) set_lane<VB>(rb[r], e, k < p.K ? row[e] : 0.f);
+            }
+        };
+        auto stash = [&](int slot) {
+#pragma unroll
+            for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
+#pragma unroll
+            for (int r = 0; r < LB; ++r) *(TB*)(&Bs[slot][(b_ki0 + r * B_RS) * BROW + b_nc]) = rb[r];
+        };
+        auto load = [&](int64_t kt) {
+            if constexpr (TAIL) {
+                if (kt < nfull) fetch(kt);
+                else fetch_tail(kt);
+            } else {
+                fetch(kt);          // K % BK == 0 (host-checked)
+            }
+        };
+
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+        load(k0);
+        stash(0);
+        __syncthreads();
+        for (int64_t kt = k0; kt < k1; ++kt) {
+            const int cur = (int)((kt - k0) & 1);
+            if (kt + 1 < k1) load(kt + 1);
+            const float* as = &As[cur][(wm * WTM + lcol) * AROW + lrow * HALF];
+            const float* bs = &Bs[cur][(lrow * HALF) * BROW + wn * WTN + lcol];
+#pragma unroll
+            for (int s0 = 0; s0 < HALF; s0 += 4) {
+                f32x4v a4[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) a4[i] = *(const f32x4v*)(as + i * 32 * AROW + s0);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float b[TN];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) b[j] = bs[(s0 + s) * BROW + j * 32];
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[i][s], b[j], acc[i][j], 0, 0, 0);
+                }
+            }
+            if (kt + 1 < k1) stash(cur ^ 1);
+            __syncthreads();
+        }
+
+        if constexpr (SK) {
+            if (k0 != 0 || k1 != nk) {
+                // Owner of pair x: the largest g with g*T/G <= x.
+                auto owner = [&](int64_t x) { return ((x + 1) * G - 1) / T; };
+                const int64_t first = owner(t * nk), last = owner((t + 1) * nk - 1);
+                const int nc = (int)(last - first + 1);
+                // A contributor's piece is the end of its share (slot 1) if its
+                // share began before this tile, else the start (slot 0).
+                auto slot_base = [&](int64_t gg) {
+                    const int64_t sl = gg * T / G < t * nk ? 1 : 0;
+                    return (unsigned)((gg * 2 + sl) * (int64_t)(BM * BN * 4));
+                };
+                const __amdgpu_buffer_rsrc_t ws =
+                    __builtin_amdgcn_make_buffer_rsrc(sk.part, 0, sk.part_bytes, 0x00020000);
+                const unsigned mine = slot_base(g) + (unsigned)tid * 16u;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) store_coherent(ws, mine + (unsigned)(c * NT * 16), chunk(c));
+                __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): stores done
+                __syncthreads();
+                if (tid == 0) {
+                    const unsigned old = __hip_atomic_fetch_add(sk.cnt + t, 1u, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT);
+                    last_arrival = old == (unsigned)(nc - 1);
+                }
+                __syncthreads();
+                if (!last_arrival) return;
+                if (tid == 0) sk.cnt[t] = 0u;
+                // Sum the pieces in contributor (= K) order, all of them
+                // (this one's too) read back from the workspace, GRP chunks per
+                // round with their loads in flight.
+                constexpr int GRP = 8;
+#pragma unroll
+                for (int c0 = 0; c0 < NCH; c0 += GRP) {
+                    f32x4 tot[GRP];
+                    const unsigned b0 = slot_base(first) + (unsigned)tid * 16u;
+#pragma unroll
+                    for (int q = 0; q < GRP; ++q) tot[q] = load_coherent(ws, b0 + (unsigned)((c0 + q) * NT * 16));
+                    for (int cc = 1; cc < nc; ++cc) {
+                        const unsigned base = slot_base(first + cc) + (unsigned)tid * 16u;
+                        f32x4 v[GRP];
+#pragma unroll
+                        for (int q = 0; q < GRP; ++q) v[q] = load_coherent(ws, base + (unsigned)((c0 + q) * NT * 16));
+#pragma unroll
+                        for (int q = 0; q < GRP; ++q) tot[q] = tot[q] + v[q];
                     }
+#pragma unroll
+                    for (int q = 0; q < GRP; ++q) set_chunk(c0 + q, tot[q]);
                 }
             }
         }
-    });
+
+        float* C = (float*)p.C;
+        with_epilogue(p.epilogue, [&](auto E) {
+            constexpr int EPI = decltype(E)::value;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int ni = wn * WTN + j * 32 + lcol;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int mi = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lrow + (r & 3);
+                        if (mi < mlim && ni < nlim) {
+                            const int64_t idx = (m0 + mi) * p.ldc + n0 + ni;
+                            float v = p.alpha * acc[i][j][r];
+                            if (p.beta != 0.f) v = fmaf(p.beta, C[idx], v);
+                            C[idx] = epilogue_op<F32, EPI>(v);
+                        }
+                    }
+                }
+            }
+        });
+    };
+
+    if constexpr (!SK) {
+        int tmi, tni;
+        tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tmi, tni);
+        tile_pass((int)threadIdx.x, tmi, tni, 0, nk, 0, 0, 1, 1);
+    } else {
+        const int64_t G = gridDim.x;
+        const int64_t T = (int64_t)tiles_m * tiles_n * nk;
+        const int64_t g = xcd_linear(blockIdx.x, (int)G);
+        int64_t it = g * T / G;
+        const int64_t end = (g + 1) * T / G;
+        while (it < end) {
+            const int64_t t = it / nk, k0 = it - t * nk;
+            const int64_t k1 = nk - k0 < end - it ? nk : k0 + (end - it);
+            int tmi, tni;
+            tile_from_linear((int)t, tiles_m, tiles_n, 8, tmi, tni);
+            int tid = (int)threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            tile_pass(tid, tmi, tni, k0, k1, t, g, T, G);
+            it += k1 - k0;
+        }
+    }
 }
 
 // Tile shapes: 256x256x32 on 16 waves (one workgroup per CU) for aligned
@@ -413,9 +523,31 @@ bool fast_supports(const Problem& p) {
 template <class CF, int VA, int VB, bool TAIL>
 hipError_t fast_launch(const Problem& p, hipStream_t s) {
     const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
-    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL>),
-                       dim3((unsigned)tiles), dim3(64 * CF::WM * CF::WN), 0, s, p);
+    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL, false>),
+                       dim3((unsigned)tiles), dim3(64 * CF::WM * CF::WN), 0, s, p, SKArgs{});
     return hipGetLastError();
+}
+// Stream-K: one workgroup per CU (the 256x256 tiles hold one per CU).
+template <class CF, int VA, int VB, bool TAIL>
+hipError_t sk_launch(const Problem& p, const Workspace& ws, hipStream_t s) {
+    // At most one workgroup per (tile, slice) pair, so that every share is
+    // non-empty and the contributors to a tile are consecutive workgroups.
+    const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
+    const int64_t pairs = tiles * ((p.K + CF::BK - 1) / CF::BK);
+    const int64_t cus = p.num_cu > 0 ? p.num_cu : 256;
+    const int G = (int)(pairs < cus ? pairs : cus);
+    SKArgs a{(float*)ws.part, (int)(ws.part_bytes < 0x7fffffff ? ws.part_bytes : 0x7fffffff),
+             ws.counters};
+    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL, true>),
+                       dim3((unsigned)G), dim3(64 * CF::WM * CF::WN), 0, s, p, a);
+    return hipGetLastError();
+}
+template <class CF>
+bool sk_fits(const Problem& p, const Workspace& ws) {
+    const int64_t G = p.num_cu > 0 ? p.num_cu : 256;
+    const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
+    return ws.part != nullptr && ws.counters != nullptr && tiles <= ws.ncounters &&
+           G * 2 * CF::BM * CF::BN * (int64_t)sizeof(float) <= ws.part_bytes;
 }
 
 // Widest loads the operands allow: A loads of 4 floats need 16-byte aligned
@@ -461,6 +593,20 @@ hipError_t launch_f32_unaligned(const Problem& p, hipStream_t s) {
     }
     if (vb == 4) return fast_launch<U, 1, 4, true>(p, s);
     return fast_launch<U, 1, 2, true>(p, s);           // (1, 1) is declined by the supports check
+}
+
+bool f32_sk_fits(const Problem& p, const Workspace& ws) { return sk_fits<UnalignedCfg>(p, ws); }
+
+hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
+    const int va = unaligned_va(p), vb = unaligned_vb(p);
+    using U = UnalignedCfg;
+    if (va == 4) {
+        if (vb == 4) return sk_launch<U, 4, 4, true>(p, ws, s);
+        if (vb == 2) return sk_launch<U, 4, 2, true>(p, ws, s);
+        return sk_launch<U, 4, 1, true>(p, ws, s);
+    }
+    if (vb == 4) return sk_launch<U, 1, 4, true>(p, ws, s);
+    return sk_launch<U, 1, 2, true>(p, ws, s);
 }
 
 }  // namespace mgemm

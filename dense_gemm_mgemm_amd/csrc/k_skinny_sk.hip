@@ -48,7 +48,6 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -85,21 +84,6 @@ __device__ __forceinline__ void wait_steps(int n) {
         if (n >= K) wait_vm<K * L>();
         else wait_steps<L, K - 1>(n);
     }
-}
-// Device-coherent 16-byte store and load of the partial blocks: buffer
-// accesses with the device-scope cache policy (sc1), so the store writes
-// through this XCD's L2 and the load does not hit a stale line there.  A
-// partial written on one XCD and counted with a device-scope atomic is thus
-// read correctly on another, with no whole-L2 write-back or invalidation.
-// The compiler sees both (it resolves the store's register hazards and keeps
-// many loads in flight); offsets past the workspace read as zero.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int CPOL_DEVICE = 16;   // sc1
-__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off, f32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws, off, 0, CPOL_DEVICE);
-}
-__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t ws, unsigned off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, off, 0, CPOL_DEVICE));
 }
 __device__ __forceinline__ void fence_sched() {
     __builtin_amdgcn_sched_barrier(0);

@@ -72,7 +72,9 @@ typedef enum {
     MGEMM_KERNEL_F8_MFMA = 14,   /* FP8 codes (mgemm_run_fp8 only): 256x256 tiles, f8f6f4 MFMA */
     MGEMM_KERNEL_F8_GENERAL = 15, /* FP8 codes (mgemm_run_fp8 only): any K/alignment, VALU */
     MGEMM_KERNEL_F8_MFMA_192 = 16, /* FP8 codes (mgemm_run_fp8 only): 256x192 tiles, f8f6f4 MFMA */
-    MGEMM_KERNEL_COUNT = 17
+    MGEMM_KERNEL_F32_SK = 17,    /* FP32 NN as F32_FAST_U, stream-K: one workgroup per CU, equal
+                                    shares of all (tile, K slice) pairs, deterministic fix-up */
+    MGEMM_KERNEL_COUNT = 18
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */

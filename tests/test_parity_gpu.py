@@ -156,7 +156,7 @@ def test_f32_unaligned_bit_exact(h, M, N, K, lda, ldb, ldc):
     case = W.Case("f32u", M, N, K, "f32", lda=lda, ldb=ldb, ldc=ldc, alpha=1.0, beta=-0.5,
                   kindA="int", kindB="int", kindC="int", seeds=(M, N, K))
     inputs = case.make()
-    for k in ("auto", "f32_fast_u"):
+    for k in ("auto", "f32_fast_u", "f32_sk"):
         out = supported(h, case, k, inputs)
         if out is None:
             assert k != "auto"
@@ -165,7 +165,25 @@ def test_f32_unaligned_bit_exact(h, M, N, K, lda, ldb, ldc):
         P.check_bit_exact(case, *out)
 
 
-@pytest.mark.parametrize("kernel", ["f32_fast_u", "f32_mfma"])
+# Stream-K FP32 (one workgroup per CU, equal shares of the (tile, K slice)
+# pairs): shares that cut tiles into two or three pieces, a single tile whose
+# 157 slices are each a piece of their own, unaligned operands and K tails;
+# integer data with beta != 0, so every piece order must give the oracle's
+# bits.  (M, N, K, lda, ldb, ldc)
+STREAM_K_F32 = [(1000, 6000, 700, 701, 6002, 6000), (512, 4096, 1024, 1024, 4096, 4096),
+                (200, 200, 5000, 5001, 202, 200), (300, 514, 100, 101, 514, 514),
+                (2048, 2304, 96, 96, 2304, 2304)]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", STREAM_K_F32)
+def test_f32_stream_k_bit_exact(h, M, N, K, lda, ldb, ldc):
+    case = W.Case("f32sk", M, N, K, "f32", lda=lda, ldb=ldb, ldc=ldc, alpha=1.0, beta=-0.5,
+                  kindA="int", kindB="int", kindC="int", seeds=(M + 1, N, K))
+    say("f32 stream-K", (M, N, K, lda, ldb, ldc))
+    P.check_bit_exact(case, *P.run_gpu(h, case, "f32_sk"))
+
+
+@pytest.mark.parametrize("kernel", ["f32_fast_u", "f32_mfma", "f32_sk"])
 def test_ragged_f32_forced(h, kernel):
     case = W.ragged_f32()
     say("ragged_f32", kernel)
@@ -491,6 +509,12 @@ def test_invalid_arguments_leave_c_untouched(h):
 
 
 def test_deterministic_run_to_run(h):
+    # Stream-K: the pieces of a tile are summed in K order whoever arrives last.
+    case = W.Case("det_sk", 1000, 3000, 2000, "f32", lda=2001, seeds=(5, 6, 7))
+    inputs = case.make()
+    outs = [W.storage_view(P.run_gpu(h, case, "f32_sk", inputs=inputs)[4]) for _ in range(3)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0]), case.name
     for case in (W.Case("det32", 1000, 1200, 777, "f32", seeds=(5, 6, 7)),
                  W.Case("det16", 1024, 1280, 1000, "bf16", kindA="normal", kindB="normal",
                         seeds=(5, 6, 7)),
@@ -543,7 +567,7 @@ def test_dispatch_choices(h):
                                       case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
                                       case.ldc, case.dtype)
     assert sel(W.sgemm_4096()) == "f32_fast"
-    assert sel(W.ragged_f32()) == "f32_fast_u"
+    assert sel(W.ragged_f32()) == "f32_sk"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x192"
     assert all(sel(W.ffn_bf16(m)) == "skinny_sk" for m in W.SKINNY_M)
