@@ -100,8 +100,8 @@ typedef struct mgemm_variant {
  * the device cannot be queried or its workspace cannot be allocated,
  * MGEMM_ERR_INVALID_ARG if out is NULL.
  * The handle owns a device workspace (128 MiB of FP32 partial results plus
- * 64 Ki arrival counters, allocated and zeroed here) that the split-K forms
- * use: calls that run at the same time on different streams must use
+ * 64 Ki arrival counters, allocated and zeroed here) that the split-K and
+ * stream-K forms use: calls that run at the same time on different streams must use
  * different handles; calls on one stream (or otherwise ordered) may share one.
  * The counters return to zero at the end of every call that uses them.
  */
@@ -144,7 +144,11 @@ mgemm_status_t mgemm_run(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_
 /*
  * mgemm_run_kernel -- as mgemm_run, but force one kernel variant.
  * Returns MGEMM_ERR_UNSUPPORTED (nothing enqueued) when that variant cannot
- * run this problem (wrong dtype, alignment or shape class).  Used to check
+ * run this problem (wrong dtype, alignment or shape class; for
+ * MGEMM_KERNEL_F32_SK also more than 64 Ki tiles or a device with more than
+ * 256 CUs, whose two 256 KiB partial tiles per CU exceed the workspace).
+ * MGEMM_KERNEL_F32_SK sums the pieces of a split tile in K order, so its
+ * results are the same on every run of one problem on one device.  Used to check
  * every dispatch branch against the same reference, so that no branch goes
  * untested (the lesson of the MTT S4000 GEMM write-up, section 8).
  */
