@@ -56,25 +56,26 @@ def replay_matches_eager(call, out, replays=3):
 
 
 GEMM_CASES = [
-    # (case, expected variant) -- FP32 stream-K, the 16-bit two-launch split,
-    # the skinny last-arrival split.
-    (W.Case("graph_sk", 1000, 3000, 2000, "f32", lda=2001, seeds=(21, 22, 23)), ("f32_sk", 1)),
-    (W.ffn_share_bf16(), ("h_dma_256x192", 5)),
+    # (case, kernel, K ranges) -- FP32 stream-K, the 16-bit two-launch split,
+    # the skinny last-arrival split, and the library's own choice for the FFN.
+    (W.Case("graph_sk", 1000, 3000, 2000, "f32", lda=2001, seeds=(21, 22, 23)), "f32_sk", 1),
+    (W.ffn_share_bf16(), "h_dma_256x192", 5),
     (W.Case("graph_skinny", 16, 12288, 4096, "bf16", kindA="normal", kindB="normal",
-            seeds=(24, 25, 26)), ("skinny_sk", 4)),
+            seeds=(24, 25, 26)), "skinny_sk", 4),
+    (W.ffn_bf16(), "auto", 0),
 ]
 
 
-@pytest.mark.parametrize("case,variant", GEMM_CASES, ids=[c.name for c, _ in GEMM_CASES])
-def test_gemm_graph_replay(h, case, variant):
+@pytest.mark.parametrize("case,kernel,ksplit", GEMM_CASES,
+                         ids=["%s-%s" % (c.name, k) for c, k, _ in GEMM_CASES])
+def test_gemm_graph_replay(h, case, kernel, ksplit):
     A, B, C0 = case.make()
     dA, dB = A.cuda(), B.cuda()
     dC = P.c_initial(case, None).cuda()
     args = (case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, dA, case.lda, dB,
             case.ldb, 0.0, dC, case.ldc, case.dtype)
-    assert mg.mgemm_select_variant(h, *args) == variant
-    say("graph", case.name, variant)
-    ref = replay_matches_eager(lambda: mg.mgemm_run(h, *args), dC)
+    say("graph", case.name, kernel, ksplit)
+    ref = replay_matches_eager(lambda: mg.mgemm_run_variant(h, kernel, ksplit, *args), dC)
     # The eager result itself agrees with the oracle on sampled rows.
     Cin = P.c_initial(case, None)
     P.check_tolerance(case, A, B, None, Cin, ref.cpu(), rows=P.sample_rows(case.M, 64),
@@ -87,8 +88,9 @@ def test_gated_split_graph_replay(h):
     dX, dWg, dWu = X.cuda(), Wg.cuda(), Wu.cuda()
     dZ = P.c_initial(case, None).cuda()
     say("graph gated", case.name)
-    replay_matches_eager(lambda: mg.mgemm_run_gated(h, case.M, case.N, case.K, dX, case.lda, dWg,
-                                                    dWu, case.ldb, dZ, case.ldc, case.dtype), dZ)
+    replay_matches_eager(lambda: mg.mgemm_run_gated_ex(h, 4, case.M, case.N, case.K, dX, case.lda,
+                                                       dWg, dWu, case.ldb, dZ, case.ldc,
+                                                       case.dtype), dZ)
 
 
 def test_fp8_step_graph_replay(h):
