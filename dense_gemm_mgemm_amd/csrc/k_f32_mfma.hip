@@ -228,7 +228,15 @@ struct SKArgs {
     unsigned* cnt;      // [tiles] arrival counters, zero between calls
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int OCC, int VA, int VB, bool TAIL, bool SK>
+// Operand layouts (LAY, 16-byte loads only, K % BK == 0): 0 = the canonical
+// NN form (A' K-contiguous, B' N-contiguous); 1 = B' K-contiguous (a
+// row-major A times a column-major B); 2 = A' M-contiguous (column-major A
+// times row-major B, after the transpose identity).  Forms 1 and 2 load four
+// consecutive k of one column of B' (four consecutive m of one column of A')
+// and write them to the same [k][n] ([m][k]) LDS rows as form 0, one float at
+// a time; the MFMA loop is the same.
+template <int BM, int BN, int BK, int WM, int WN, int OCC, int VA, int VB, bool TAIL, bool SK,
+          int LAY = 0>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArgs sk) {
     typedef typename VecT<VA>::T TA;
     typedef typename VecT<VB>::T TB;
@@ -258,6 +266,13 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
     constexpr int AK = BK / VA, A_RS = NT / AK;
     constexpr int BNV = BN / VB, B_RS = NT / BNV;
     static_assert(NT % AK == 0 && NT % BNV == 0, "loads must tile the slice");
+    static_assert(LAY == 0 || (VA == 4 && VB == 4 && !TAIL && !SK), "layout forms are 16-byte only");
+    // Form 1: B' column n = b_nj + r*B_NRS, k = b_k4..b_k4+3 of the slice.
+    // Form 2: A' row k = a_kj + r*A_KRS, m = a_m4..a_m4+3 of the tile.
+    constexpr int BKV = BK / 4, B_NRS = NT / BKV;
+    constexpr int AMV = BM / 4, A_KRS = NT / AMV;
+    static_assert(LAY != 1 || (NT % BKV == 0 && LB * B_NRS == BN), "form 1 must tile the slice");
+    static_assert(LAY != 2 || (NT % AMV == 0 && LA * A_KRS == BK), "form 2 must tile the slice");
 
     f32x16 acc[TM][TN];
     // Thread-chunk c of the accumulators: 4 consecutive values of one MFMA
@@ -311,18 +326,39 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
         constexpr bool WIDE = VA == 4 && VB == 4;
         const float* a_src[WIDE ? LA : 1];
         const float* b_src[WIDE ? LB : 1];
+        const int b_nj = tid / BKV, b_k4 = (tid % BKV) * 4;
+        const int a_kj = tid / AMV, a_m4 = (tid % AMV) * 4;
         if constexpr (WIDE) {
+            if constexpr (LAY == 2) {
+                // Columns past M read the last valid 4-float chunk (M % 4 == 0).
+                const int a_mm = a_m4 + 4 <= mlim ? a_m4 : mlim - 4;
 #pragma unroll
-            for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
+                for (int r = 0; r < LA; ++r)
+                    a_src[r] = A + (int64_t)(a_kj + r * A_KRS) * p.lda + m0 + a_mm;
+            } else {
 #pragma unroll
-            for (int r = 0; r < LB; ++r) b_src[r] = b_ptr(r);
+                for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
+            }
+            if constexpr (LAY == 1) {
+                // Columns past N read the last valid column.
+#pragma unroll
+                for (int r = 0; r < LB; ++r) {
+                    const int nj = b_nj + r * B_NRS;
+                    b_src[r] = B + (n0 + (nj < nlim ? nj : nlim - 1)) * p.ldb + b_k4;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < LB; ++r) b_src[r] = b_ptr(r);
+            }
         }
+        const int64_t a_step = LAY == 2 ? (int64_t)BK * p.lda : BK;
+        const int64_t b_step = LAY == 1 ? (int64_t)BK : (int64_t)BK * p.ldb;
         auto fetch = [&](int64_t kt) {
             if constexpr (WIDE) {
 #pragma unroll
-                for (int r = 0; r < LA; ++r) ra[r] = *(const TA*)(a_src[r] + kt * BK);
+                for (int r = 0; r < LA; ++r) ra[r] = *(const TA*)(a_src[r] + kt * a_step);
 #pragma unroll
-                for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(b_src[r] + kt * BK * p.ldb);
+                for (int r = 0; r < LB; ++r) rb[r] = *(const TB*)(b_src[r] + kt * b_step);
             } else {
                 const float* ab = a_base + kt * BK;
                 const float* bb = b_base + kt * BK * p.ldb;
@@ -357,10 +393,26 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
             }
         };
         auto stash = [&](int slot) {
+            if constexpr (LAY == 2) {
 #pragma unroll
-            for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
+                for (int r = 0; r < LA; ++r)
 #pragma unroll
-            for (int r = 0; r < LB; ++r) *(TB*)(&Bs[slot][(b_ki0 + r * B_RS) * BROW + b_nc]) = rb[r];
+                    for (int e = 0; e < 4; ++e)
+                        As[slot][(a_m4 + e) * AROW + a_kj + r * A_KRS] = lane_of<VA>(ra[r], e);
+            } else {
+#pragma unroll
+                for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
+            }
+            if constexpr (LAY == 1) {
+#pragma unroll
+                for (int r = 0; r < LB; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Bs[slot][(b_k4 + e) * BROW + b_nj + r * B_NRS] = lane_of<VB>(rb[r], e);
+            } else {
+#pragma unroll
+                for (int r = 0; r < LB; ++r) *(TB*)(&Bs[slot][(b_ki0 + r * B_RS) * BROW + b_nc]) = rb[r];
+            }
         };
         auto load = [&](int64_t kt) {
             if constexpr (TAIL) {
@@ -511,19 +563,30 @@ struct BigCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 4
 struct SmallCfg { static constexpr int BM = 128, BN = 128, BK = 16, WM = 2, WN = 2, OCC = 2; };
 struct UnalignedCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = 4, OCC = 1; };
 
+// Operand form of the 16-byte kernels (the LAY parameter), -1 if none.
+int fast_layout(const Problem& p) {
+    if (p.a_kc && !p.b_kc) return 0;
+    if (p.a_kc && p.b_kc) return 1;
+    if (!p.a_kc && !p.b_kc) return 2;
+    return -1;
+}
 template <class CF>
-bool fast_supports(const Problem& p) {
-    if (p.dtype != F32 || !p.a_kc || p.b_kc) return false;
-    if (p.K <= 0 || p.K % CF::BK != 0 || p.N % 4 != 0) return false;
+bool fast_supports(const Problem& p, bool any_layout) {
+    if (p.dtype != F32) return false;
+    const int lay = fast_layout(p);
+    if (lay < 0 || (lay != 0 && !any_layout)) return false;
+    if (p.K <= 0 || p.K % CF::BK != 0) return false;
+    if (lay != 1 && p.N % 4 != 0) return false;      // B' rows read as 4-float chunks
+    if (lay == 2 && p.M % 4 != 0) return false;      // A' columns read as 4-float chunks
     if (p.lda % 4 != 0 || p.ldb % 4 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
     return tiles > 0 && tiles <= 0x7fffffff;
 }
-template <class CF, int VA, int VB, bool TAIL>
+template <class CF, int VA, int VB, bool TAIL, int LAY = 0>
 hipError_t fast_launch(const Problem& p, hipStream_t s) {
     const int64_t tiles = ((p.M + CF::BM - 1) / CF::BM) * ((p.N + CF::BN - 1) / CF::BN);
-    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL, false>),
+    hipLaunchKernelGGL((k_f32_fast<CF::BM, CF::BN, CF::BK, CF::WM, CF::WN, CF::OCC, VA, VB, TAIL, false, LAY>),
                        dim3((unsigned)tiles), dim3(64 * CF::WM * CF::WN), 0, s, p, SKArgs{});
     return hipGetLastError();
 }
@@ -565,11 +628,16 @@ int unaligned_vb(const Problem& p) {
 }  // namespace
 
 bool f32_fast_supports(const Problem& p, bool big) {
-    return big ? fast_supports<BigCfg>(p) : fast_supports<SmallCfg>(p);
+    return big ? fast_supports<BigCfg>(p, true) : fast_supports<SmallCfg>(p, false);
 }
 
 hipError_t launch_f32_fast(const Problem& p, bool big, hipStream_t s) {
-    return big ? fast_launch<BigCfg, 4, 4, false>(p, s) : fast_launch<SmallCfg, 4, 4, false>(p, s);
+    if (!big) return fast_launch<SmallCfg, 4, 4, false>(p, s);
+    switch (fast_layout(p)) {
+    case 1: return fast_launch<BigCfg, 4, 4, false, 1>(p, s);
+    case 2: return fast_launch<BigCfg, 4, 4, false, 2>(p, s);
+    default: return fast_launch<BigCfg, 4, 4, false>(p, s);
+    }
 }
 
 bool f32_unaligned_supports(const Problem& p) {

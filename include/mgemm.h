@@ -63,7 +63,8 @@ typedef enum {
     MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
     MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
     MGEMM_KERNEL_H_PP_256 = 7,   /* FP16/BF16 NN, 256x256 tiles, 8-wave ping-pong, direct-to-LDS */
-    MGEMM_KERNEL_F32_FAST = 8,   /* FP32 NN, 16-byte aligned operands, 256x256x32 tiles, 16 waves */
+    MGEMM_KERNEL_F32_FAST = 8,   /* FP32 (any layout pair), 16-byte aligned operands, K % 32 == 0,
+                                    256x256x32 tiles, 16 waves */
     MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
     MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 NN, 256x256 tiles, 4 waves of 128x128, direct-to-LDS ring */
     MGEMM_KERNEL_SKINNY_SK = 11, /* FP16/BF16, M <= 64, 256-column blocks, K split over workgroups */

@@ -165,6 +165,33 @@ def test_f32_unaligned_bit_exact(h, M, N, K, lda, ldb, ldc):
         P.check_bit_exact(case, *out)
 
 
+# The 16-byte FP32 kernel on the two mixed layout pairs (row-major A with
+# column-major B: B' K-contiguous; column-major A with row-major B: A'
+# M-contiguous after the transpose identity): edge tiles in both directions,
+# beta != 0, integer data: bit-exact.  (M, N, K, layoutA, layoutB)
+F32_MIXED = [(300, 516, 160, "row", "col"), (300, 516, 160, "col", "row"),
+             (520, 260, 96, "row", "col"), (260, 520, 64, "col", "row")]
+
+
+@pytest.mark.parametrize("M,N,K,la,lb", F32_MIXED)
+def test_f32_fast_mixed_layouts_bit_exact(h, M, N, K, la, lb):
+    case = W.Case("f32mix", M, N, K, "f32", layoutA=la, layoutB=lb, alpha=1.0, beta=-0.5,
+                  kindA="int", kindB="int", kindC="int", seeds=(M, N, K + 7))
+    inputs = case.make()
+    for k in ("auto", "f32_fast"):
+        say("f32 mixed", (M, N, K, la, lb), k)
+        P.check_bit_exact(case, *P.run_gpu(h, case, k, inputs=inputs))
+
+
+@pytest.mark.parametrize("la,lb", [("row", "col"), ("col", "row")])
+def test_sgemm_4096_mixed_layouts_sampled(h, la, lb):
+    case = W.Case("sgemm_4096_%s_%s" % (la, lb), 4096, 4096, 4096, "f32", layoutA=la,
+                  layoutB=lb, seeds=(2001, 2002, 2003))
+    say(case.name)
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 128), cols=[0, 127, 128, 4095])
+
+
 # Stream-K FP32 (one workgroup per CU, equal shares of the (tile, K slice)
 # pairs): shares that cut tiles into two or three pieces, a single tile whose
 # 157 slices are each a piece of their own, unaligned operands and K tails;
@@ -567,6 +594,8 @@ def test_dispatch_choices(h):
                                       case.alpha, 256, case.lda, 256, case.ldb, case.beta, 256,
                                       case.ldc, case.dtype)
     assert sel(W.sgemm_4096()) == "f32_fast"
+    for la, lb in (("row", "col"), ("col", "row")):
+        assert sel(W.Case("mixed", 4096, 4096, 4096, "f32", layoutA=la, layoutB=lb)) == "f32_fast"
     assert sel(W.ragged_f32()) == "f32_sk"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x192"
