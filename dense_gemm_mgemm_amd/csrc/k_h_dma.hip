@@ -55,8 +55,9 @@
 // The sum order is fixed, so results do not depend on timing; the kernel
 // boundary orders the two phases, so no atomics or fences are needed.
 //
-// Restrictions (host-checked): A' K-contiguous, B' N-contiguous, K % 32 == 0,
-// N % 8 == 0, lda and ldb multiples of 8, 16-byte aligned bases.
+// Restrictions (host-checked): A' K-contiguous, B' N-contiguous (N % 8 == 0)
+// or K-contiguous (the BKC form), K % 32 == 0, lda and ldb multiples of 8,
+// 16-byte aligned bases.
 #include "common.h"
 
 namespace mgemm {
@@ -162,9 +163,14 @@ struct Frags {
     i32x4 b[TN];
 };
 
-template <int DT, int BN, bool DUAL, int EPI>
+// BKC: B' K-contiguous (a row-major A times a column-major B, the x W^T
+// layout of weights stored out x in).  The B slot then holds BN rows of 64
+// bytes, one column of B' each, staged and read exactly like A's rows
+// (ds_read_b128 fragments, no transposed reads).
+template <int DT, int BN, bool DUAL, int EPI, bool BKC = false>
 __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     using G = Cfg<BN, DUAL>;
+    static_assert(!(BKC && DUAL), "the gated pair takes N-contiguous weights");
     constexpr int TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
     constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
     using Fr = Frags<TM, TN>;
@@ -204,6 +210,18 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
         src[i] = A + (m0 + rr) * p.lda + (int64_t)j0 * BK + 8 * c;
         dst[i] = (64 * wave + 16 * i) * A_ROW;
     }
+    if constexpr (BKC) {
+        constexpr int BR = BN / 4;                        // B' columns copied per wave
+        static_assert(BR == 16 * G::B_COPIES, "B copies must cover the slot");
+#pragma unroll
+        for (int i = 0; i < G::B_COPIES; ++i) {
+            const int r = BR * wave + 16 * i + (lane >> 2);
+            const int c = (lane & 3) ^ a_swz(r);
+            const int rr = r < nlim ? r : nlim - 1;      // columns past N: the last valid one
+            src[A_COPIES + i] = B + (n0 + rr) * p.ldb + (int64_t)j0 * BK + 8 * c;
+            dst[A_COPIES + i] = A_BYTES + (BR * wave + 16 * i) * A_ROW;
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < G::B_COPIES; ++i) {
         const int j = wave * G::B_COPIES + i;
@@ -223,8 +241,9 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
         }
         dst[A_COPIES + i] = A_BYTES + j * 1024;
     }
+    }
     // (The gated pair's two B matrices share ldb: host-checked.)
-    const int64_t a_kstep = BK, b_kstep = (int64_t)BK * p.ldb;
+    const int64_t a_kstep = BK, b_kstep = BKC ? (int64_t)BK : (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
         const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
@@ -242,7 +261,17 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
             a_off[tm][ks] = r * A_ROW + ((c ^ a_swz(r)) << 4);
         }
     int b_off[TN][2][2];
-    {
+    if constexpr (BKC) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int r = G::WN * wn + 32 * tn + (lane & 31);
+                const int c = 2 * ks + (lane >> 5);
+                b_off[tn][ks][0] = A_BYTES + r * A_ROW + ((c ^ a_swz(r)) << 4);
+                b_off[tn][ks][1] = 0;
+            }
+    } else {
         const int q = lane >> 4, t = lane & 15;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
@@ -261,6 +290,10 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     };
     auto read_b = [&](Fr& f, int s, int ks, int tn) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
+        if constexpr (BKC) {
+            f.b[tn] = *(const i32x4*)(base + b_off[tn][ks][0]);
+            return;
+        }
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(base + b_off[tn][ks][0]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -451,9 +484,9 @@ constexpr int64_t tile_part_bytes() {
     return (int64_t)NT * Cfg<BN, DUAL>::TM * Cfg<BN, DUAL>::TN * 16 * (int64_t)sizeof(float);
 }
 
-template <int DT, int BN, bool DUAL, int EPI>
+template <int DT, int BN, bool DUAL, int EPI, bool BKC>
 hipError_t launch_epi(const Problem& p, const HSplit& sp, hipStream_t s) {
-    auto kern = k_h_dma<DT, BN, DUAL, EPI>;
+    auto kern = k_h_dma<DT, BN, DUAL, EPI, BKC>;
     const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
@@ -477,19 +510,19 @@ hipError_t launch_reduce(const Problem& p, const HSplit& sp, hipStream_t s) {
 // One kernel per epilogue: the store loop is unrolled over every output of
 // the tile, so a runtime choice would put the activation's code between the
 // plain stores (and the 256-wide tile has no registers to spare for it).
-template <int DT, int BN, bool DUAL>
+template <int DT, int BN, bool DUAL, bool BKC = false>
 hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
     const int nk = (int)(p.K / BK);
     HSplit sp{(float*)ws.part, 1, nk};
     const bool silu = !DUAL && p.epilogue == EPI_SILU;
     if (ksplit <= 1) {
         if constexpr (!DUAL)
-            if (silu) return launch_epi<DT, BN, false, EPI_SILU>(p, sp, s);
-        return launch_epi<DT, BN, DUAL, EPI_NONE>(p, sp, s);
+            if (silu) return launch_epi<DT, BN, false, EPI_SILU, BKC>(p, sp, s);
+        return launch_epi<DT, BN, DUAL, EPI_NONE, BKC>(p, sp, s);
     }
     sp.nks = (nk + ksplit - 1) / ksplit;
     sp.ksplit = (nk + sp.nks - 1) / sp.nks;
-    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL>(p, sp, s);
+    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL, BKC>(p, sp, s);
     if (e != hipSuccess) return e;
     if constexpr (!DUAL)
         if (silu) return launch_reduce<DT, BN, false, EPI_SILU>(p, sp, s);
@@ -501,8 +534,10 @@ hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStrea
 bool h_dma_supports(const Problem& p, int bn) {
     if (bn != 256 && bn != 192) return false;
     if (p.dtype != F16 && p.dtype != BF16) return false;
-    if (!p.a_kc || p.b_kc) return false;
-    if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || p.N % 8 != 0) return false;
+    if (!p.a_kc) return false;
+    // N-contiguous B' rows are read as 8-element chunks; K-contiguous B'
+    // columns (b_kc) as 32-element K slices like A's rows.
+    if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || (!p.b_kc && p.N % 8 != 0)) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
@@ -523,6 +558,13 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
 }
 
 hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s) {
+    if (p.b_kc) {
+        if (bn == 192)
+            return p.dtype == F16 ? launch_dt<F16, 192, false, true>(p, ksplit, ws, s)
+                                  : launch_dt<BF16, 192, false, true>(p, ksplit, ws, s);
+        return p.dtype == F16 ? launch_dt<F16, 256, false, true>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 256, false, true>(p, ksplit, ws, s);
+    }
     if (bn == 192)
         return p.dtype == F16 ? launch_dt<F16, 192, false>(p, ksplit, ws, s)
                               : launch_dt<BF16, 192, false>(p, ksplit, ws, s);
@@ -531,7 +573,7 @@ hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& w
 }
 
 bool h_gated_supports(const Problem& p) {
-    if (!h_dma_supports(p, 192) || p.B2 == nullptr || p.ldb2 != p.ldb) return false;
+    if (p.b_kc || !h_dma_supports(p, 192) || p.B2 == nullptr || p.ldb2 != p.ldb) return false;
     return ((uintptr_t)p.B2 & 15) == 0;
 }
 

@@ -397,6 +397,41 @@ def test_h_dma_split_k_bit_exact(h, M, N, K):
                 P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
 
 
+# The direct-to-LDS kernel with a K-contiguous B' (row-major A times a
+# column-major B: weights stored out x in): ragged edges in both directions, N
+# not a multiple of 8, both widths, unsplit and split, plain and SiLU; integer
+# data, so every form must give the oracle's bits.
+BKC_SHAPES = [(300, 200, 640), (256, 192, 1024), (513, 777, 320), (37, 100, 160)]
+
+
+@pytest.mark.parametrize("M,N,K", BKC_SHAPES)
+def test_h_dma_b_k_contiguous_bit_exact(h, M, N, K):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("hbkc", M, N, K, dtype, layoutB="col", kindA="int", kindB="int",
+                      kindC="int", alpha=1.0, beta=-0.5, seeds=(M, N, K + 1))
+        inputs = case.make()
+        for kernel in ("h_dma_256x256", "h_dma_256x192"):
+            for ks in (1, 3):
+                say("h_dma B K-contiguous", dtype, (M, N, K), kernel, ks)
+                P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
+        case_s = W.Case("hbkc_silu", M, N, K, dtype, layoutB="col", kindA="int", kindB="int",
+                        kindC="int", alpha=0.25, beta=-0.5, seeds=(M, N, K + 2))
+        P.check_silu(case_s, *P.run_gpu(h, case_s, "h_dma_256x192", epilogue="silu"),
+                     exact_gemm=True)
+
+
+def test_ffn_bf16_weights_out_by_in_sampled(h):
+    # x W^T with W stored 12288 x 4096 (out x in): B column-major.
+    case = W.Case("ffn_bf16_wt", 1024, 12288, 4096, "bf16", layoutB="col", kindA="normal",
+                  kindB="normal", scaleB=0.02, seeds=(4001, 4002, 4003))
+    sel = mg.mgemm_select_variant(h, "row", "col", 1024, 12288, 4096, 1.0, 256, 4096, 256, 4096,
+                                  0.0, 256, 12288, "bf16")
+    say("ffn W^T", sel)
+    assert sel[0].startswith("h_dma")
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, rows=P.sample_rows(case.M, 256), cols=[0, 191, 192, 12287])
+
+
 def test_h_dma_split_k_silu(h):
     for dtype in ("bf16", "f16"):
         case = W.Case("hsplit_silu", 300, 520, 640, dtype, alpha=0.25, beta=-0.5, kindA="int",
