@@ -55,8 +55,9 @@
 // The sum order is fixed, so results do not depend on timing; the kernel
 // boundary orders the two phases, so no atomics or fences are needed.
 //
-// Restrictions (host-checked): A' K-contiguous, B' N-contiguous (N % 8 == 0)
-// or K-contiguous (the BKC form), K % 32 == 0, lda and ldb multiples of 8,
+// Restrictions (host-checked): A' K-contiguous, or M-contiguous with M % 8 ==
+// 0 (the AMC form, with an N-contiguous B'); B' N-contiguous (N % 8 == 0) or
+// K-contiguous (the BKC form); K % 32 == 0, lda and ldb multiples of 8,
 // 16-byte aligned bases.
 #include "common.h"
 
@@ -167,10 +168,13 @@ struct Frags {
 // layout of weights stored out x in).  The B slot then holds BN rows of 64
 // bytes, one column of B' each, staged and read exactly like A's rows
 // (ds_read_b128 fragments, no transposed reads).
-template <int DT, int BN, bool DUAL, int EPI, bool BKC = false>
+// AMC: A' M-contiguous (a column-major A times a row-major B, after the
+// transpose identity).  The A slot then holds 32 K-rows of 512 bytes staged
+// and read exactly like the 256-wide B slot (chunk swizzle, transposed reads).
+template <int DT, int BN, bool DUAL, int EPI, bool BKC = false, bool AMC = false>
 __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     using G = Cfg<BN, DUAL>;
-    static_assert(!(BKC && DUAL), "the gated pair takes N-contiguous weights");
+    static_assert(!(BKC && DUAL) && !(AMC && DUAL) && !(AMC && BKC), "operand forms");
     constexpr int TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
     constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
     using Fr = Frags<TM, TN>;
@@ -202,6 +206,21 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     // the B slot (lane l: position 64j+l of the row-major slot).
     const uint16_t* src[COPIES];
     int dst[COPIES];
+    if constexpr (AMC) {
+        // Copy j covers the 64 chunk positions [64j, 64j+64) of the A slot
+        // (32 K-rows of 32 chunks); rows past M read the last valid chunk.
+#pragma unroll
+        for (int i = 0; i < A_COPIES; ++i) {
+            const int j = wave * A_COPIES + i;
+            const int f = 64 * j + lane;
+            const int k = f / 32, pos = f % 32;
+            int c = b_pos<256>(pos, k);
+            const int cmax = (mlim >> 3) - 1;
+            c = c <= cmax ? c : cmax;
+            src[i] = A + ((int64_t)j0 * BK + k) * p.lda + m0 + 8 * c;
+            dst[i] = j * 1024;
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < A_COPIES; ++i) {
         const int r = 64 * wave + 16 * i + (lane >> 2);
@@ -209,6 +228,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
         const int rr = r < mlim ? r : mlim - 1;
         src[i] = A + (m0 + rr) * p.lda + (int64_t)j0 * BK + 8 * c;
         dst[i] = (64 * wave + 16 * i) * A_ROW;
+    }
     }
     if constexpr (BKC) {
         constexpr int BR = BN / 4;                        // B' columns copied per wave
@@ -243,7 +263,8 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     }
     }
     // (The gated pair's two B matrices share ldb: host-checked.)
-    const int64_t a_kstep = BK, b_kstep = BKC ? (int64_t)BK : (int64_t)BK * p.ldb;
+    const int64_t a_kstep = AMC ? (int64_t)BK * p.lda : (int64_t)BK;
+    const int64_t b_kstep = BKC ? (int64_t)BK : (int64_t)BK * p.ldb;
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto copy = [&](int s, int i) {
         const unsigned base = lds0 + (unsigned)(s % SLOTS) * SLOT_BYTES;
@@ -251,15 +272,29 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     };
 
     // Fragment read offsets within a slot.
-    int a_off[TM][2];
+    int a_off[TM][2][AMC ? 2 : 1];
+    if constexpr (AMC) {
+        const int q = lane >> 4, t = lane & 15;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+        for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int r = G::WROWS * wm + 32 * tm + (lane & 31);
-            const int c = 2 * ks + (lane >> 5);
-            a_off[tm][ks] = r * A_ROW + ((c ^ a_swz(r)) << 4);
-        }
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = ks * 16 + 8 * (q >> 1) + 4 * h + (t >> 2);
+                    const int m = G::WROWS * wm + 32 * tm + 16 * (q & 1) + 4 * (t & 3);
+                    a_off[tm][ks][h] = k * 512 + (b_pos<256>(m >> 3, k) << 4) + ((m & 7) << 1);
+                }
+    } else {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int r = G::WROWS * wm + 32 * tm + (lane & 31);
+                const int c = 2 * ks + (lane >> 5);
+                a_off[tm][ks][0] = r * A_ROW + ((c ^ a_swz(r)) << 4);
+            }
+    }
     int b_off[TN][2][2];
     if constexpr (BKC) {
 #pragma unroll
@@ -286,7 +321,16 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     }
     auto read_a = [&](Fr& f, int s, int ks, int tm) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
-        f.a[tm] = *(const i32x4*)(base + a_off[tm][ks]);
+        if constexpr (AMC) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + a_off[tm][ks][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(base + a_off[tm][ks][AMC ? 1 : 0]));
+            const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+            f.a[tm] = i32x4{l2.x, l2.y, h2.x, h2.y};
+        } else {
+            f.a[tm] = *(const i32x4*)(base + a_off[tm][ks][0]);
+        }
     };
     auto read_b = [&](Fr& f, int s, int ks, int tn) {
         const unsigned char* base = smem + (s % SLOTS) * SLOT_BYTES;
@@ -484,9 +528,9 @@ constexpr int64_t tile_part_bytes() {
     return (int64_t)NT * Cfg<BN, DUAL>::TM * Cfg<BN, DUAL>::TN * 16 * (int64_t)sizeof(float);
 }
 
-template <int DT, int BN, bool DUAL, int EPI, bool BKC>
+template <int DT, int BN, bool DUAL, int EPI, bool BKC, bool AMC>
 hipError_t launch_epi(const Problem& p, const HSplit& sp, hipStream_t s) {
-    auto kern = k_h_dma<DT, BN, DUAL, EPI, BKC>;
+    auto kern = k_h_dma<DT, BN, DUAL, EPI, BKC, AMC>;
     const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
@@ -510,19 +554,19 @@ hipError_t launch_reduce(const Problem& p, const HSplit& sp, hipStream_t s) {
 // One kernel per epilogue: the store loop is unrolled over every output of
 // the tile, so a runtime choice would put the activation's code between the
 // plain stores (and the 256-wide tile has no registers to spare for it).
-template <int DT, int BN, bool DUAL, bool BKC = false>
+template <int DT, int BN, bool DUAL, bool BKC = false, bool AMC = false>
 hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
     const int nk = (int)(p.K / BK);
     HSplit sp{(float*)ws.part, 1, nk};
     const bool silu = !DUAL && p.epilogue == EPI_SILU;
     if (ksplit <= 1) {
         if constexpr (!DUAL)
-            if (silu) return launch_epi<DT, BN, false, EPI_SILU, BKC>(p, sp, s);
-        return launch_epi<DT, BN, DUAL, EPI_NONE, BKC>(p, sp, s);
+            if (silu) return launch_epi<DT, BN, false, EPI_SILU, BKC, AMC>(p, sp, s);
+        return launch_epi<DT, BN, DUAL, EPI_NONE, BKC, AMC>(p, sp, s);
     }
     sp.nks = (nk + ksplit - 1) / ksplit;
     sp.ksplit = (nk + sp.nks - 1) / sp.nks;
-    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL, BKC>(p, sp, s);
+    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL, BKC, AMC>(p, sp, s);
     if (e != hipSuccess) return e;
     if constexpr (!DUAL)
         if (silu) return launch_reduce<DT, BN, false, EPI_SILU>(p, sp, s);
@@ -534,10 +578,11 @@ hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStrea
 bool h_dma_supports(const Problem& p, int bn) {
     if (bn != 256 && bn != 192) return false;
     if (p.dtype != F16 && p.dtype != BF16) return false;
-    if (!p.a_kc) return false;
-    // N-contiguous B' rows are read as 8-element chunks; K-contiguous B'
-    // columns (b_kc) as 32-element K slices like A's rows.
+    if (!p.a_kc && p.b_kc) return false;
+    // N-contiguous B' rows (M-contiguous A' columns) are read as 8-element
+    // chunks; K-contiguous operands as 32-element K slices.
     if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || (!p.b_kc && p.N % 8 != 0)) return false;
+    if (!p.a_kc && p.M % 8 != 0) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
@@ -558,6 +603,13 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
 }
 
 hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s) {
+    if (!p.a_kc) {
+        if (bn == 192)
+            return p.dtype == F16 ? launch_dt<F16, 192, false, false, true>(p, ksplit, ws, s)
+                                  : launch_dt<BF16, 192, false, false, true>(p, ksplit, ws, s);
+        return p.dtype == F16 ? launch_dt<F16, 256, false, false, true>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 256, false, false, true>(p, ksplit, ws, s);
+    }
     if (p.b_kc) {
         if (bn == 192)
             return p.dtype == F16 ? launch_dt<F16, 192, false, true>(p, ksplit, ws, s)
@@ -573,7 +625,8 @@ hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& w
 }
 
 bool h_gated_supports(const Problem& p) {
-    if (p.b_kc || !h_dma_supports(p, 192) || p.B2 == nullptr || p.ldb2 != p.ldb) return false;
+    if (p.b_kc || !p.a_kc || !h_dma_supports(p, 192) || p.B2 == nullptr || p.ldb2 != p.ldb)
+        return false;
     return ((uintptr_t)p.B2 & 15) == 0;
 }
 

@@ -420,6 +420,28 @@ def test_h_dma_b_k_contiguous_bit_exact(h, M, N, K):
                      exact_gemm=True)
 
 
+# Column-major A times row-major B: after the transpose identity A' is
+# M-contiguous and staged like the 256-wide B slot (transposed reads).  M and N
+# multiples of 8, ragged against the tiles.
+AMC_SHAPES = [(304, 200, 640), (256, 192, 1024), (520, 776, 320), (40, 104, 160)]
+
+
+@pytest.mark.parametrize("M,N,K", AMC_SHAPES)
+def test_h_dma_a_m_contiguous_bit_exact(h, M, N, K):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("hamc", M, N, K, dtype, layoutA="col", kindA="int", kindB="int",
+                      kindC="int", alpha=1.0, beta=-0.5, seeds=(M, N, K + 3))
+        inputs = case.make()
+        for kernel in ("h_dma_256x256", "h_dma_256x192"):
+            for ks in (1, 3):
+                say("h_dma A M-contiguous", dtype, (M, N, K), kernel, ks)
+                P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
+        case_s = W.Case("hamc_silu", M, N, K, dtype, layoutA="col", kindA="int", kindB="int",
+                        kindC="int", alpha=0.25, beta=-0.5, seeds=(M, N, K + 4))
+        P.check_silu(case_s, *P.run_gpu(h, case_s, "h_dma_256x256", epilogue="silu"),
+                     exact_gemm=True)
+
+
 def test_ffn_bf16_weights_out_by_in_sampled(h):
     # x W^T with W stored 12288 x 4096 (out x in): B column-major.
     case = W.Case("ffn_bf16_wt", 1024, 12288, 4096, "bf16", layoutB="col", kindA="normal",
