@@ -66,9 +66,11 @@ typedef enum {
     MGEMM_KERNEL_F32_FAST = 8,   /* FP32 (any layout pair), 16-byte aligned operands, K % 32 == 0,
                                     256x256x32 tiles, 16 waves */
     MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
-    MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 NN, 256x256 tiles, 4 waves of 128x128, direct-to-LDS ring */
+    MGEMM_KERNEL_H_DMA_256 = 10, /* FP16/BF16 (any layout pair), 256x256 tiles, 4 waves of 128x128,
+                                    direct-to-LDS ring */
     MGEMM_KERNEL_SKINNY_SK = 11, /* FP16/BF16, M <= 64, 256-column blocks, K split over workgroups */
-    MGEMM_KERNEL_H_DMA_192 = 12, /* FP16/BF16 NN, 256x192 tiles, 4 waves of 128x96, direct-to-LDS ring */
+    MGEMM_KERNEL_H_DMA_192 = 12, /* FP16/BF16 (any layout pair), 256x192 tiles, 4 waves of 128x96,
+                                    direct-to-LDS ring */
     MGEMM_KERNEL_F32_FAST_U = 13, /* FP32 NN, any alignment and K: 256x256x32 tiles, narrower loads */
     MGEMM_KERNEL_F8_MFMA = 14,   /* FP8 codes (mgemm_run_fp8 only): 256x256 tiles, f8f6f4 MFMA */
     MGEMM_KERNEL_F8_GENERAL = 15, /* FP8 codes (mgemm_run_fp8 only): any K/alignment, VALU */
