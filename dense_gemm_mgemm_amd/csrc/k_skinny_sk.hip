@@ -1,5 +1,6 @@
 // Skinny-M FP16/BF16 GEMM (M <= 64) with K split across workgroups:
-// C[M x N] = X[M x K] * W[K x N], W N-contiguous, read once from HBM.
+// C[M x N] = X[M x K] * W[K x N], W N-contiguous (or, in the BKC form below,
+// K-contiguous: weights stored out x in), read once from HBM.
 //
 // Why a second skinny kernel.  Streaming W as 128-byte row segments (one
 // 64-column block per workgroup over the whole K range) reaches only about
@@ -103,7 +104,15 @@ struct SplitArgs {
     int per;            // K steps per range (the last range may be shorter)
 };
 
-template <int DT, int MT>
+// BKC: W' K-contiguous (weights stored out x in, C = X W^T).  The W slot then
+// holds the block's 256 columns as rows of 64 bytes (32 K-values each), copied
+// 16 rows per 1 KiB copy with the XOR swizzle ((r>>1) ^ (r>>2)) & 3 on the
+// four 16-byte chunks of row r, and each fragment is one ds_read_b128 (lane l:
+// column 16nb + l%16 of the wave's 64, chunk l/16), which that swizzle keeps
+// free of bank conflicts.
+__device__ __forceinline__ int kc_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+template <int DT, int MT, bool BKC = false>
 __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     constexpr int MB = MT / 16;
     constexpr int X_BYTES = MT * KS * 2;
@@ -138,12 +147,19 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     int w_dst[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int j = 4 * w + i;                     // copy j: rows 2j, 2j+1 of the step
-        const int k = 2 * j + (lane >> 5);
-        int c = (lane & 31) ^ w_swz(k);
-        const int cmax = (nlim >> 3) - 1;
-        c = c <= cmax ? c : cmax;
-        w_src[i] = Wt + (s_begin * KS + k) * p.ldb + n0 + 8 * c;
+        const int j = 4 * w + i;
+        if constexpr (BKC) {                         // copy j: columns 16j .. 16j+15
+            const int r = 16 * j + (lane >> 2);
+            const int c = (lane & 3) ^ kc_swz(r);
+            const int rr = r < nlim ? r : nlim - 1;  // columns past N: the last valid one
+            w_src[i] = Wt + (n0 + rr) * p.ldb + s_begin * KS + 8 * c;
+        } else {                                     // copy j: rows 2j, 2j+1 of the step
+            const int k = 2 * j + (lane >> 5);
+            int c = (lane & 31) ^ w_swz(k);
+            const int cmax = (nlim >> 3) - 1;
+            c = c <= cmax ? c : cmax;
+            w_src[i] = Wt + (s_begin * KS + k) * p.ldb + n0 + 8 * c;
+        }
         w_dst[i] = j * 1024;
     }
     const uint16_t* x_src;
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
         x_src = X + (int64_t)rr * p.lda + s_begin * KS + 8 * c;
     }
     const int x_dst = W_BYTES + (has_x ? w : 0) * 1024;
-    const int64_t w_step = (int64_t)KS * p.ldb;
+    const int64_t w_step = BKC ? (int64_t)KS : (int64_t)KS * p.ldb;
 
     const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     auto issue = [&](int s) {
@@ -176,7 +192,14 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
         x_off[mb] = W_BYTES + r * 64 + ((c ^ x_swz(r)) << 4);
     }
     int w_off[4][2];
-    {
+    if constexpr (BKC) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int r = 64 * w + 16 * nb + (lane & 15), c = lane >> 4;
+            w_off[nb][0] = r * 64 + ((c ^ kc_swz(r)) << 4);
+            w_off[nb][1] = 0;
+        }
+    } else {
         const int q = lane >> 4, tt = lane & 15;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
@@ -209,6 +232,10 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
         for (int mb = 0; mb < MB; ++mb) xf[mb] = *(const i32x4*)(base + x_off[mb]);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
+            if constexpr (BKC) {
+                wf[nb] = *(const i32x4*)(base + w_off[nb][0]);
+                continue;
+            }
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) i16x4*)(base + w_off[nb][0]));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -364,9 +391,9 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     });
 }
 
-template <int DT, int MT>
+template <int DT, int MT, bool BKC>
 hipError_t launch_cfg(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
-    auto kern = k_skinny_sk<DT, MT>;
+    auto kern = k_skinny_sk<DT, MT, BKC>;
     const size_t lds = (size_t)SLOTS * (W_BYTES + MT * KS * 2);
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
@@ -375,11 +402,15 @@ hipError_t launch_cfg(const Problem& p, const SplitArgs& sa, int64_t grid, hipSt
     return hipGetLastError();
 }
 
+template <int DT, bool BKC>
+hipError_t launch_mt(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
+    if (p.M <= 16) return launch_cfg<DT, 16, BKC>(p, sa, grid, s);
+    if (p.M <= 32) return launch_cfg<DT, 32, BKC>(p, sa, grid, s);
+    return launch_cfg<DT, 64, BKC>(p, sa, grid, s);
+}
 template <int DT>
 hipError_t launch_dt(const Problem& p, const SplitArgs& sa, int64_t grid, hipStream_t s) {
-    if (p.M <= 16) return launch_cfg<DT, 16>(p, sa, grid, s);
-    if (p.M <= 32) return launch_cfg<DT, 32>(p, sa, grid, s);
-    return launch_cfg<DT, 64>(p, sa, grid, s);
+    return p.b_kc ? launch_mt<DT, true>(p, sa, grid, s) : launch_mt<DT, false>(p, sa, grid, s);
 }
 
 int mt_of(int64_t M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
@@ -388,8 +419,10 @@ int mt_of(int64_t M) { return M <= 16 ? 16 : (M <= 32 ? 32 : 64); }
 
 bool skinny_sk_supports(const Problem& p) {
     if (p.dtype != F16 && p.dtype != BF16) return false;
-    if (!p.a_kc || p.b_kc) return false;
-    if (p.M < 1 || p.M > 64 || p.K <= 0 || p.K % KS != 0 || p.N % 8 != 0) return false;
+    if (!p.a_kc) return false;
+    // N-contiguous W rows are read as 8-element chunks; K-contiguous W'
+    // columns (b_kc) as 32-element K slices.
+    if (p.M < 1 || p.M > 64 || p.K <= 0 || p.K % KS != 0 || (!p.b_kc && p.N % 8 != 0)) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     return (p.N + BNS - 1) / BNS <= 0x7fffffff / 64;

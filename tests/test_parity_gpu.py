@@ -442,6 +442,32 @@ def test_h_dma_a_m_contiguous_bit_exact(h, M, N, K):
                      exact_gemm=True)
 
 
+# The skinny split kernel with K-contiguous weights (C = X W^T, W stored
+# out x in): every M class, N not a multiple of 8, one to eight K ranges,
+# beta != 0; integer data: bit-exact.
+@pytest.mark.parametrize("M", [1, 5, 16, 33, 64])
+def test_skinny_weights_out_by_in_bit_exact(h, M):
+    for dtype in ("bf16", "f16"):
+        case = W.Case("skinny_wt", M, 1000, 1024, dtype, layoutB="col", kindA="int", kindB="int",
+                      kindC="int", alpha=1.0, beta=-0.5, seeds=(M, 1000, 1024))
+        inputs = case.make()
+        for ks in (1, 3, 8):
+            say("skinny W^T", dtype, M, ks)
+            P.check_bit_exact(case, *P.run_gpu(h, case, "skinny_sk", inputs=inputs, ksplit=ks))
+
+
+@pytest.mark.parametrize("M", W.SKINNY_M)
+def test_skinny_weights_out_by_in_ffn_sampled(h, M):
+    case = W.Case("skinny_wt_ffn", M, 12288, 4096, "bf16", layoutB="col", kindA="normal",
+                  kindB="normal", scaleB=0.02, seeds=(4001, 4002, 4003))
+    sel = mg.mgemm_select_variant(h, "row", "col", M, 12288, 4096, 1.0, 256, 4096, 256, 4096,
+                                  0.0, 256, 12288, "bf16")
+    say("skinny W^T ffn", M, sel)
+    assert sel[0] == "skinny_sk"
+    out = P.run_gpu(h, case)
+    P.check_tolerance(case, *out, cols=[0, 255, 256, 12287])
+
+
 def test_ffn_bf16_weights_out_by_in_sampled(h):
     # x W^T with W stored 12288 x 4096 (out x in): B column-major.
     case = W.Case("ffn_bf16_wt", 1024, 12288, 4096, "bf16", layoutB="col", kindA="normal",
