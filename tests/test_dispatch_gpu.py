@@ -123,12 +123,15 @@ def test_tune_argument_errors(h):
 
 
 def test_tune_other_dtypes_and_layouts(h):
-    # FP32 (aligned and ragged), column-major FP16 and skinny BF16 shapes: the
+    # FP32 (aligned and ragged), column-major FP16, skinny BF16 and the mixed
+    # layout pairs (weights stored out x in included): the
     # tuner measures whatever can run each one, the table steers mgemm_run,
     # and the results stay exact on integer data.
     cases = [("f32", "row", "row", [(1000, 1000, 1000), (512, 512, 2048)]),
+             ("f32", "col", "row", [(512, 512, 1024)]),
              ("f16", "col", "col", [(512, 1024, 2048)]),
-             ("bf16", "row", "row", [(16, 12288, 4096), (64, 6144, 1024)])]
+             ("bf16", "row", "row", [(16, 12288, 4096), (64, 6144, 1024)]),
+             ("bf16", "row", "col", [(512, 1024, 2048), (16, 4096, 2048)])]
     for dtype, la, lb, shapes in cases:
         res = mg.mgemm_tune(h, dtype, la, lb, shapes)
         for r in res:
