@@ -17,13 +17,25 @@ CSRC = os.path.join(ROOT, "dense_gemm_mgemm_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
 
 
+_BUILT = {}
+
+
+def device_build(name, tmp_path):
+    """gfx950 assembly of one source and the compiler's per-kernel resource
+    remarks, from a single compile shared by every test of this module."""
+    if name not in _BUILT:
+        out = tmp_path / (name + ".s")
+        r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-S", "-O3",
+                            "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                            "-Rpass-analysis=kernel-resource-usage",
+                            "-I" + os.path.join(ROOT, "include"), os.path.join(CSRC, name),
+                            "-o", str(out)], check=True, capture_output=True, text=True)
+        _BUILT[name] = (out.read_text(), r.stderr)
+    return _BUILT[name]
+
+
 def device_asm(src, tmp_path):
-    out = tmp_path / (os.path.basename(src) + ".s")
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-S", "-O3",
-                    "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                    "-I" + os.path.join(ROOT, "include"), src, "-o", str(out)],
-                   check=True, capture_output=True)
-    return out.read_text()
+    return device_build(os.path.basename(src), tmp_path)[0]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
@@ -50,15 +62,11 @@ def test_m0_only_written_by_our_copies(name, tmp_path):
 @pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip",
                                   "k_h_dma.hip", "k_general.hip", "k_f8.hip", "k_util.hip"])
 def test_no_register_spills(name, tmp_path):
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-c", "-O3",
-                        "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                        "-Rpass-analysis=kernel-resource-usage", "-I" + os.path.join(ROOT, "include"),
-                        os.path.join(CSRC, name), "-o", str(tmp_path / "k.o")],
-                       capture_output=True, text=True, check=True)
-    spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", r.stderr)]
-    assert spills and max(spills) == 0, r.stderr[-2000:]
-    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)]
-    assert len(scratch) == len(spills) and max(scratch) == 0, r.stderr[-2000:]
+    remarks = device_build(name, tmp_path)[1]
+    spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", remarks)]
+    assert spills and max(spills) == 0, remarks[-2000:]
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)]
+    assert len(scratch) == len(spills) and max(scratch) == 0, remarks[-2000:]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
