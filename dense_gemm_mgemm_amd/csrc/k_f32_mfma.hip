@@ -268,11 +268,17 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
     static_assert(NT % AK == 0 && NT % BNV == 0, "loads must tile the slice");
     static_assert(LAY == 0 || (VA == 4 && VB == 4 && !TAIL && !SK), "layout forms are 16-byte only");
     // Form 1: B' column n = b_nj + r*B_NRS, k = b_k4..b_k4+3 of the slice.
-    // Form 2: A' row k = a_kj + r*A_KRS, m = a_m4..a_m4+3 of the tile.
+    // Form 2: sixteen lanes cover 64 consecutive m of one K row of A' (256
+    // contiguous bytes); load r of thread t is unit U = t/16 + r*NT/16, K row
+    // U % BK, m = 64*(U / BK) + 4*(t % 16) .. +3.  In LDS element (m, k) sits
+    // at column k ^ 4*((m >> 3) & 7) of row m: aligned groups of four k stay
+    // together (the MFMA loop reads them as one 16-byte read, of eight lanes
+    // with the same m >> 3: still conflict-free), and the scattered writes of
+    // a wave spread over the banks (at most two lanes per bank instead of 32).
     constexpr int BKV = BK / 4, B_NRS = NT / BKV;
-    constexpr int AMV = BM / 4, A_KRS = NT / AMV;
     static_assert(LAY != 1 || (NT % BKV == 0 && LB * B_NRS == BN), "form 1 must tile the slice");
-    static_assert(LAY != 2 || (NT % AMV == 0 && LA * A_KRS == BK), "form 2 must tile the slice");
+    static_assert(LAY != 2 || ((NT / 16) * LA == BK * (BM / 64) && BK == 32),
+                  "form 2 must tile the slice");
 
     f32x16 acc[TM][TN];
     // Thread-chunk c of the accumulators: 4 consecutive values of one MFMA
@@ -327,14 +333,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
         const float* a_src[WIDE ? LA : 1];
         const float* b_src[WIDE ? LB : 1];
         const int b_nj = tid / BKV, b_k4 = (tid % BKV) * 4;
-        const int a_kj = tid / AMV, a_m4 = (tid % AMV) * 4;
+        auto amc_k = [&](int r) { return ((tid >> 4) + r * (NT / 16)) % BK; };
+        auto amc_m = [&](int r) { return 64 * (((tid >> 4) + r * (NT / 16)) / BK) + 4 * (tid & 15); };
         if constexpr (WIDE) {
             if constexpr (LAY == 2) {
                 // Columns past M read the last valid 4-float chunk (M % 4 == 0).
-                const int a_mm = a_m4 + 4 <= mlim ? a_m4 : mlim - 4;
 #pragma unroll
-                for (int r = 0; r < LA; ++r)
-                    a_src[r] = A + (int64_t)(a_kj + r * A_KRS) * p.lda + m0 + a_mm;
+                for (int r = 0; r < LA; ++r) {
+                    const int m = amc_m(r), mm = m + 4 <= mlim ? m : mlim - 4;
+                    a_src[r] = A + (int64_t)amc_k(r) * p.lda + m0 + mm;
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < LA; ++r) a_src[r] = a_ptr(r);
@@ -395,10 +403,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
         auto stash = [&](int slot) {
             if constexpr (LAY == 2) {
 #pragma unroll
-                for (int r = 0; r < LA; ++r)
+                for (int r = 0; r < LA; ++r) {
+                    const int m = amc_m(r), kk = amc_k(r) ^ (4 * ((m >> 3) & 7));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        As[slot][(a_m4 + e) * AROW + a_kj + r * A_KRS] = lane_of<VA>(ra[r], e);
+                    for (int e = 0; e < 4; ++e) As[slot][(m + e) * AROW + kk] = lane_of<VA>(ra[r], e);
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < LA; ++r) *(TA*)(&As[slot][(a_mi0 + r * A_RS) * AROW + a_kc]) = ra[r];
@@ -434,13 +443,21 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
         for (int64_t kt = k0; kt < k1; ++kt) {
             const int cur = (int)((kt - k0) & 1);
             if (kt + 1 < k1) load(kt + 1);
-            const float* as = &As[cur][(wm * WTM + lcol) * AROW + lrow * HALF];
+            const float* as = &As[cur][(wm * WTM + lcol) * AROW + (LAY == 2 ? 0 : lrow * HALF)];
             const float* bs = &Bs[cur][(lrow * HALF) * BROW + wn * WTN + lcol];
 #pragma unroll
             for (int s0 = 0; s0 < HALF; s0 += 4) {
                 f32x4v a4[TM];
 #pragma unroll
-                for (int i = 0; i < TM; ++i) a4[i] = *(const f32x4v*)(as + i * 32 * AROW + s0);
+                for (int i = 0; i < TM; ++i) {
+                    if constexpr (LAY == 2) {
+                        // Row m = wm*WTM + lcol + 32i: its swizzle 4*((m >> 3) & 7).
+                        const int sw = 4 * ((((wm * WTM + lcol) >> 3) + 4 * i) & 7);
+                        a4[i] = *(const f32x4v*)(as + i * 32 * AROW + ((lrow * HALF + s0) ^ sw));
+                    } else {
+                        a4[i] = *(const f32x4v*)(as + i * 32 * AROW + s0);
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     float b[TN];
