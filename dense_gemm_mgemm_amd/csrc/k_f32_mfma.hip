@@ -579,6 +579,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_f32_fast(Problem p, SKArg
 struct BigCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 4, WN = 4, OCC = 1; };
 struct SmallCfg { static constexpr int BM = 128, BN = 128, BK = 16, WM = 2, WN = 2, OCC = 2; };
 struct UnalignedCfg { static constexpr int BM = 256, BN = 256, BK = 32, WM = 2, WN = 4, OCC = 1; };
+// Stream-K tiles for short M (M <= 32, 64, 128): 32, 64 or 128 rows by 256
+// columns on 4, 8 or 8 waves, so that a few rows do not pay for 256 rows of
+// MFMA work; the K shares then stream B with one workgroup per CU.
+struct SkinnyCfg32 { static constexpr int BM = 32, BN = 256, BK = 32, WM = 1, WN = 4, OCC = 1; };
+struct SkinnyCfg64 { static constexpr int BM = 64, BN = 256, BK = 32, WM = 2, WN = 4, OCC = 1; };
+struct SkinnyCfg128 { static constexpr int BM = 128, BN = 256, BK = 32, WM = 2, WN = 4, OCC = 1; };
 
 // Operand form of the 16-byte kernels (the LAY parameter), -1 if none.
 int fast_layout(const Problem& p) {
@@ -680,11 +686,16 @@ hipError_t launch_f32_unaligned(const Problem& p, hipStream_t s) {
     return fast_launch<U, 1, 2, true>(p, s);           // (1, 1) is declined by the supports check
 }
 
-bool f32_sk_fits(const Problem& p, const Workspace& ws) { return sk_fits<UnalignedCfg>(p, ws); }
+bool f32_sk_fits(const Problem& p, const Workspace& ws) {
+    if (p.M <= 32) return sk_fits<SkinnyCfg32>(p, ws);
+    if (p.M <= 64) return sk_fits<SkinnyCfg64>(p, ws);
+    if (p.M <= 128) return sk_fits<SkinnyCfg128>(p, ws);
+    return sk_fits<UnalignedCfg>(p, ws);
+}
 
-hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
+template <class U>
+hipError_t sk_launch_loads(const Problem& p, const Workspace& ws, hipStream_t s) {
     const int va = unaligned_va(p), vb = unaligned_vb(p);
-    using U = UnalignedCfg;
     if (va == 4) {
         if (vb == 4) return sk_launch<U, 4, 4, true>(p, ws, s);
         if (vb == 2) return sk_launch<U, 4, 2, true>(p, ws, s);
@@ -692,6 +703,13 @@ hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
     }
     if (vb == 4) return sk_launch<U, 1, 4, true>(p, ws, s);
     return sk_launch<U, 1, 2, true>(p, ws, s);
+}
+
+hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s) {
+    if (p.M <= 32) return sk_launch_loads<SkinnyCfg32>(p, ws, s);
+    if (p.M <= 64) return sk_launch_loads<SkinnyCfg64>(p, ws, s);
+    if (p.M <= 128) return sk_launch_loads<SkinnyCfg128>(p, ws, s);
+    return sk_launch_loads<UnalignedCfg>(p, ws, s);
 }
 
 }  // namespace mgemm

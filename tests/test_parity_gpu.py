@@ -199,7 +199,11 @@ def test_sgemm_4096_mixed_layouts_sampled(h, la, lb):
 # bits.  (M, N, K, lda, ldb, ldc)
 STREAM_K_F32 = [(1000, 6000, 700, 701, 6002, 6000), (512, 4096, 1024, 1024, 4096, 4096),
                 (200, 200, 5000, 5001, 202, 200), (300, 514, 100, 101, 514, 514),
-                (2048, 2304, 96, 96, 2304, 2304)]
+                (2048, 2304, 96, 96, 2304, 2304),
+                # Short M: 32- and 64-row stream-K tiles.
+                (1, 3000, 1000, 1000, 3000, 3000), (17, 1030, 700, 701, 1030, 1030),
+                (40, 2048, 512, 512, 2048, 2048), (64, 12288, 4096, 4096, 12288, 12288),
+                (100, 2600, 800, 801, 2600, 2600)]
 
 
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc", STREAM_K_F32)
