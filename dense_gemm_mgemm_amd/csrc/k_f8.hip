@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(int64_t M, int64_t K, const 
 // the registers, so the row crosses HBM once and each thread waits for one
 // round of loads (rows of up to 16384 16-bit or 8192 FP32 elements).
 template <int XT, int R>
-__global__ __launch_bounds__(256) void k_quant_rows_reg(int64_t M, int64_t K, const void* X,
+__global__ __launch_bounds__(256) void k_quant_rows_reg(int64_t /*M: one workgroup per row*/, int64_t K, const void* X,
                                                         int64_t ldx, uint8_t* Q, int64_t ldq,
                                                         float* scales) {
     constexpr int ES = XT == F32 ? 4 : 2;
