@@ -291,14 +291,16 @@ bool h_pp_supports(const Problem& p);
 // request for at most `requested` turns into (whole 32-slices per range; 1
 // for requests <= 1), 0 when the partials would not fit the workspace.
 constexpr int MAX_KSPLIT = 32;
-int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws);
-hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s);
+int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws,
+                 int bm = 256);
+hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s,
+                        int bm = 256);
 bool h_gated_supports(const Problem& p);
 hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s);
 bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s);
-bool h_dma_supports(const Problem& p, int bn);
+bool h_dma_supports(const Problem& p, int bn, int bm = 256);
 // FP8 E4M3: per-row quantisation of an M x K matrix of xtype (codes Q with
 // row stride ldq, FP32 dequantisation scales), and the FP8 GEMM on codes:
 // p.A = A codes (M x K, stride lda), p.B = B codes one output column per row

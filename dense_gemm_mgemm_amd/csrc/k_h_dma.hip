@@ -83,26 +83,31 @@ struct HSplit {
 #ifndef MGEMM_DMA_SLOTS
 #define MGEMM_DMA_SLOTS 4
 #endif
-constexpr int BM = 256, BK = 32, NT = 256;
+constexpr int BK = 32, NT = 256;
 constexpr int SLOTS = MGEMM_DMA_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
-constexpr int A_ROW = BK * 2, A_BYTES = BM * A_ROW;         // 16 KiB
-constexpr int A_COPIES = 4;                                 // 1 KiB A copies per wave per slice
+constexpr int A_ROW = BK * 2;                               // bytes per A row of a slice
 
 // BN is the width of the B slot.  The plain GEMM lays its four waves out 2x2
 // (128 rows x BN/2 columns each).  The gated pair (DUAL) fills the 192-wide
 // slot with 96 columns of each of two B matrices and lays the waves out 4x1
 // (64 rows x all 192 columns each), so that every wave holds the G and U
 // blocks of the same outputs in matching registers.
-template <int BN, bool DUAL>
+// BMT = 128 halves the tile height for short M (the four waves then hold
+// 64 x BN/2 each): a 128-row problem no longer pays for 256 rows of MFMA work.
+template <int BN, bool DUAL, int BMT = 256>
 struct Cfg {
     static_assert(BN == 256 || BN == 192, "tile width");
     static_assert(!DUAL || BN == 192, "the gated pair uses the 192-wide slot");
+    static_assert(BMT == 256 || (BMT == 128 && !DUAL), "tile height");
+    static constexpr int BM = BMT;
+    static constexpr int A_BYTES = BM * A_ROW;              // 16 or 8 KiB
+    static constexpr int A_COPIES = BM / 64;                // 1 KiB A copies per wave per slice
     static constexpr int B_ROW = BN * 2, B_CHUNKS = BN / 8;
     static constexpr int B_BYTES = BK * B_ROW;
     static constexpr int B_COPIES = B_BYTES / 1024 / 4;     // per wave per slice
     static constexpr int COPIES = A_COPIES + B_COPIES;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-    static constexpr int WROWS = DUAL ? 64 : 128;           // rows per wave
+    static constexpr int WROWS = DUAL ? 64 : BM / 2;        // rows per wave
     static constexpr int TM = WROWS / 32;                   // 32-row blocks per wave
     static constexpr int TN = DUAL ? BN / 32 : BN / 64;     // 32-column blocks per wave
     static constexpr int WN = DUAL ? 0 : BN / 2;            // column offset of wave column 1
@@ -171,10 +176,12 @@ struct Frags {
 // AMC: A' M-contiguous (a column-major A times a row-major B, after the
 // transpose identity).  The A slot then holds 32 K-rows of 512 bytes staged
 // and read exactly like the 256-wide B slot (chunk swizzle, transposed reads).
-template <int DT, int BN, bool DUAL, int EPI, bool BKC = false, bool AMC = false>
+template <int DT, int BN, bool DUAL, int EPI, bool BKC = false, bool AMC = false, int BMT = 256>
 __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
-    using G = Cfg<BN, DUAL>;
+    using G = Cfg<BN, DUAL, BMT>;
     static_assert(!(BKC && DUAL) && !(AMC && DUAL) && !(AMC && BKC), "operand forms");
+    static_assert(!AMC || BMT == 256, "the M-contiguous A slot is 256 wide");
+    constexpr int BM = G::BM, A_BYTES = G::A_BYTES, A_COPIES = G::A_COPIES;
     constexpr int TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
     constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
     using Fr = Frags<TM, TN>;
@@ -223,11 +230,11 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     } else {
 #pragma unroll
     for (int i = 0; i < A_COPIES; ++i) {
-        const int r = 64 * wave + 16 * i + (lane >> 2);
+        const int r = (BM / 4) * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ a_swz(r);
         const int rr = r < mlim ? r : mlim - 1;
         src[i] = A + (m0 + rr) * p.lda + (int64_t)j0 * BK + 8 * c;
-        dst[i] = (64 * wave + 16 * i) * A_ROW;
+        dst[i] = ((BM / 4) * wave + 16 * i) * A_ROW;
     }
     }
     if constexpr (BKC) {
@@ -473,9 +480,10 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
 // accumulators (the chunk and thread of the first phase), sums the K ranges in
 // range order and stores four outputs as the one-phase epilogue would.  The
 // gated pair's threads take a G chunk and the U chunk of the same outputs.
-template <int DT, int BN, bool DUAL, int EPI>
+template <int DT, int BN, bool DUAL, int EPI, int BMT = 256>
 __global__ __launch_bounds__(NT) void k_h_dma_reduce(Problem p, HSplit sp) {
-    using G = Cfg<BN, DUAL>;
+    using G = Cfg<BN, DUAL, BMT>;
+    constexpr int BM = G::BM;
     constexpr int TM = G::TM, TN = G::TN, OUT = G::OUT;
     constexpr int TNO = DUAL ? TN / 2 : TN;                 // blocks that hold outputs
     constexpr int CH = TM * TNO * 4;                        // chunks walked per tile
@@ -523,30 +531,32 @@ __global__ __launch_bounds__(NT) void k_h_dma_reduce(Problem p, HSplit sp) {
     }
 }
 
-template <int BN, bool DUAL>
+template <int BN, bool DUAL, int BMT = 256>
 constexpr int64_t tile_part_bytes() {
-    return (int64_t)NT * Cfg<BN, DUAL>::TM * Cfg<BN, DUAL>::TN * 16 * (int64_t)sizeof(float);
+    using G = Cfg<BN, DUAL, BMT>;
+    return (int64_t)NT * G::TM * G::TN * 16 * (int64_t)sizeof(float);
 }
 
-template <int DT, int BN, bool DUAL, int EPI, bool BKC, bool AMC>
+template <int DT, int BN, bool DUAL, int EPI, bool BKC, bool AMC, int BMT>
 hipError_t launch_epi(const Problem& p, const HSplit& sp, hipStream_t s) {
-    auto kern = k_h_dma<DT, BN, DUAL, EPI, BKC, AMC>;
-    const size_t lds = (size_t)SLOTS * Cfg<BN, DUAL>::SLOT_BYTES;
+    using G = Cfg<BN, DUAL, BMT>;
+    auto kern = k_h_dma<DT, BN, DUAL, EPI, BKC, AMC, BMT>;
+    const size_t lds = (size_t)SLOTS * G::SLOT_BYTES;
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
         return e;
-    constexpr int OUT = Cfg<BN, DUAL>::OUT;
+    constexpr int OUT = G::OUT, BM = G::BM;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + OUT - 1) / OUT);
     hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * sp.ksplit)), dim3(NT), lds, s, p, sp);
     return hipGetLastError();
 }
 
-template <int DT, int BN, bool DUAL, int EPI>
+template <int DT, int BN, bool DUAL, int EPI, int BMT>
 hipError_t launch_reduce(const Problem& p, const HSplit& sp, hipStream_t s) {
-    using G = Cfg<BN, DUAL>;
+    using G = Cfg<BN, DUAL, BMT>;
     constexpr int CH = G::TM * (DUAL ? G::TN / 2 : G::TN) * 4;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + G::OUT - 1) / G::OUT);
-    hipLaunchKernelGGL((k_h_dma_reduce<DT, BN, DUAL, EPI>), dim3((unsigned)(tiles * CH)), dim3(NT), 0,
+    const int64_t tiles = ((p.M + G::BM - 1) / G::BM) * ((p.N + G::OUT - 1) / G::OUT);
+    hipLaunchKernelGGL((k_h_dma_reduce<DT, BN, DUAL, EPI, BMT>), dim3((unsigned)(tiles * CH)), dim3(NT), 0,
                        s, p, sp);
     return hipGetLastError();
 }
@@ -554,29 +564,30 @@ hipError_t launch_reduce(const Problem& p, const HSplit& sp, hipStream_t s) {
 // One kernel per epilogue: the store loop is unrolled over every output of
 // the tile, so a runtime choice would put the activation's code between the
 // plain stores (and the 256-wide tile has no registers to spare for it).
-template <int DT, int BN, bool DUAL, bool BKC = false, bool AMC = false>
+template <int DT, int BN, bool DUAL, bool BKC = false, bool AMC = false, int BMT = 256>
 hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
     const int nk = (int)(p.K / BK);
     HSplit sp{(float*)ws.part, 1, nk};
     const bool silu = !DUAL && p.epilogue == EPI_SILU;
     if (ksplit <= 1) {
         if constexpr (!DUAL)
-            if (silu) return launch_epi<DT, BN, false, EPI_SILU, BKC, AMC>(p, sp, s);
-        return launch_epi<DT, BN, DUAL, EPI_NONE, BKC, AMC>(p, sp, s);
+            if (silu) return launch_epi<DT, BN, false, EPI_SILU, BKC, AMC, BMT>(p, sp, s);
+        return launch_epi<DT, BN, DUAL, EPI_NONE, BKC, AMC, BMT>(p, sp, s);
     }
     sp.nks = (nk + ksplit - 1) / ksplit;
     sp.ksplit = (nk + sp.nks - 1) / sp.nks;
-    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL, BKC, AMC>(p, sp, s);
+    hipError_t e = launch_epi<DT, BN, DUAL, EPI_PARTIAL, BKC, AMC, BMT>(p, sp, s);
     if (e != hipSuccess) return e;
     if constexpr (!DUAL)
-        if (silu) return launch_reduce<DT, BN, false, EPI_SILU>(p, sp, s);
-    return launch_reduce<DT, BN, DUAL, EPI_NONE>(p, sp, s);
+        if (silu) return launch_reduce<DT, BN, false, EPI_SILU, BMT>(p, sp, s);
+    return launch_reduce<DT, BN, DUAL, EPI_NONE, BMT>(p, sp, s);
 }
 
 }  // namespace
 
-bool h_dma_supports(const Problem& p, int bn) {
+bool h_dma_supports(const Problem& p, int bn, int bm) {
     if (bn != 256 && bn != 192) return false;
+    if (bm != 256 && (bm != 128 || bn != 192 || !p.a_kc)) return false;   // 128 rows: 128x192, A' K-contiguous
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (!p.a_kc && p.b_kc) return false;
     // N-contiguous B' rows (M-contiguous A' columns) are read as 8-element
@@ -585,15 +596,16 @@ bool h_dma_supports(const Problem& p, int bn) {
     if (!p.a_kc && p.M % 8 != 0) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
+    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
     return tiles > 0 && tiles <= 0x7fffffff / 64;
 }
 
-int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws) {
+int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Workspace& ws, int bm) {
     const int out = dual ? 96 : bn;
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + out - 1) / out);
+    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + out - 1) / out);
     const int64_t nk = p.K / BK;
-    const int64_t tile_bytes = bn == 256 ? tile_part_bytes<256, false>() : tile_part_bytes<192, false>();
+    const int64_t tile_bytes = bm == 128 ? tile_part_bytes<192, false, 128>()
+                               : (bn == 256 ? tile_part_bytes<256, false>() : tile_part_bytes<192, false>());
     if (requested <= 1 || nk < 2) return 1;
     int64_t ks = requested < nk ? requested : nk;
     const int64_t nks = (nk + ks - 1) / ks;                 // whole slices per range
@@ -602,7 +614,15 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
     return (int)ks;
 }
 
-hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s) {
+hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s,
+                        int bm) {
+    if (bm == 128) {
+        if (p.b_kc)
+            return p.dtype == F16 ? launch_dt<F16, 192, false, true, false, 128>(p, ksplit, ws, s)
+                                  : launch_dt<BF16, 192, false, true, false, 128>(p, ksplit, ws, s);
+        return p.dtype == F16 ? launch_dt<F16, 192, false, false, false, 128>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 192, false, false, false, 128>(p, ksplit, ws, s);
+    }
     if (!p.a_kc) {
         if (bn == 192)
             return p.dtype == F16 ? launch_dt<F16, 192, false, false, true>(p, ksplit, ws, s)

@@ -81,6 +81,7 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
     case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p, 256);
     case MGEMM_KERNEL_H_DMA_192: return mgemm::h_dma_supports(p, 192);
+    case MGEMM_KERNEL_H_DMA_128: return mgemm::h_dma_supports(p, 192, 128);
     case MGEMM_KERNEL_F32_FAST_U: return mgemm::f32_unaligned_supports(p);
     case MGEMM_KERNEL_F32_SK: return mgemm::f32_unaligned_supports(p);
     case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_supports(p);
@@ -115,17 +116,18 @@ double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int
 // Split of K with the smallest predicted time for the direct-to-LDS kernel
 // (tile width bn; the gated pair's tile holds 96 output columns), among the
 // splits that fit the workspace.
-int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, double* t_out) {
+int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, double* t_out,
+               int bm = 256) {
     const double speed = bn == 256 ? 1.4 : 1.3;
     const int out_n = dual ? 96 : bn;
     int best = 1;
-    double best_t = predict_us(p, 256, bn, out_n, speed, 1, 1);
+    double best_t = predict_us(p, bm, bn, out_n, speed, 1, 1);
     int last = 1;
     for (int req = 2; req <= mgemm::MAX_KSPLIT; ++req) {
-        const int ks = mgemm::h_dma_splits(p, bn, dual, req, ws);
+        const int ks = mgemm::h_dma_splits(p, bn, dual, req, ws, bm);
         if (ks <= last) continue;          // same number of ranges as a smaller request
         last = ks;
-        const double t = predict_us(p, 256, bn, out_n, speed, 1, ks);
+        const double t = predict_us(p, bm, bn, out_n, speed, 1, ks);
         if (t < best_t) { best_t = t; best = ks; }
     }
     if (t_out) *t_out = best_t;
@@ -191,6 +193,15 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         const int ks = auto_split(p, bn, false, ws, &t);
         if (t < best_t) { best_t = t; best = {bn == 256 ? MGEMM_KERNEL_H_DMA_256 : MGEMM_KERNEL_H_DMA_192, ks}; }
     }
+    // 128-row tiles for M <= 128 only: measured on BF16 x W[4096 x 12288] they
+    // win at M = 96 / 128 (33.5 / 36.5 us against 38.3 / 40.8) and lose from
+    // M = 192 on (45.3 against 44.1 us), where the model alone would still
+    // pick them.
+    if (p.M <= 128 && mgemm::h_dma_supports(p, 192, 128)) {
+        double t;
+        const int ks = auto_split(p, 192, false, ws, &t, 128);
+        if (t < best_t) { best_t = t; best = {MGEMM_KERNEL_H_DMA_128, ks}; }
+    }
     // Register-staged kernels (any layout); two 128x128 workgroups share a CU
     // and together run at 0.8 of the 256x256 rate (2048^3 BF16: 43.9 us).
     struct Cand { mgemm_kernel_t k; int bm, bn, per_cu; double speed; };
@@ -206,7 +217,8 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
 }
 
 bool splittable(mgemm_kernel_t k) {
-    return k == MGEMM_KERNEL_H_DMA_256 || k == MGEMM_KERNEL_H_DMA_192 || k == MGEMM_KERNEL_SKINNY_SK;
+    return k == MGEMM_KERNEL_H_DMA_256 || k == MGEMM_KERNEL_H_DMA_192 || k == MGEMM_KERNEL_H_DMA_128 ||
+           k == MGEMM_KERNEL_SKINNY_SK;
 }
 
 // Number of K ranges a forced variant runs with (0: it cannot run them).
@@ -218,6 +230,9 @@ int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k
     case MGEMM_KERNEL_H_DMA_192:
         return requested == 0 ? auto_split(p, 192, false, ws, nullptr)
                               : mgemm::h_dma_splits(p, 192, false, requested, ws);
+    case MGEMM_KERNEL_H_DMA_128:
+        return requested == 0 ? auto_split(p, 192, false, ws, nullptr, 128)
+                              : mgemm::h_dma_splits(p, 192, false, requested, ws, 128);
     case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_splits(p, ws, requested);
     case MGEMM_KERNEL_F32_SK: return requested <= 1 && mgemm::f32_sk_fits(p, ws) ? 1 : 0;
     default: return requested <= 1 ? 1 : 0;
@@ -256,6 +271,7 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t 
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
     case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, c.ksplit, h->ws, s); break;
     case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, c.ksplit, h->ws, s); break;
+    case MGEMM_KERNEL_H_DMA_128: e = mgemm::launch_h_dma(p, 192, c.ksplit, h->ws, s, 128); break;
     case MGEMM_KERNEL_F32_FAST_U: e = mgemm::launch_f32_unaligned(p, s); break;
     case MGEMM_KERNEL_F32_SK: e = mgemm::launch_f32_sk(p, h->ws, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
@@ -576,6 +592,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_F8_GENERAL: return "f8_general";
     case MGEMM_KERNEL_F8_MFMA_192: return "f8_mfma_256x192";
     case MGEMM_KERNEL_F32_SK: return "f32_sk";
+    case MGEMM_KERNEL_H_DMA_128: return "h_dma_128x192";
     default: return "unknown";
     }
 }

@@ -77,7 +77,9 @@ typedef enum {
     MGEMM_KERNEL_F8_MFMA_192 = 16, /* FP8 codes (mgemm_run_fp8 only): 256x192 tiles, f8f6f4 MFMA */
     MGEMM_KERNEL_F32_SK = 17,    /* FP32 NN as F32_FAST_U, stream-K: one workgroup per CU, equal
                                     shares of all (tile, K slice) pairs, deterministic fix-up */
-    MGEMM_KERNEL_COUNT = 18
+    MGEMM_KERNEL_H_DMA_128 = 18, /* FP16/BF16, A' K-contiguous (row-major A), 128x192 tiles, 4 waves
+                                    of 64x96, direct-to-LDS ring (short M) */
+    MGEMM_KERNEL_COUNT = 19
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */

@@ -25,7 +25,7 @@ CANARY = {"f32": 0x7FA5A5A5, "f16": 0x7E5A, "bf16": 0x7FA5}
 
 KERNELS_F32 = ["general", "f32_mfma", "f32_fast", "f32_fast_128", "f32_fast_u", "f32_sk"]
 KERNELS_16 = ["general", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128", "h_pp_256x256",
-              "h_dma_256x256", "h_dma_256x192"]
+              "h_dma_256x256", "h_dma_256x192", "h_dma_128x192"]
 
 
 def c_initial(case: Case, C0):

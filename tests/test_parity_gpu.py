@@ -384,14 +384,15 @@ def test_h_dma_split_k_bit_exact(h, M, N, K):
         case = W.Case("hsplit", M, N, K, dtype, kindA="int", kindB="int", kindC="int",
                       alpha=1.0, beta=-0.5, seeds=(M, N, K))
         inputs = case.make()
-        for kernel in ("h_dma_256x256", "h_dma_256x192"):
+        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192"):
             bn = 256 if kernel.endswith("256") else 192
-            tiles = -(-M // 256) * -(-N // bn)
+            bm = 128 if "_128x" in kernel else 256
+            tiles = -(-M // bm) * -(-N // bn)
             for ks in (1, 2, 3, 5, 8, 32):
                 say("h_dma split", dtype, (M, N, K), kernel, ks)
                 nk = K // 32
                 ranges = -(-nk // -(-nk // min(ks, nk)))
-                if tiles * ranges * 1024 * bn > WORKSPACE_BYTES:
+                if tiles * ranges * 4 * bm * bn > WORKSPACE_BYTES:
                     # The FP32 partials (256 x bn per tile and range) would
                     # not fit the handle's workspace: refused, nothing runs.
                     with pytest.raises(mg.MgemmError) as ei:
@@ -414,7 +415,7 @@ def test_h_dma_b_k_contiguous_bit_exact(h, M, N, K):
         case = W.Case("hbkc", M, N, K, dtype, layoutB="col", kindA="int", kindB="int",
                       kindC="int", alpha=1.0, beta=-0.5, seeds=(M, N, K + 1))
         inputs = case.make()
-        for kernel in ("h_dma_256x256", "h_dma_256x192"):
+        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192"):
             for ks in (1, 3):
                 say("h_dma B K-contiguous", dtype, (M, N, K), kernel, ks)
                 P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
