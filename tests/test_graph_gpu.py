@@ -63,6 +63,9 @@ GEMM_CASES = [
     (W.Case("graph_skinny", 16, 12288, 4096, "bf16", kindA="normal", kindB="normal",
             seeds=(24, 25, 26)), "skinny_sk", 4),
     (W.ffn_bf16(), "auto", 0),
+    (W.Case("graph_mid_m", 128, 12288, 4096, "bf16", kindA="normal", kindB="normal",
+            seeds=(27, 28, 29)), "h_dma_128x192", 4),
+    (W.Case("graph_sk_short_m", 16, 6000, 2000, "f32", lda=2001, seeds=(30, 31, 32)), "f32_sk", 1),
 ]
 
 
