@@ -44,7 +44,7 @@ KERNEL_SOURCE = {
     "h_mfma_256x192": "k_h_mfma.hip", "h_mfma_128x128": "k_h_mfma.hip",
     "h_pp_256x256": "k_h_pp.hip", "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
     "skinny_sk": "k_skinny_sk.hip", "h_dma_256x192": "k_h_dma.hip", "f32_fast_u": "k_f32_mfma.hip",
-    "h_dma_gated": "k_h_dma.hip", "fp8_quant+fp8_gemm": "k_f8.hip", "f32_sk": "k_f32_mfma.hip",
+    "h_dma_gated": "k_h_dma.hip", "fp8_quant+fp8_gemm": "k_f8.hip", "f32_sk": "k_f32_mfma.hip", "h_dma_128x192": "k_h_dma.hip",
 }
 
 
