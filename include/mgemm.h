@@ -197,8 +197,9 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
  * Runtime", section 5.2.4: the order of a floating-point sum changes its last
  * bits), so a given variant gives the same bits on every run; different
  * splits round differently (within the tolerance of the sum).
- * Only MGEMM_KERNEL_H_DMA_256, MGEMM_KERNEL_H_DMA_192 and
- * MGEMM_KERNEL_SKINNY_SK take ksplit > 1; the number of ranges used is
+ * Only MGEMM_KERNEL_H_DMA_256, MGEMM_KERNEL_H_DMA_192, MGEMM_KERNEL_H_DMA_128
+ * and MGEMM_KERNEL_SKINNY_SK take ksplit > 1 (MGEMM_KERNEL_F32_SK balances K
+ * itself and takes 0 or 1); the number of ranges used is
  * ceil(S / ceil(S / ksplit)) for S = K / 32 slices.  The direct-to-LDS kernels
  * then run in two launches on `stream` (partial products, then the sum and
  * the epilogue); the partials live in the handle's workspace.
