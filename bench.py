@@ -392,20 +392,25 @@ def cpu_baseline_fp8(case, out_dev, budget_s):
              "ok": bool(np.all(err <= tol))})
 
 
-def traffic_for(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources."""
+def counters_for(kernel, workload):
+    """The committed rocprofv3 counter summary of this kernel and workload, if
+    it was taken on the current kernel sources, else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        t = json.load(open(p))
-        e = t.get("%s/%s" % (kernel, workload))
+        e = json.load(open(p)).get("%s/%s" % (kernel, workload))
         if e and e.get("src_hash") == src_hash(kernel):
-            return e["bytes_per_launch"]
-    except (ValueError, KeyError):
+            return e
+    except ValueError:
         pass
     return None
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary (or None)."""
+    e = counters_for(kernel, workload)
+    return e.get("bytes_per_launch") if e else None
 
 
 def main():
@@ -477,6 +482,7 @@ def main():
                    if case.name == "sgemm_4096" else None},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "mfma_busy": (counters_for(r["kernel"], case.name) or {}).get("mfma_busy"),
                      "algorithmic_per_launch": flops if not hbm else nbytes,
                      "launch_ms_mean": round(r["launch_ms_mean"], 5),
                      "single_launch_ms_p10": round(r["launch_ms_p10"], 5),
@@ -507,6 +513,9 @@ def main():
             else:
                 tf = f2 / s / 1e12
                 ent.update(TFLOPs=round(tf, 2), frac_peak=round(tf / cm.PEAK_TFLOPS[peak_key(c)], 4))
+            cnt = counters_for(rr["kernel"], name)
+            if cnt:
+                ent.update(traffic=cnt.get("bytes_per_launch"), mfma_busy=cnt.get("mfma_busy"))
             others[name] = ent
             del rr
             torch.cuda.empty_cache()
