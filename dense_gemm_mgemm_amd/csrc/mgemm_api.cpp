@@ -199,11 +199,15 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         const int ks = auto_split(p, bn, false, ws, &t);
         if (t < best_t) { best_t = t; best = {bn == 256 ? MGEMM_KERNEL_H_DMA_256 : MGEMM_KERNEL_H_DMA_192, ks}; }
     }
-    // 128-row tiles for M <= 128 only: measured on BF16 x W[4096 x 12288] they
-    // win at M = 96 / 128 (33.5 / 36.5 us against 38.3 / 40.8) and lose from
-    // M = 192 on (45.3 against 44.1 us), where the model alone would still
-    // pick them.
-    if (p.M <= 128 && mgemm::h_dma_supports(p, 192, 128)) {
+    // 128-row tiles: each extra 128-row band streams B once more, so they are
+    // considered only for M <= 128 or a B small enough to be shared through
+    // the 256 MiB last-level cache (<= 32 MiB).  Measured (BF16): M = 96 / 128
+    // x W[4096 x 12288] 33.5 / 36.5 us against 38.3 / 40.8 on 256-row tiles,
+    // but M = 192 / 256 45.3 / 52.3 against 44.1 / 47.4 (W is 96 MiB); the
+    // FFN share 1024x1536x4096 25.9 against 28.6 us, 512x1024x2048 15.9
+    // against 19.4, 256x4096x4096 22.1 against 25.0.
+    const bool b_small = (double)p.K * (double)p.N * 2.0 <= 32.0 * 1024 * 1024;
+    if ((p.M <= 128 || b_small) && mgemm::h_dma_supports(p, 192, 128)) {
         double t;
         const int ks = auto_split(p, 192, false, ws, &t, 128);
         if (t < best_t) { best_t = t; best = {MGEMM_KERNEL_H_DMA_128, ks}; }
