@@ -296,7 +296,8 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
 hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s,
                         int bm = 256);
 bool h_gated_supports(const Problem& p);
-hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s);
+hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s,
+                          int bm = 256);
 bool skinny_sk_supports(const Problem& p);
 int skinny_sk_splits(const Problem& p, const Workspace& ws, int requested);
 hipError_t launch_skinny_sk(const Problem& p, const Workspace& ws, int ksplit, hipStream_t s);

@@ -98,7 +98,7 @@ template <int BN, bool DUAL, int BMT = 256>
 struct Cfg {
     static_assert(BN == 256 || BN == 192, "tile width");
     static_assert(!DUAL || BN == 192, "the gated pair uses the 192-wide slot");
-    static_assert(BMT == 256 || (BMT == 128 && !DUAL), "tile height");
+    static_assert(BMT == 256 || BMT == 128, "tile height");
     static constexpr int BM = BMT;
     static constexpr int A_BYTES = BM * A_ROW;              // 16 or 8 KiB
     static constexpr int A_COPIES = BM / 64;                // 1 KiB A copies per wave per slice
@@ -107,7 +107,7 @@ struct Cfg {
     static constexpr int B_COPIES = B_BYTES / 1024 / 4;     // per wave per slice
     static constexpr int COPIES = A_COPIES + B_COPIES;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-    static constexpr int WROWS = DUAL ? 64 : BM / 2;        // rows per wave
+    static constexpr int WROWS = DUAL ? BM / 4 : BM / 2;    // rows per wave
     static constexpr int TM = WROWS / 32;                   // 32-row blocks per wave
     static constexpr int TN = DUAL ? BN / 32 : BN / 64;     // 32-column blocks per wave
     static constexpr int WN = DUAL ? 0 : BN / 2;            // column offset of wave column 1
@@ -383,6 +383,20 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
             }
             fence_sched();
         }
+        // Tiles with fewer MFMAs per K-step than fragments to read (the
+        // 128-row gated pair: 1 x 6 blocks) issue the remaining reads here.
+        if constexpr (NM < TM + TN + 1) {
+            if (do_read) {
+                if (NM <= 1) read_a(nxt, rs, rks, 0);
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    if (2 + t >= NM) read_b(nxt, rs, rks, t);
+#pragma unroll
+                for (int m = 1; m < TM; ++m)
+                    if (1 + TN + m >= NM) read_a(nxt, rs, rks, m);
+            }
+            fence_sched();
+        }
     };
 
     const int nk_all = (int)(p.K / BK);
@@ -650,7 +664,10 @@ bool h_gated_supports(const Problem& p) {
     return ((uintptr_t)p.B2 & 15) == 0;
 }
 
-hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s) {
+hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s, int bm) {
+    if (bm == 128)
+        return p.dtype == F16 ? launch_dt<F16, 192, true, false, false, 128>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 192, true, false, false, 128>(p, ksplit, ws, s);
     return p.dtype == F16 ? launch_dt<F16, 192, true>(p, ksplit, ws, s)
                           : launch_dt<BF16, 192, true>(p, ksplit, ws, s);
 }

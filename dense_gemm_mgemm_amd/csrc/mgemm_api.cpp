@@ -437,10 +437,20 @@ mgemm_status_t mgemm_run_gated_ex(mgemm_handle_t h, int32_t ksplit, int64_t M, i
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
     if (!mgemm::h_gated_supports(p)) return MGEMM_ERR_UNSUPPORTED;
-    const int ks = ksplit == 0 ? auto_split(p, 192, true, h->ws, nullptr)
-                               : mgemm::h_dma_splits(p, 192, true, ksplit, h->ws);
+    // Tile height as for the plain product: 128-row tiles for M <= 128 or
+    // weights small enough (both of them) to be shared through the
+    // last-level cache, when the model predicts them faster.
+    int bm = 256;
+    if (p.M <= 128 || 2.0 * (double)p.K * (double)p.N * 2.0 <= 32.0 * 1024 * 1024) {
+        double t256, t128;
+        auto_split(p, 192, true, h->ws, &t256);
+        auto_split(p, 192, true, h->ws, &t128, 128);
+        if (t128 < t256) bm = 128;
+    }
+    const int ks = ksplit == 0 ? auto_split(p, 192, true, h->ws, nullptr, bm)
+                               : mgemm::h_dma_splits(p, 192, true, ksplit, h->ws, bm);
     if (ks < 1) return MGEMM_ERR_UNSUPPORTED;
-    hipError_t e = mgemm::launch_h_gated(p, ks, h->ws, stream);
+    hipError_t e = mgemm::launch_h_gated(p, ks, h->ws, stream, bm);
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
