@@ -21,7 +21,7 @@ MGEMM_SUCCESS, MGEMM_ERR_INVALID_ARG, MGEMM_ERR_UNSUPPORTED, MGEMM_ERR_HIP, MGEM
 MGEMM_ROW_MAJOR, MGEMM_COL_MAJOR = 0, 1
 MGEMM_F32, MGEMM_F16, MGEMM_BF16 = 0, 1, 2
 KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
-           "skinny", "h_pp_256x256", "f32_fast", "f32_fast_128",
+           "skinny", "reserved_7", "f32_fast", "f32_fast_128",
            "h_dma_256x256", "skinny_sk", "h_dma_256x192", "f32_fast_u",
            "f8_mfma_256x256", "f8_general", "f8_mfma_256x192", "f32_sk", "h_dma_128x192"]
 MGEMM_KERNEL_AUTO = 0

@@ -284,8 +284,6 @@ hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s);
 hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s);
 bool h_mfma_supports(const Problem& p, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
-hipError_t launch_h_pp(const Problem& p, hipStream_t s);
-bool h_pp_supports(const Problem& p);
 // Direct-to-LDS FP16/BF16 kernel.  ksplit > 1 cuts K into that many ranges
 // (two launches, partials in ws); h_dma_splits gives the number of ranges a
 // request for at most `requested` turns into (whole 32-slices per range; 1

@@ -36,7 +36,8 @@
 // published peak is out of reach and fewer stalls partly turn into a lower
 // clock.
 //
-// LDS layouts: A rows of 64 bytes with the XOR swizzle of k_h_pp.hip; B rows
+// LDS layouts: A rows of 64 bytes, chunk c of row r at chunk position
+// c ^ a_swz(r) with a_swz(r) = ((r >> 1) ^ (r >> 2)) & 3; B rows
 // of 2*BN bytes, chunk c of K-row k at chunk position pos(c, k): for BN = 256
 // c ^ {0,6,10,12}[k&3], for BN = 192 the 16-byte chunks are permuted inside
 // each 128-byte group by a 16-row XOR table.  Both are free of bank conflicts
@@ -147,8 +148,11 @@ __device__ __forceinline__ void wait_slices(int n) {
     else if (n == 2) wait_vm<2 * L>();
     else wait_vm<3 * L>();
 }
-// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l); see
-// k_h_pp.hip for why it is inline asm.
+// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l).
+// Issued through inline asm so that the compiler does not treat the LDS reads
+// that follow as dependent on it (it would otherwise wait for every copy in
+// flight before each such read); completion is tracked by hand with the vmcnt
+// waits of the schedule.
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(src), "s"(lds) : "memory", "m0");

@@ -54,7 +54,7 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
-    // See k_h_pp.hip: inline asm keeps the compiler from draining these
+    // Inline asm keeps the compiler from draining these
     // copies before LDS reads; completion is tracked with explicit vmcnt.
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(src), "s"(lds) : "memory", "m0");

@@ -76,7 +76,6 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_256x192:
     case MGEMM_KERNEL_H_128x128: return mgemm::h_mfma_supports(p, (int)k);
     case MGEMM_KERNEL_SKINNY: return mgemm::skinny_supports(p);
-    case MGEMM_KERNEL_H_PP_256: return mgemm::h_pp_supports(p);
     case MGEMM_KERNEL_F32_FAST: return mgemm::f32_fast_supports(p, true);
     case MGEMM_KERNEL_F32_FAST_128: return mgemm::f32_fast_supports(p, false);
     case MGEMM_KERNEL_H_DMA_256: return mgemm::h_dma_supports(p, 256);
@@ -276,7 +275,6 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t 
     case MGEMM_KERNEL_H_256x192:
     case MGEMM_KERNEL_H_128x128: e = mgemm::launch_h_mfma(p, (int)c.k, s); break;
     case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
-    case MGEMM_KERNEL_H_PP_256: e = mgemm::launch_h_pp(p, s); break;
     case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
     case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, c.ksplit, h->ws, s); break;
@@ -601,7 +599,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_H_256x192: return "h_mfma_256x192";
     case MGEMM_KERNEL_H_128x128: return "h_mfma_128x128";
     case MGEMM_KERNEL_SKINNY: return "skinny";
-    case MGEMM_KERNEL_H_PP_256: return "h_pp_256x256";
+    case MGEMM_KERNEL_RESERVED_7: return "reserved_7";
     case MGEMM_KERNEL_F32_FAST: return "f32_fast";
     case MGEMM_KERNEL_F32_FAST_128: return "f32_fast_128";
     case MGEMM_KERNEL_H_DMA_256: return "h_dma_256x256";

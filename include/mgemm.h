@@ -62,7 +62,8 @@ typedef enum {
     MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles */
     MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
     MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
-    MGEMM_KERNEL_H_PP_256 = 7,   /* FP16/BF16 NN, 256x256 tiles, 8-wave ping-pong, direct-to-LDS */
+    MGEMM_KERNEL_RESERVED_7 = 7, /* no longer built (an 8-wave variant that no shape chose);
+                                    forcing it returns MGEMM_ERR_UNSUPPORTED */
     MGEMM_KERNEL_F32_FAST = 8,   /* FP32 (any layout pair), 16-byte aligned operands, K % 32 == 0,
                                     256x256x32 tiles, 16 waves */
     MGEMM_KERNEL_F32_FAST_128 = 9, /* FP32 NN, 16-byte aligned operands, 128x128x16 tiles */
@@ -371,12 +372,15 @@ int32_t mgemm_weighted_choice(int32_t n_shapes, int32_t n_variants, const double
  * type xtype = F32, F16 or BF16, leading dimension ldx >= max(1, K)) into
  * codes Q (M x K bytes, row stride ldq >= max(1, K)) and FP32 dequantisation
  * scales (M floats): for each row, amax = largest |x| (NaN if the row holds
- * a NaN), scales[row] = amax / 448 and
- *     Q[row][k] = E4M3( (x * 448) / amax )
- * computed in FP32 (x * 448 exact, the division correctly rounded), rounded
- * to the nearest E4M3 value with ties to the even mantissa; magnitudes of 448
- * and above give 448, NaN gives 0x7F, the sign of zero is kept.  A row of
- * zeros gets scale 0 and keeps its signed zeros.  So X ~ decode(Q) * scales.
+ * a NaN), scales[row] = amax / 448 (FP32, one rounding), the row factor
+ * r = 448 / amax rounded once to FP32, and
+ *     Q[row][k] = E4M3( x * r )
+ * with the product x * r rounded to FP32 (round to nearest even), then to the
+ * nearest E4M3 value with ties to the even mantissa; magnitudes of 448 and
+ * above give 448, NaN gives 0x7F, the sign of zero is kept.  (Two roundings,
+ * of r and of x * r, so a code can differ by one step from E4M3(x*448/amax)
+ * evaluated exactly.)  A row of zeros gets scale 0 and keeps its signed
+ * zeros.  So X ~ decode(Q) * scales.
  * Device pointers; asynchronous on `stream`.
  * Errors: MGEMM_ERR_INVALID_ARG for negative sizes, a leading dimension or
  * row stride below K, an unknown xtype or a NULL pointer with M, K > 0.

@@ -108,9 +108,12 @@ def fp8_gemm(M, N, K, alpha, qa, lda, sa, qb, ldb, sb, beta=0.0, c0=None):
     + beta * c0 (M x N).  qa, qb: flat uint8 code buffers with row strides lda,
     ldb (qb holds one row of K codes per output column); sa, sb: float32.
 
-    Products of two E4M3 values are exact in FP64 and every partial sum of up
-    to 2^20 of them is too (they span at most 36 + 20 bits), so the K sum is
-    exact in any order; the scaling is one FP64 rounding more."""
+    A product of two E4M3 values is a multiple of 2^-18 below 2^18 (36
+    significant bits at most), so a partial sum of up to 2^17 of them needs at
+    most 53 bits and is exact in FP64: for K <= 2^17 the K sum is exact in any
+    order; the scaling is one FP64 rounding more.  Larger K is refused."""
+    if K > 2 ** 17:
+        raise ValueError("fp8_gemm: K = %d exceeds 2^17, where the FP64 sum stops being exact" % K)
     qa = np.asarray(qa, np.uint8)
     qb = np.asarray(qb, np.uint8)
     A = e4m3_decode(np.lib.stride_tricks.as_strided(qa, (M, K), (lda, 1))) if M and K else \

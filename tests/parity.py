@@ -6,8 +6,9 @@ Bars (the tolerance rules come with the workloads):
     oracle's (every partial sum is exact in FP32, so one rounding of the exact
     integer is the only answer);
   * FP32: max|C - C_exact| <= 1e-4 * sqrt(K/256) * max|C_exact|;
-  * FP16/BF16: per element |C - C_exact| <= 0.01*sqrt(K/512) + ulp(C_exact)/2,
-    the stated absolute bound plus the output format's own rounding;
+  * FP16/BF16: per element |C - C_exact| <= max(tol, ulp(C_exact)/2 + tol/8),
+    tol = 0.01*sqrt(K/512): the stated absolute bound, relaxed only where the
+    output format's own spacing makes it impossible to meet;
   * outside the logical M x N region (the ldc padding) C is never written.
 """
 from __future__ import annotations
@@ -18,25 +19,11 @@ import torch
 import dense_gemm_mgemm_amd as mg
 import oracle
 from dense_gemm_mgemm_amd.costmodel import tol_f32_rel, tol_half
-from workloads import Case, storage_view
-
-# Canary bit patterns written into C before a call (quiet NaNs).
-CANARY = {"f32": 0x7FA5A5A5, "f16": 0x7E5A, "bf16": 0x7FA5}
+from workloads import CANARY, Case, c_initial, storage_view
 
 KERNELS_F32 = ["general", "f32_mfma", "f32_fast", "f32_fast_128", "f32_fast_u", "f32_sk"]
-KERNELS_16 = ["general", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128", "h_pp_256x256",
+KERNELS_16 = ["general", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
               "h_dma_256x256", "h_dma_256x192", "h_dma_128x192"]
-
-
-def c_initial(case: Case, C0):
-    """Initial C buffer (CPU): C0 when beta != 0, else canary bits everywhere."""
-    if C0 is not None:
-        return C0.clone()
-    n = case.c_numel()
-    if case.dtype == "f32":
-        return torch.full((n,), CANARY["f32"], dtype=torch.int32).view(torch.float32)
-    t = torch.full((n,), CANARY[case.dtype], dtype=torch.int16)   # both patterns < 0x8000
-    return t.view(torch.float16 if case.dtype == "f16" else torch.bfloat16)
 
 
 def run_gpu(h, case: Case, kernel: str = "auto", inputs=None, stream=None, epilogue="none",
@@ -97,14 +84,24 @@ def compare(case: Case, got: np.ndarray, exact: np.ndarray) -> dict:
         ok = bool(np.all(err <= tol)) and not np.isnan(got).any()
         return {"ok": ok, "max_err": float(np.nanmax(err)) if err.size else 0.0, "tol": tol}
     tol = tol_half(case.K)
-    # Half an ulp of the output format at the exact value: the distance from
-    # the exact value to its rounding is at most that, and the bound allows it.
-    rounded = oracle.round_to(case.dtype, exact)
-    ulp = _ulp(case.dtype, rounded)
-    bound = tol + 0.5 * ulp
+    bound = half_bound(case.dtype, case.K, exact)
     ok = bool(np.all(err <= bound)) and not np.isnan(got).any()
     return {"ok": ok, "max_err": float(np.nanmax(err)) if err.size else 0.0, "tol": tol,
             "over_bare_tol": int(np.sum(err > tol))}
+
+
+def half_bound(dtype: str, K: int, exact: np.ndarray) -> np.ndarray:
+    """Per-element FP16/BF16 bound: max(tol, ulp/2 + tol/8), tol = 0.01*sqrt(K/512).
+
+    The stated absolute bound holds wherever the output format can meet it.
+    Where half the output spacing at the exact value comes within tol/8 of
+    tol or exceeds it (FP16 outputs of magnitude >= 64 at K = 2048, >= 128 at
+    K = 16384), no rounding of the exact value could meet the bare bound, and
+    the bound becomes that half spacing plus tol/8 for the FP32 accumulation
+    error (which stays below 1e-3 on every workload here)."""
+    tol = tol_half(K)
+    ulp = _ulp(dtype, oracle.round_to(dtype, exact))
+    return np.maximum(tol, 0.5 * ulp + tol / 8)
 
 
 def _ulp(dtype: str, x: np.ndarray) -> np.ndarray:
@@ -146,6 +143,98 @@ def check_tolerance(case: Case, A, B, C0, Cin, Cout, rows=None, cols=None):
     for r in reports:
         assert r["ok"], "%s: %s" % (case.name, r)
     return reports
+
+
+def exact_cols(case: Case, A, B, C0, cols) -> np.ndarray:
+    """Oracle values of whole logical columns of C, shape (M, len(cols)).
+
+    With one layout for A and B this is the transpose identity the oracle is
+    pinned to: the columns of C are the rows of C^T = B^T A^T, where B^T, A^T
+    and C^T are the same bytes read in the other storage order.  With mixed
+    layouts C^T would be stored in the wrong order, so the columns are summed
+    point by point instead."""
+    if case.layoutA != case.layoutB:
+        pi = np.repeat(np.arange(case.M), len(cols))
+        pj = np.tile(np.asarray(cols, np.int64), case.M)
+        v = oracle.gemm_points(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha,
+                               storage_view(A), case.lda, storage_view(B), case.ldb, case.beta,
+                               None if C0 is None else storage_view(C0), case.ldc, case.dtype,
+                               pi, pj)
+        return v.reshape(case.M, len(cols))
+    flip = {"row": "col", "col": "row"}
+    t = oracle.gemm(flip[case.layoutB], flip[case.layoutA], case.N, case.M, case.K, case.alpha,
+                    storage_view(B), case.ldb, storage_view(A), case.lda, case.beta,
+                    None if C0 is None else storage_view(C0), None, case.ldc, case.dtype,
+                    rows=np.asarray(cols, np.int64))
+    return t.T
+
+
+def boundary_lines(n: int, step: int = 64) -> list[int]:
+    """First and last index of every aligned block of `step` (every tile
+    boundary of every kernel here: all tile sizes are multiples of 64)."""
+    out = set()
+    for b in range(0, n, step):
+        out.update({b, min(b + step, n) - 1})
+    return sorted(out)
+
+
+def block_points(M: int, N: int, block: int = 64, per_block: int = 4, seed: int = 0):
+    """per_block random points inside every block x block block of an M x N
+    matrix (fewer only where a ragged block has fewer elements)."""
+    rng = np.random.default_rng(seed)
+    pi, pj = [], []
+    for b0 in range(0, M, block):
+        h = min(block, M - b0)
+        for c0 in range(0, N, block):
+            w = min(block, N - c0)
+            k = min(per_block, h * w)
+            flat = rng.choice(h * w, size=k, replace=False)
+            pi.append(b0 + flat // w)
+            pj.append(c0 + flat % w)
+    return np.concatenate(pi).astype(np.int64), np.concatenate(pj).astype(np.int64)
+
+
+def check_stratified(case: Case, A, B, C0, Cin, Cout, block: int = 64, per_block: int = 4,
+                     seed: int = 0) -> dict:
+    """Full-size check without the whole oracle product:
+      * no canary left anywhere in the logical C (beta == 0: C starts as NaN
+        canaries, so an output never written is found wherever it is), and the
+        ldc padding untouched;
+      * every row and every column on a 64-aligned block boundary (the first
+        and last row and column of every output tile of every kernel);
+      * per_block random points inside every 64 x 64 block of C.
+    Returns counts for the report (points, lines, 256 x 256 tiles reached)."""
+    got_bits = storage_view(Cout)
+    if C0 is None:
+        logical_bits = logical(case, got_bits)
+        left = int(np.count_nonzero(logical_bits == CANARY[case.dtype]))
+        assert left == 0, "%s: %d outputs were never written" % (case.name, left)
+    pad = padding_mask(case)
+    assert np.array_equal(got_bits[pad], storage_view(Cin)[pad]), "%s: wrote outside C" % case.name
+    got = logical(case, oracle.decode(case.dtype, got_bits))
+    a, b = storage_view(A), storage_view(B)
+    c0 = None if C0 is None else storage_view(C0)
+    rows = boundary_lines(case.M)
+    cols = boundary_lines(case.N)
+    reports = []
+    exact = oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
+                        case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
+                        rows=np.asarray(rows, np.int64))
+    reports.append(("rows", compare(case, got[rows], exact)))
+    reports.append(("cols", compare(case, got[:, cols], exact_cols(case, A, B, C0, cols))))
+    pi, pj = block_points(case.M, case.N, block, per_block, seed)
+    exact = oracle.gemm_points(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha,
+                               a, case.lda, b, case.ldb, case.beta, c0, case.ldc, case.dtype,
+                               pi, pj)
+    reports.append(("points", compare(case, got[pi, pj], exact)))
+    for what, r in reports:
+        assert r["ok"], "%s (%s): %s" % (case.name, what, r)
+    tiles = {(int(i) // 256, int(j) // 256) for i, j in zip(pi, pj)}
+    return {"points": int(pi.size), "rows": len(rows), "cols": len(cols),
+            "tiles_256_reached": len(tiles),
+            "tiles_256": ((case.M + 255) // 256) * ((case.N + 255) // 256),
+            "max_err": max(r["max_err"] for _, r in reports),
+            "over_bare_tol": sum(r.get("over_bare_tol", 0) for _, r in reports)}
 
 
 def sample_rows(M: int, tile: int = 256, extra: int = 16, seed: int = 0) -> list[int]:

@@ -39,7 +39,7 @@ def device_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_h_dma.hip", "k_skinny_sk.hip",
+@pytest.mark.parametrize("name", ["k_skinny.hip", "k_h_dma.hip", "k_skinny_sk.hip",
                                   "k_f8.hip"])
 def test_m0_only_written_by_our_copies(name, tmp_path):
     text = device_asm(os.path.join(CSRC, name), tmp_path)
@@ -59,7 +59,7 @@ def test_m0_only_written_by_our_copies(name, tmp_path):
 # VGPRs outside the main loop.  Scratch memory also appears when a store loop
 # over the accumulators is too large to unroll fully (the array then lives in
 # memory), so the per-lane scratch size must be zero as well.
-@pytest.mark.parametrize("name", ["k_h_pp.hip", "k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip",
+@pytest.mark.parametrize("name", ["k_skinny.hip", "k_f32_mfma.hip", "k_skinny_sk.hip",
                                   "k_h_dma.hip", "k_general.hip", "k_f8.hip", "k_util.hip"])
 def test_no_register_spills(name, tmp_path):
     remarks = device_build(name, tmp_path)[1]

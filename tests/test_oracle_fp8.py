@@ -119,6 +119,31 @@ def check_fp8_gemm_closed_forms():
     assert np.array_equal(c3, -1.5 * sa[:, None].astype(np.float64) * sb[None, :])
 
 
+def check_fp8_gemm_exact_at_its_limit():
+    # The K sum is exact up to K = 2^17: the widest products (448^2, near
+    # 2^17.6) and the narrowest (2^-9 * 2^-9 = 2^-18) mixed in one row, compared
+    # with the exact integer sum of the products scaled by 2^18; K = 2^17 + 1
+    # is refused.
+    K = 2 ** 17
+    rng = np.random.default_rng(17)
+    big = rng.random(K) < 0.5
+    va = np.where(big, 448.0, 2.0 ** -9) * np.where(rng.random(K) < 0.5, -1.0, 1.0)
+    vb = np.where(big, 448.0, 2.0 ** -9)
+    qa, qb = fp8.e4m3_encode(va), fp8.e4m3_encode(vb)
+    assert np.array_equal(fp8.e4m3_decode(qa), va) and np.array_equal(fp8.e4m3_decode(qb), vb)
+    one = np.ones(1, np.float32)
+    c = fp8.fp8_gemm(1, 1, K, 1.0, qa, K, one, qb, K, one)
+    exact = sum(int(a * b * 2 ** 18) for a, b in zip(va.tolist(), vb.tolist()))
+    assert c[0, 0] == exact / 2 ** 18
+    try:
+        fp8.fp8_gemm(1, 1, K + 1, 1.0, np.zeros(K + 1, np.uint8), K + 1, one,
+                     np.zeros(K + 1, np.uint8), K + 1, one)
+        refused = False
+    except ValueError:
+        refused = True
+    assert refused, "K = 2^17 + 1 must be refused"
+
+
 def check_quant_traffic_example():
     ex = GOLD["fp8_quant_traffic"]
     sep = ex["A_fp16_mib"] + ex["A_fp8_mib"] + ex["col_blocks"] * ex["A_fp8_mib"]
@@ -132,7 +157,8 @@ def check_quant_traffic_example():
 
 
 FP8_PINS = [check_format, check_encode_against_library, check_row_scale_example,
-            check_quantize_invariants, check_fp8_gemm_closed_forms, check_quant_traffic_example]
+            check_quantize_invariants, check_fp8_gemm_closed_forms, check_fp8_gemm_exact_at_its_limit,
+            check_quant_traffic_example]
 
 
 @pytest.mark.parametrize("check", FP8_PINS, ids=lambda f: f.__name__)

@@ -32,6 +32,10 @@ MUTATIONS = {
     "round_half_up": ("double r = rint(n);", "double r = floor(n + 0.5);"),
     "lost_alpha": ("double v = alpha * acc[j];", "double v = acc[j];"),
     "f16_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "points_beta_sign": ("if (beta != 0.0) v += beta * orc_decode(dtype, C_in, c_index(layoutA, i, j, ldc));\n        value[p] = v;",
+                         "if (beta != 0.0) v -= beta * orc_decode(dtype, C_in, c_index(layoutA, i, j, ldc));\n        value[p] = v;"),
+    "points_b_transposed": ("orc_decode(dtype, B, b_index(layoutB, k, j, ldb));\n        double v = alpha * s;",
+                            "orc_decode(dtype, B, b_index(layoutB, j, k, ldb));\n        double v = alpha * s;"),
     "c_row_col_swapped": ("return layout == ORC_ROW ? i * ldc + j : j * ldc + i;",
                           "return layout == ORC_ROW ? j * ldc + i : i * ldc + j;"),
 }

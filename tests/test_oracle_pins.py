@@ -310,6 +310,42 @@ def check_brute_force_fractions():
                 assert exact[i, j] == float(s)   # f16 products/sums this small are exact in f64
 
 
+def check_points_closed_forms():
+    # gemm_points sums each listed output on its own; it is pinned like the
+    # row form, at beta != 0, in every layout pair, with padded leading
+    # dimensions: all-ones (C = alpha*K + beta*C0), exact integers against
+    # numpy int64 (C = A B + 2 C0), and one-hot A rows that pick single rows
+    # of B (C = B[k(i), j] - C0, which also catches a transposed B).
+    M, N, K = 13, 11, 29
+    pi = np.array([0, 12, 5, 7, 0, 12, 3], np.int64)
+    pj = np.array([0, 10, 4, 9, 10, 0, 7], np.int64)
+    for dtype in ("f32", "f16", "bf16"):
+        for la, lb in LAYOUTS:
+            lda = (K if la == "row" else M) + 3
+            ldb = (N if lb == "row" else K) + 2
+            ldc = (N if la == "row" else M) + 1
+            C0 = oracle.round_to(dtype, RNG.uniform(-8, 8, (M, N)))
+            c0 = _store(la, C0, ldc, dtype)
+            got = oracle.gemm_points(la, lb, M, N, K, 0.5, _store(la, np.ones((M, K)), lda, dtype),
+                                     lda, _store(lb, np.ones((K, N)), ldb, dtype), ldb, -0.75, c0,
+                                     ldc, dtype, pi, pj)
+            assert np.array_equal(got, 0.5 * K - 0.75 * C0[pi, pj]), (dtype, la, lb)
+            Ai = RNG.integers(-4, 5, (M, K))
+            Bi = RNG.integers(-4, 5, (K, N))
+            Ci = RNG.integers(-4, 5, (M, N))
+            got = oracle.gemm_points(la, lb, M, N, K, 1.0, _store(la, Ai.astype(float), lda, dtype),
+                                     lda, _store(lb, Bi.astype(float), ldb, dtype), ldb, 2.0,
+                                     _store(la, Ci.astype(float), ldc, dtype), ldc, dtype, pi, pj)
+            assert np.array_equal(got, (Ai @ Bi + 2 * Ci)[pi, pj].astype(np.float64)), (dtype, la, lb)
+            pick = RNG.integers(0, K, M)
+            H = np.zeros((M, K))
+            H[np.arange(M), pick] = 1.0
+            Bv = oracle.round_to(dtype, RNG.uniform(-4, 4, (K, N)))
+            got = oracle.gemm_points(la, lb, M, N, K, 1.0, _store(la, H, lda, dtype), lda,
+                                     _store(lb, Bv, ldb, dtype), ldb, -1.0, c0, ldc, dtype, pi, pj)
+            assert np.array_equal(got, Bv[pick[pi], pj] - C0[pi, pj]), (dtype, la, lb)
+
+
 def check_silu_epilogue():
     """SiLU epilogue: the pages' two-partial-sums example, a library sigmoid,
     rounding before the activation, and the limits."""
@@ -369,7 +405,7 @@ PIN_CHECKS = [check_silu_epilogue, check_swiglu, check_f16_against_numpy, check_
               check_permutation, check_all_ones_alpha_beta, check_rank_one,
               check_alpha_zero_and_k_zero, check_beta_zero_never_reads_c,
               check_transpose_identity, check_integer_exact, check_against_numpy_float64,
-              check_brute_force_fractions]
+              check_brute_force_fractions, check_points_closed_forms]
 
 
 @pytest.mark.parametrize("check", PIN_CHECKS, ids=lambda f: f.__name__)

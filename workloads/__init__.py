@@ -72,6 +72,23 @@ def operand(kind: str, seed: int, rows: int, cols: int, layout: str, ld: int, dt
     return cast(buf.reshape(-1)[: max(outer, 1) * ld], dtype)
 
 
+# Canary bit patterns written into C before a call whose beta is 0 (quiet
+# NaNs): an output the library never wrote still holds one afterwards.
+CANARY = {"f32": 0x7FA5A5A5, "f16": 0x7E5A, "bf16": 0x7FA5}
+
+
+def c_initial(case: "Case", C0):
+    """Initial C buffer (CPU): a copy of C0 when beta != 0, else canary bits
+    everywhere."""
+    if C0 is not None:
+        return C0.clone()
+    n = case.c_numel()
+    if case.dtype == "f32":
+        return torch.full((n,), CANARY["f32"], dtype=torch.int32).view(torch.float32)
+    t = torch.full((n,), CANARY[case.dtype], dtype=torch.int16)   # both patterns < 0x8000
+    return t.view(torch.float16 if case.dtype == "f16" else torch.bfloat16)
+
+
 def storage_view(t: torch.Tensor) -> np.ndarray:
     """The raw bits of a CPU tensor as a numpy uint array (for the oracle)."""
     t = t.contiguous()
