@@ -3,33 +3,60 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one mgemm_run over the workload (host normalisation and dispatch,
-tile rasterisation, LDS staging, the MFMA/FMA contraction and the epilogue,
-all in one kernel launch) with every operand already resident in HBM.  The
-default workload is FP32 SGEMM 4096^3 row-major (uniform [-1,1] inputs).
+A step is one call of the library over the workload (host normalisation and
+dispatch, tile rasterisation, LDS staging, the MFMA contraction and the
+epilogue) with every operand already resident in HBM.  The default workload is
+the largest configuration: FP16 in / FP16 out with FP32 accumulation,
+column-major A(8192 x 16384), B(16384 x 8192), C(8192 x 8192), uniform [-1,1]
+inputs.
 
-Prints ONE JSON line.  `roofline` is measured live with HIP events around
-each launch on the stream the kernel runs on; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload (and checks that sample
-against the GPU result).  Other workloads are measured briefly and reported
-under `workloads` (skip with --only-headline).
+Prints ONE JSON line.  `roofline` is measured live with HIP events around the
+timed launches on the stream the kernel runs on, and put against both the
+published peak and the peak at the shader clock read from the GPU while the
+timed launches ran (amdsmi); `cpu_baseline` times the CPU oracle on a bounded
+row sample of the same workload, and `parity_sample` checks the GPU output
+against the oracle (for the headline: four points in every 64 x 64 block,
+every tile-boundary row and column, and no unwritten output anywhere).  The
+other workloads are measured briefly, each with its own CPU baseline and
+parity sample, under `workloads` (skip with --only-headline).
+
+Two helper modes read rocprofv3 output (no GPU needed):
+    python bench.py --summarize-trace DIR [--steady-after S]
+    python bench.py --summarize-pmc DIR [--steady-after S]
+The first prints per-kernel durations from a --kernel-trace run, over all
+calls and over the calls that started at least S seconds after the kernel's
+first call (the settled ones); the second prints per-dispatch counter values
+(FETCH_SIZE, WRITE_SIZE, ...) over the settled dispatches, and the same
+counters of the largest copy kernel for calibration.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s and % of MFMA/FP32 peak (HBM GB/s for M≤64) vs CPU oracle, 1 GPU"
-# Pages' number for this exact workload and metric: cuBLAS pure-FP32 SGEMM
-# 4096^3 on an RTX 4090 (SGEMM report, cuBLAS denominator section): context only.
-PAGES_SGEMM_4096_TFLOPS = 57.2424
+DEFAULT_WORKLOAD = "hgemm_col_8192x8192x16384"
+PEAK_SCLK_MHZ = 2400.0          # the clock the published peaks are quoted at
+
+# The pages' own numbers for some workloads (other machines: context only,
+# never a target).
+PAGES_CONTEXT = {
+    "hgemm_col_8192x8192x16384": "MTT S4000 write-up: hand kernel 73.8 TFLOP/s, muBLAS 86.0 "
+                                 "TFLOP/s (FP16 peak 100 TFLOP/s)",
+    "sgemm_4096": "SGEMM report: cuBLAS pure FP32 57.24 TFLOP/s, hand kernel K6 40.93 TFLOP/s "
+                  "(RTX 4090)",
+}
 
 
 def log(*a):
@@ -42,9 +69,10 @@ KERNEL_SOURCE = {
     "general": "k_general.hip", "f32_mfma": "k_f32_mfma.hip", "f32_fast": "k_f32_mfma.hip",
     "f32_fast_128": "k_f32_mfma.hip", "h_mfma_256x256": "k_h_mfma.hip",
     "h_mfma_256x192": "k_h_mfma.hip", "h_mfma_128x128": "k_h_mfma.hip",
-    "h_pp_256x256": "k_h_pp.hip", "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
+    "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
     "skinny_sk": "k_skinny_sk.hip", "h_dma_256x192": "k_h_dma.hip", "f32_fast_u": "k_f32_mfma.hip",
-    "h_dma_gated": "k_h_dma.hip", "fp8_quant+fp8_gemm": "k_f8.hip", "f32_sk": "k_f32_mfma.hip", "h_dma_128x192": "k_h_dma.hip",
+    "h_dma_gated": "k_h_dma.hip", "fp8_quant+fp8_gemm": "k_f8.hip", "f32_sk": "k_f32_mfma.hip",
+    "h_dma_128x192": "k_h_dma.hip",
 }
 
 
@@ -62,16 +90,173 @@ def src_hash(kernel: str | None = None) -> str:
     return h.hexdigest()[:16]
 
 
+# ---------------------------------------------------------------------------
+# GPU clock, power and health (amdsmi), sampled from a host thread.
+# ---------------------------------------------------------------------------
+class GpuMonitor:
+    """Reads the GPU's metrics table (shader clock per XCD, socket power,
+    temperatures, throttle status) through amdsmi.  Every method degrades to
+    None when amdsmi or the metrics are unavailable: the numbers are reported,
+    never required."""
+
+    def __init__(self, torch_device: int = 0):
+        self.handle = None
+        self.error = None
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+            import torch
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(torch_device)
+            want = (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", None),
+                    getattr(props, "pci_device_id", None))
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for hnd in handles:
+                try:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(hnd)      # "dddd:bb:dd.f"
+                    dom, bus, rest = bdf.split(":")
+                    dev = rest.split(".")[0]
+                    if (int(dom, 16), int(bus, 16), int(dev, 16)) == want:
+                        self.handle = hnd
+                        break
+                except Exception:
+                    continue
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            if self.handle is None:
+                self.error = "no amdsmi device matches torch device %d" % torch_device
+        except Exception as e:                 # amdsmi missing or not permitted
+            self.error = "%s: %s" % (type(e).__name__, e)
+
+    @staticmethod
+    def _valid(v):
+        return isinstance(v, (int, float)) and 0 < v < 0xFFFF
+
+    def read(self) -> dict | None:
+        if self.handle is None:
+            return None
+        try:
+            m = self._smi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception as e:
+            self.error = "%s: %s" % (type(e).__name__, e)
+            return None
+        clks = [v for v in (m.get("current_gfxclks") or []) if self._valid(v)]
+        clk = sum(clks) / len(clks) if clks else (m.get("current_gfxclk")
+                                                  if self._valid(m.get("current_gfxclk")) else None)
+        pw = m.get("current_socket_power")
+        if not self._valid(pw):
+            pw = m.get("average_socket_power") if self._valid(m.get("average_socket_power")) else None
+        return {"t": time.perf_counter(), "sclk_mhz": clk, "power_w": pw,
+                "temp_hotspot_c": m.get("temperature_hotspot"),
+                "temp_mem_c": m.get("temperature_mem"),
+                "throttle_status": m.get("throttle_status"),
+                "ppt_residency_acc": m.get("ppt_residency_acc"),
+                "accumulation_counter": m.get("accumulation_counter")}
+
+    def health(self) -> dict | None:
+        """One reading before any timing, with the clock limits."""
+        r = self.read()
+        if r is None:
+            return {"available": False, "why": self.error}
+        out = {"available": True, "sclk_mhz_idle": r["sclk_mhz"], "power_w_idle": r["power_w"],
+               "temp_hotspot_c": r["temp_hotspot_c"], "temp_mem_c": r["temp_mem_c"],
+               "throttle_status": r["throttle_status"]}
+        try:
+            ci = self._smi.amdsmi_get_clock_info(self.handle, self._smi.AmdSmiClkType.GFX)
+            out["sclk_mhz_max"] = ci.get("max_clk")
+        except Exception:
+            out["sclk_mhz_max"] = None
+        t = r["temp_hotspot_c"]
+        out["ok"] = not (self._valid(t) and t >= 95)
+        return out
+
+    def start(self, period_s: float = 0.002):
+        if self.handle is None:
+            return
+        self.samples = []
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                r = self.read()
+                if r is not None:
+                    self.samples.append(r)
+                time.sleep(period_s)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self, t0: float, t1: float, min_samples: int = 3, back_s: float = 0.3):
+        """Median clock and power over samples taken in [t0, t1]; with fewer
+        than min_samples there, over [t0 - back_s, t1] (the same kernel ran
+        back to back in the settle period before t0)."""
+        win = [s for s in self.samples if t0 <= s["t"] <= t1]
+        span = "timed region"
+        if len(win) < min_samples:
+            win = [s for s in self.samples if t0 - back_s <= s["t"] <= t1]
+            span = "timed region and the %.1f s of settled launches before it" % back_s
+        clk = [s["sclk_mhz"] for s in win if s["sclk_mhz"]]
+        pw = [s["power_w"] for s in win if s["power_w"]]
+        if not clk:
+            return {"available": False, "why": self.error or "no samples"}
+        ppt = [s["ppt_residency_acc"] for s in win if isinstance(s["ppt_residency_acc"], (int, float))]
+        acc = [s["accumulation_counter"] for s in win
+               if isinstance(s["accumulation_counter"], (int, float))]
+        out = {"available": True, "samples": len(win), "span": span,
+               "sclk_mhz_median": round(statistics.median(clk), 1),
+               "sclk_mhz_min": round(min(clk), 1), "sclk_mhz_max": round(max(clk), 1),
+               "power_w_median": round(statistics.median(pw), 1) if pw else None,
+               "temp_hotspot_c_max": max((s["temp_hotspot_c"] for s in win
+                                          if self._valid(s["temp_hotspot_c"])), default=None),
+               "throttle_status": sorted({s["throttle_status"] for s in win
+                                          if s["throttle_status"] is not None})}
+        if len(ppt) >= 2 and len(acc) >= 2 and acc[-1] > acc[0]:
+            # Share of the firmware's accumulation ticks spent at the package
+            # power limit over the span.
+            out["power_limited_share"] = round((ppt[-1] - ppt[0]) / (acc[-1] - acc[0]), 3)
+        return out
+
+
+def cpu_info() -> dict:
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": avail, "cpu_count": os.cpu_count()}
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
 def workload_table():
     import workloads as W
-    t = {"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(), "ragged_f32": W.ragged_f32(),
-         "ffn_bf16": W.ffn_bf16(), "ffn_bf16_silu": W.ffn_bf16_silu(),
-         "ffn_gated_bf16": W.ffn_gated_bf16(), "ffn_share_bf16": W.ffn_share_bf16(),
-         "ffn_gated_share_bf16": W.ffn_gated_share_bf16(), "fp8_ffn": W.fp8_ffn_bf16(),
-         "fp8_4096x1536x4096": W.fp8_quant_example()}
-    for s in W.HGEMM_SHAPES:
+    t = {}
+    for s in W.HGEMM_SHAPES[::-1]:
         c = W.hgemm_colmajor(*s)
         t[c.name] = c
+    t.update({"sgemm_4096": W.sgemm_4096(), "sgemm_256": W.sgemm_256(),
+              "ragged_f32": W.ragged_f32(), "ffn_bf16": W.ffn_bf16(),
+              "ffn_bf16_silu": W.ffn_bf16_silu(), "ffn_gated_bf16": W.ffn_gated_bf16(),
+              "ffn_share_bf16": W.ffn_share_bf16(),
+              "ffn_gated_share_bf16": W.ffn_gated_share_bf16(), "fp8_ffn": W.fp8_ffn_bf16(),
+              "fp8_4096x1536x4096": W.fp8_quant_example()})
     for m in W.SKINNY_M:
         c = W.ffn_bf16(m)
         t["skinny_bf16_m%d" % m] = c
@@ -96,10 +281,18 @@ def peak_key(case) -> str:
     return "fp8" if case.extra.get("fp8") else case.dtype
 
 
+def arith_dtype(case) -> str:
+    """The type the contraction computes in (FP8 workloads: E4M3 codes)."""
+    return "fp8_e4m3" if case.extra.get("fp8") else case.dtype
+
+
 def is_hbm_bound(case) -> bool:
     return case.dtype != "f32" and case.M <= 64
 
 
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
 _SLEEP_CYCLES_PER_S = None
 
 
@@ -124,13 +317,14 @@ def hold_stream(stream, seconds):
         torch.cuda._sleep(int(min(seconds, 0.05) * _SLEEP_CYCLES_PER_S))
 
 
-def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
+def measure(h, case, steps, warmup, rotate=1, settle_s=0.0, monitor=None):
     """Time `steps` launches after `warmup` untimed ones (continued until
-    `warm_s` seconds have passed, so short kernels run at a settled clock);
-    returns timings, the kernel name and device buffers."""
+    `settle_s` seconds have passed, so the clock has settled to what sustained
+    use of the kernel gives); returns timings, the kernel name, device buffers
+    and the host-clock window of the timed launches."""
     import torch
     import dense_gemm_mgemm_amd as mg
-    from tests.parity import c_initial
+    from workloads import c_initial
 
     stream = torch.cuda.current_stream()
     epilogue = case.extra.get("epilogue", "none")
@@ -185,13 +379,18 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
                          dA[j], case.lda, dB[j], case.ldb, case.beta, dC[j], case.ldc,
                          case.dtype, stream=stream)
 
+    if monitor is not None:
+        monitor.start()
+    n_pre = 0
     for i in range(warmup):
         launch(i)
+    n_pre += warmup
     torch.cuda.synchronize()
     t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < warm_s:
+    while time.perf_counter() - t_warm < settle_s:
         for i in range(8):
             launch(i)
+        n_pre += 8
         torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -201,21 +400,24 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
     t_host = time.perf_counter()
     for i in range(16):
         launch(i)
+    n_pre += 16
     host_s = (time.perf_counter() - t_host) / 16
     torch.cuda.synchronize()
     # The timed region: `steps` launches back to back between two events.  A
     # kernel shorter than the host's enqueue time would otherwise be timed
     # with the GPU waiting for the host between steps, so the stream is held
     # until all of them are enqueued.  Average launch duration = region / steps.
-    hold_stream(stream, 1.25 * host_s * steps + 1e-4)
+    hold_stream(stream, 1.5 * host_s * steps + 1e-4)
     wall0 = time.perf_counter()
     t_all0.record(stream)
     for i in range(steps):
         launch(i)
     t_all1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    wall1 = time.perf_counter()
     total_ms = t_all0.elapsed_time(t_all1)
+    # The GPU ran the timed launches during the last total_ms of the host window.
+    gpu0 = max(wall0, wall1 - total_ms * 1e-3)
     # Spread of single launches, from a second pass with an event pair around
     # each (each pair adds a few microseconds of its own).
     hold_stream(stream, 1.5 * host_s * steps + 1e-4)
@@ -224,12 +426,16 @@ def measure(h, case, steps, warmup, rotate=1, warm_s=0.0):
         launch(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    if monitor is not None:
+        monitor.stop()
     per = sorted(a.elapsed_time(b) for a, b in ev)
     return {
-        "kernel": kname, "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+        "kernel": kname, "ms_per_step": total_ms / steps,
+        "wall_ms_per_step": (wall1 - wall0) * 1e3 / steps,
         "host_ms_per_step": host_s * 1e3, "launch_ms_mean": total_ms / steps,
         "launch_ms_single_median": per[len(per) // 2],
         "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
+        "untimed_launches": n_pre, "window": (gpu0, wall1),
         "inputs": (A, B, C0), "out": dC[(steps - 1) % len(dC)],
     }
 
@@ -265,7 +471,7 @@ def measure_mix(h, steps=20):
         group(hh)
         host_s = time.perf_counter() - t1
         torch.cuda.synchronize()
-        hold_stream(stream, 1.25 * host_s * steps + 1e-4)
+        hold_stream(stream, 1.5 * host_s * steps + 1e-4)
         e0.record(stream)
         for _ in range(steps):
             group(hh)
@@ -293,9 +499,25 @@ def measure_mix(h, steps=20):
             "choices_model_vs_tuned": {str(k): v for k, v in picks.items()}}
 
 
-def cpu_baseline(case, out_dev, budget_s):
-    """Time the oracle on a bounded row sample of the workload and check that
-    sample against the GPU output."""
+# ---------------------------------------------------------------------------
+# CPU baseline and parity samples (the only part of this file that uses the
+# oracle)
+# ---------------------------------------------------------------------------
+def _row_order(M: int, seed: int = 0):
+    """Rows in the order the sample takes them: the first and last row of
+    every 64-row block (tile boundaries) in random order, then the rest."""
+    import numpy as np
+    from tests.parity import boundary_lines
+    rng = np.random.default_rng(seed)
+    b = np.asarray(boundary_lines(M), np.int64)
+    rest = np.setdiff1d(np.arange(M, dtype=np.int64), b)
+    return np.concatenate([rng.permutation(b), rng.permutation(rest)])
+
+
+def cpu_baseline(case, out_cpu, budget_s):
+    """Time the oracle on a bounded row sample of the workload (doubling the
+    sample until it takes about `budget_s`) and check that sample against the
+    GPU output."""
     import numpy as np
     import oracle
     from tests import parity as P
@@ -303,18 +525,17 @@ def cpu_baseline(case, out_dev, budget_s):
 
     A, B, C0 = case.inputs
     if case.extra.get("fp8"):
-        return cpu_baseline_fp8(case, out_dev, budget_s)
+        return cpu_baseline_fp8(case, out_cpu, budget_s)
     gated = bool(case.extra.get("gated"))
     a = storage_view(A)
     bs = [storage_view(x) for x in (B if gated else (B,))]
     c0 = None if C0 is None else storage_view(C0)
     threads = oracle.max_threads()
+    order = _row_order(case.M)
     nrows = max(1, min(case.M, 16))
-    rng = np.random.default_rng(0)
     rows_done, t_total, results = [], 0.0, []
     while True:
-        rows = np.sort(rng.choice(case.M, size=nrows, replace=False)) if nrows < case.M \
-            else np.arange(case.M)
+        rows = np.sort(order[:nrows])
         t0 = time.perf_counter()
         exact = [oracle.gemm(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha, a,
                              case.lda, b, case.ldb, case.beta, c0, None, case.ldc, case.dtype,
@@ -329,12 +550,12 @@ def cpu_baseline(case, out_dev, budget_s):
     flops = 2.0 * len(rows_done) * case.N * case.K * len(bs)
     if gated:
         try:
-            err = P.check_gated(case, A, B[0], B[1], out_dev.cpu(), rows=rows_done)
+            err = P.check_gated(case, A, B[0], B[1], out_cpu, rows=rows_done)
             rep = {"ok": True, "max_err": err, "tol": None}
         except AssertionError as e:
             rep = {"ok": False, "max_err": None, "tol": None, "what": str(e)[:200]}
     else:
-        got = P.logical(case, oracle.decode(case.dtype, storage_view(out_dev.cpu())))[rows_done]
+        got = P.logical(case, oracle.decode(case.dtype, storage_view(out_cpu)))[rows_done]
         if case.extra.get("epilogue") == "silu":
             y, bound = P.silu_reference(case, results[0])
             err = np.abs(got - y)
@@ -342,14 +563,21 @@ def cpu_baseline(case, out_dev, budget_s):
                    "tol": float(np.max(bound))}
         else:
             rep = P.compare(case, got, results[0])
-    return ({"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads,
-             "kind": "oracle", "sample": "%d of %d rows of C (%.1f GFLOP in %.1f s, FP64)" % (
-                 len(rows_done), case.M, flops / 1e9, t_total)},
-            {"rows": len(rows_done), "max_err": rep["max_err"], "tol": rep["tol"],
-             "ok": rep["ok"]})
+    cb = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+          "sample": "%d of %d rows of C, tile-boundary rows first (%.1f GFLOP in %.2f s, FP64)" % (
+              len(rows_done), case.M, flops / 1e9, t_total)}
+    cb.update(cpu_info())
+    if is_hbm_bound(case):
+        es = 2
+        r = len(rows_done)
+        cb["GBs"] = es * (r * case.K + case.K * case.N + r * case.N) / t_total / 1e9
+    chk = {"rows": len(rows_done), "max_err": rep["max_err"], "tol": rep["tol"], "ok": rep["ok"]}
+    if "what" in rep:
+        chk["what"] = rep["what"]
+    return cb, chk
 
 
-def cpu_baseline_fp8(case, out_dev, budget_s):
+def cpu_baseline_fp8(case, out_cpu, budget_s):
     """The FP8 oracle on a row sample: quantise the sampled rows of X, multiply
     by the weight codes (quantised once, not timed, like the GPU's), and check
     the sample against the GPU output within the FP32-accumulation bound."""
@@ -364,10 +592,10 @@ def cpu_baseline_fp8(case, out_dev, budget_s):
     X = oracle.decode(case.dtype, storage_view(A)).reshape(M, case.lda)[:, :K]
     Wv = oracle.decode(case.dtype, storage_view(B)).reshape(N, case.ldb)[:, :K]
     qw, sw = f8.quantize_rows(Wv)
-    rng = np.random.default_rng(0)
+    order = _row_order(M)
     nrows = max(1, min(M, 8))
     while True:
-        rows = np.sort(rng.choice(M, size=nrows, replace=False)) if nrows < M else np.arange(M)
+        rows = np.sort(order[:nrows])
         t0 = time.perf_counter()
         qx, sx = f8.quantize_rows(X[rows])
         exact = f8.fp8_gemm(len(rows), N, K, case.alpha, qx.ravel(), K, sx, qw.ravel(), K, sw)
@@ -375,7 +603,7 @@ def cpu_baseline_fp8(case, out_dev, budget_s):
         if nrows >= M or dt * 2 > budget_s:
             break
         nrows = int(min(M, max(nrows * 2, nrows * budget_s / max(dt, 1e-3) * 0.8)))
-    got = oracle.decode(case.dtype, storage_view(out_dev.cpu())).reshape(-1, case.ldc)[rows, :N]
+    got = oracle.decode(case.dtype, storage_view(out_cpu)).reshape(-1, case.ldc)[rows, :N]
     tol = P.tol_f32_rel(K) * float(np.max(np.abs(exact))) + \
         P._ulp(case.dtype, oracle.round_to(case.dtype, exact)) / 2
     err = np.abs(got - exact)
@@ -385,13 +613,33 @@ def cpu_baseline_fp8(case, out_dev, budget_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:                     # threadpoolctl missing or unreadable
         cores = 1
-    return ({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-             "sample": "%d of %d rows of C: FP8 quantisation + product (%.1f GFLOP in %.1f s, "
-                       "numpy FP64)" % (len(rows), M, flops / 1e9, dt)},
-            {"rows": len(rows), "max_err": float(np.max(err)), "tol": float(np.max(tol)),
-             "ok": bool(np.all(err <= tol))})
+    cb = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+          "sample": "%d of %d rows of C: FP8 quantisation + product (%.1f GFLOP in %.2f s, "
+                    "numpy FP64)" % (len(rows), M, flops / 1e9, dt)}
+    cb.update(cpu_info())
+    return cb, {"rows": len(rows), "max_err": float(np.max(err)), "tol": float(np.max(tol)),
+                "ok": bool(np.all(err <= tol))}
 
 
+def stratified_sample(case, out_cpu):
+    """Four oracle points in every 64 x 64 block, every tile-boundary row and
+    column, and a scan for unwritten outputs over the whole C."""
+    from tests import parity as P
+    from workloads import c_initial
+    A, B, C0 = case.inputs
+    t0 = time.perf_counter()
+    try:
+        rep = P.check_stratified(case, A, B, C0, c_initial(case, C0), out_cpu)
+        rep["ok"] = True
+    except AssertionError as e:
+        rep = {"ok": False, "what": str(e)[:300]}
+    rep["oracle_s"] = round(time.perf_counter() - t0, 2)
+    return rep
+
+
+# ---------------------------------------------------------------------------
+# Committed counter summaries
+# ---------------------------------------------------------------------------
 def counters_for(kernel, workload):
     """The committed rocprofv3 counter summary of this kernel and workload, if
     it was taken on the current kernel sources, else None."""
@@ -407,10 +655,106 @@ def counters_for(kernel, workload):
     return None
 
 
-def traffic_for(kernel, workload):
-    """HBM bytes per launch from the committed counter summary (or None)."""
-    e = counters_for(kernel, workload)
-    return e.get("bytes_per_launch") if e else None
+# ---------------------------------------------------------------------------
+# rocprofv3 output summaries (no GPU needed)
+# ---------------------------------------------------------------------------
+def _csv_rows(path_or_dir: str, suffix: str):
+    files = [path_or_dir] if os.path.isfile(path_or_dir) else sorted(
+        glob.glob(os.path.join(path_or_dir, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, path_or_dir))
+    for f in files:
+        with open(f, newline="") as fh:
+            yield from csv.DictReader(fh)
+
+
+def summarize_trace(path: str, steady_after_s: float):
+    """Per kernel: calls and mean duration over all calls, then over the calls
+    that started at least `steady_after_s` after that kernel's first call."""
+    by = {}
+    for r in _csv_rows(path, "kernel_trace.csv"):
+        by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]),
+                                                    int(r["End_Timestamp"])))
+    out = []
+    for name, ev in by.items():
+        ev.sort()
+        first = ev[0][0]
+        d_all = [(e - s) / 1e3 for s, e in ev]
+        d_st = [(e - s) / 1e3 for s, e in ev if s - first >= steady_after_s * 1e9]
+        out.append({"kernel": name, "calls": len(ev), "mean_us_all": statistics.fmean(d_all),
+                    "steady_calls": len(d_st),
+                    "steady_mean_us": statistics.fmean(d_st) if d_st else None,
+                    "steady_median_us": statistics.median(d_st) if d_st else None,
+                    "steady_min_us": min(d_st) if d_st else None,
+                    "steady_max_us": max(d_st) if d_st else None,
+                    "total_us": sum(d_all)})
+    out.sort(key=lambda x: -x["total_us"])
+    return out
+
+
+def summarize_pmc(path: str, steady_after_s: float):
+    """Per kernel: counters summed per dispatch, averaged over the dispatches
+    that started at least `steady_after_s` after that kernel's first one; plus
+    the mean per-dispatch duration of those dispatches (serialised by the
+    profiler)."""
+    disp = {}
+    for r in _csv_rows(path, "counter_collection.csv"):
+        key = int(r["Dispatch_Id"])
+        d = disp.setdefault(key, {"kernel": r["Kernel_Name"], "start": int(r["Start_Timestamp"]),
+                                  "end": int(r["End_Timestamp"]), "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    by = {}
+    for d in disp.values():
+        by.setdefault(d["kernel"], []).append(d)
+    out = []
+    for name, ds in by.items():
+        ds.sort(key=lambda d: d["start"])
+        first = ds[0]["start"]
+        st = [d for d in ds if d["start"] - first >= steady_after_s * 1e9] or ds
+        names = sorted({c for d in st for c in d["c"]})
+        out.append({"kernel": name, "dispatches": len(ds), "steady": len(st),
+                    "mean_us": statistics.fmean((d["end"] - d["start"]) / 1e3 for d in st),
+                    "counters": {c: statistics.fmean(d["c"].get(c, 0.0) for d in st)
+                                 for c in names}})
+    return out
+
+
+def print_summary(rows, kind):
+    if kind == "trace":
+        print("| Kernel | Calls | Mean us (all) | Settled calls | Settled mean us | "
+              "Settled median us | min | max |")
+        print("|---|---|---|---|---|---|---|---|")
+        for r in rows:
+            f = lambda v: "-" if v is None else "%.2f" % v
+            print("| `%s` | %d | %.2f | %d | %s | %s | %s | %s |" % (
+                r["kernel"][:110], r["calls"], r["mean_us_all"], r["steady_calls"],
+                f(r["steady_mean_us"]), f(r["steady_median_us"]), f(r["steady_min_us"]),
+                f(r["steady_max_us"])))
+    else:
+        for r in rows:
+            print("`%s`: %d dispatches (%d settled), mean %.2f us; %s" % (
+                r["kernel"][:110], r["dispatches"], r["steady"], r["mean_us"],
+                ", ".join("%s %.6g" % kv for kv in r["counters"].items())))
+
+
+# ---------------------------------------------------------------------------
+def roofline_entry(case, r, hbm, clock):
+    """Achieved rate, peaks (published and at the measured clock) and fractions."""
+    from dense_gemm_mgemm_amd import costmodel as cm
+    flops, nbytes = algorithmic(case)
+    s = r["launch_ms_mean"] * 1e-3
+    if hbm:
+        achieved, peak, unit, bound = nbytes / s / 1e9, cm.PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak = flops / s / 1e12, cm.PEAK_TFLOPS[peak_key(case)]
+        unit, bound = "TFLOP/s", "mfma"
+    e = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    if not hbm and clock and clock.get("available"):
+        pk = peak * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ
+        e.update(sclk_mhz=clock["sclk_mhz_median"], peak_at_sclk=round(pk, 1),
+                 frac_at_sclk=round(achieved / pk, 4))
+    return e, flops, nbytes
 
 
 def main():
@@ -418,13 +762,27 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sgemm_4096")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed back-to-back launches before the headline's timing")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (headline)")
+    ap.add_argument("--cpu-budget-other", type=float, default=1.0,
+                    help="seconds of oracle work for each other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--steady-after", type=float, default=1.0,
+                    help="summaries: seconds after a kernel's first call before calls count as settled")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_pmc:
+        if args.summarize_trace:
+            print_summary(summarize_trace(args.summarize_trace, args.steady_after), "trace")
+        if args.summarize_pmc:
+            print_summary(summarize_pmc(args.summarize_pmc, args.steady_after), "pmc")
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -432,20 +790,27 @@ def main():
 
     import torch
     import dense_gemm_mgemm_amd as mg
-    from dense_gemm_mgemm_amd import costmodel as cm
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    mg.load()                                   # raises if the HIP library is missing
+    monitor = GpuMonitor(0)
+    health = monitor.health()
+    if not health.get("ok", True):
+        log("GPU health warning before timing:", health)
     h = mg.mgemm_create()
     table = workload_table()
     case = table[args.workload]
-    flops, nbytes = algorithmic(case)
     hbm = is_hbm_bound(case)
     log("headline:", case.name)
-    r = measure(h, case, args.steps, args.warmup, rotate=4 if hbm else 1)
+    r = measure(h, case, args.steps, args.warmup, rotate=4 if hbm else 1, settle_s=args.settle,
+                monitor=monitor)
+    clock = monitor.summary(*r["window"])
     case.inputs = r["inputs"]
+    log("headline timed: %.5f ms per step, %d untimed launches before" % (
+        r["ms_per_step"], r["untimed_launches"]))
 
     if args.copy_probe:
         n = args.copy_probe * 2 ** 20 // 4
@@ -456,75 +821,100 @@ def main():
         torch.cuda.synchronize()
         log("copy probe: %d MiB x3" % args.copy_probe)
 
-    per_launch_s = r["launch_ms_mean"] * 1e-3
-    if hbm:
-        achieved, peak, unit, bound = nbytes / per_launch_s / 1e9, cm.PEAK_HBM_GBS, "GB/s", "hbm"
-        value, vunit = nbytes / (r["ms_per_step"] * 1e-3) / 1e9, "GB/s"
-    else:
-        achieved, peak = flops / per_launch_s / 1e12, cm.PEAK_TFLOPS[peak_key(case)]
-        unit, bound = "TFLOP/s", "mfma"
-        value, vunit = flops / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
-    traffic = traffic_for(r["kernel"], case.name)
+    roof, flops, nbytes = roofline_entry(case, r, hbm, clock)
+    cnt = counters_for(r["kernel"], case.name) or {}
+    roof.update(traffic=cnt.get("bytes_per_launch"),
+                traffic_source="profiles/traffic.json (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                               "copy-calibrated) for this kernel source" if cnt else None,
+                mfma_busy=cnt.get("mfma_busy"),
+                algorithmic_per_launch=flops if not hbm else nbytes,
+                launch_ms_mean=round(r["launch_ms_mean"], 5),
+                single_launch_ms_p10=round(r["launch_ms_p10"], 5),
+                single_launch_ms_p90=round(r["launch_ms_p90"], 5))
+    value = flops / (r["ms_per_step"] * 1e-3) / 1e12 if not hbm else \
+        nbytes / (r["ms_per_step"] * 1e-3) / 1e9
     line = {
-        "metric": METRIC, "value": round(value, 3), "unit": vunit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": (round(value / PAGES_SGEMM_4096_TFLOPS, 3)
-                        if case.name == "sgemm_4096" else None),
-        "dtype": case.dtype, "data": "synthetic",
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s" if hbm else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": arith_dtype(case), "data": "synthetic",
         "config": {"workload": case.name, "M": case.M, "N": case.N, "K": case.K,
                    "layoutA": case.layoutA, "layoutB": case.layoutB, "lda": case.lda,
                    "ldb": case.ldb, "ldc": case.ldc, "alpha": case.alpha, "beta": case.beta,
                    "kernel": r["kernel"], "inputs": "%s/%s seeds %s" % (case.kindA, case.kindB,
                                                                         list(case.seeds[:2])),
-                   "vs_baseline_ref": "cuBLAS pure-FP32 4096^3 on RTX 4090 from the pages, "
-                                      "57.24 TFLOP/s (another machine: context only)"
-                   if case.name == "sgemm_4096" else None},
-        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "mfma_busy": (counters_for(r["kernel"], case.name) or {}).get("mfma_busy"),
-                     "algorithmic_per_launch": flops if not hbm else nbytes,
-                     "launch_ms_mean": round(r["launch_ms_mean"], 5),
-                     "single_launch_ms_p10": round(r["launch_ms_p10"], 5),
-                     "single_launch_ms_p90": round(r["launch_ms_p90"], 5)},
+                   "settle_s": args.settle, "untimed_launches": r["untimed_launches"],
+                   "pages_context": PAGES_CONTEXT.get(case.name)},
+        "roofline": roof,
+        "clock": clock,
+        "health": health,
         "cpu_baseline": None,
         "src_hash": src_hash(),
     }
+    out_cpu = r["out"].cpu()
+    del r
     if not args.no_cpu_baseline:
-        cb, chk = cpu_baseline(case, r["out"], args.cpu_budget)
+        cb, chk = cpu_baseline(case, out_cpu, args.cpu_budget)
         line["cpu_baseline"] = cb
+        if cb["unit"] == line["unit"] and cb["value"] > 0:
+            line["vs_baseline"] = round(line["value"] / cb["value"], 1)
+            line["config"]["vs_baseline_is"] = "value / cpu_baseline.value (the metric's CPU oracle)"
+        if not is_hbm_bound(case) and not case.extra.get("gated") and not case.extra.get("fp8") \
+                and case.extra.get("epilogue", "none") == "none":
+            chk["stratified"] = stratified_sample(case, out_cpu)
+            chk["ok"] = chk["ok"] and chk["stratified"]["ok"]
         line["parity_sample"] = chk
         if not chk["ok"]:
-            log("PARITY FAILURE on the sampled rows:", chk)
+            log("PARITY FAILURE on the sample:", chk)
+    del out_cpu
     if not args.only_headline:
         others = {}
         for name, c in table.items():
             if name == case.name:
                 continue
-            f2, b2 = algorithmic(c)
             hb = is_hbm_bound(c)
             log("workload:", name)
-            rr = measure(h, c, 20, 5, rotate=4 if hb else 1, warm_s=0.25)
-            s = rr["launch_ms_mean"] * 1e-3
+            rr = measure(h, c, 20, 5, rotate=4 if hb else 1, settle_s=0.25, monitor=monitor)
+            ck = monitor.summary(*rr["window"])
+            rf, _, _ = roofline_entry(c, rr, hb, ck)
             ent = {"kernel": rr["kernel"], "launch_ms_mean": round(rr["launch_ms_mean"], 5),
-                   "dtype": c.dtype}
+                   "dtype": arith_dtype(c)}
             if hb:
-                ent.update(GBs=round(b2 / s / 1e9, 1), frac_hbm=round(b2 / s / 1e9 / cm.PEAK_HBM_GBS, 4))
+                ent.update(GBs=rf["achieved"], frac_hbm=rf["frac"])
             else:
-                tf = f2 / s / 1e12
-                ent.update(TFLOPs=round(tf, 2), frac_peak=round(tf / cm.PEAK_TFLOPS[peak_key(c)], 4))
+                ent.update(TFLOPs=rf["achieved"], frac_peak=rf["frac"])
+                if "frac_at_sclk" in rf:
+                    ent.update(sclk_mhz=rf["sclk_mhz"], frac_at_sclk=rf["frac_at_sclk"])
+            if ck.get("available"):
+                ent["power_w"] = ck.get("power_w_median")
             cnt = counters_for(rr["kernel"], name)
             if cnt:
                 ent.update(traffic=cnt.get("bytes_per_launch"), mfma_busy=cnt.get("mfma_busy"))
+            if not args.no_cpu_baseline:
+                c.inputs = rr["inputs"]
+                o = rr["out"].cpu()
+                del rr
+                cb, chk = cpu_baseline(c, o, args.cpu_budget_other)
+                ent["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "sample")}
+                if "GBs" in cb:
+                    ent["cpu_baseline"]["GBs"] = round(cb["GBs"], 2)
+                ent["parity_sample"] = chk
+                if not chk["ok"]:
+                    log("PARITY FAILURE on", name, chk)
+                c.inputs = None
+                del o
+            else:
+                del rr
             others[name] = ent
-            del rr
             torch.cuda.empty_cache()
         log("workload: ffn_mix_bf16 (model vs tuned table)")
         others["ffn_mix_bf16"] = measure_mix(h)
         line["workloads"] = others
     mg.mgemm_destroy(h)
     print(json.dumps(line), flush=True)
-    if line.get("parity_sample") and not line["parity_sample"]["ok"]:
+    bad = [n for n, e in line.get("workloads", {}).items()
+           if not e.get("parity_sample", {"ok": True})["ok"]]
+    if (line.get("parity_sample") and not line["parity_sample"]["ok"]) or bad:
         sys.exit(1)
 
 
