@@ -17,7 +17,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmgemm.so")
 
-MGEMM_SUCCESS, MGEMM_ERR_INVALID_ARG, MGEMM_ERR_UNSUPPORTED, MGEMM_ERR_HIP, MGEMM_ERR_ALLOC = range(5)
+(MGEMM_SUCCESS, MGEMM_ERR_INVALID_ARG, MGEMM_ERR_UNSUPPORTED, MGEMM_ERR_HIP, MGEMM_ERR_ALLOC,
+ MGEMM_ERR_SCRATCH) = range(6)
 MGEMM_ROW_MAJOR, MGEMM_COL_MAJOR = 0, 1
 MGEMM_F32, MGEMM_F16, MGEMM_BF16 = 0, 1, 2
 KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
@@ -36,7 +37,7 @@ EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "m
             "mgemm_select_variant", "mgemm_tune", "mgemm_table_export", "mgemm_table_import",
             "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_quantize_fp8", "mgemm_run_fp8",
             "mgemm_status_string",
-            "mgemm_kernel_name", "mgemm_num_cu"]
+            "mgemm_kernel_name", "mgemm_num_cu", "mgemm_run_noalloc"]
 
 
 class MgemmError(RuntimeError):
@@ -82,6 +83,7 @@ def load(path: str | None = None):
                                        i64, ci, vp]
     lib.mgemm_run_variant.argtypes = [vp, ctypes.POINTER(MgemmVariant)] + run_args[:-1] + [ci, vp]
     lib.mgemm_select_variant.argtypes = [vp] + run_args[:-1] + [ctypes.POINTER(MgemmVariant)]
+    lib.mgemm_run_noalloc.argtypes = [ctypes.POINTER(MgemmVariant)] + run_args[:-1] + [ci, vp]
     pi64, pdbl = ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)
     lib.mgemm_tune.argtypes = [vp, ci, ci, ci, ctypes.c_int32, pi64, pi64, pi64, pdbl,
                                ctypes.POINTER(MgemmTuneResult), vp]
@@ -99,7 +101,7 @@ def load(path: str | None = None):
                  "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
                  "mgemm_select_variant", "mgemm_select_kernel", "mgemm_tune", "mgemm_table_export",
                  "mgemm_table_import", "mgemm_table_clear", "mgemm_quantize_fp8",
-                 "mgemm_run_fp8"):
+                 "mgemm_run_fp8", "mgemm_run_noalloc"):
         getattr(lib, name).restype = ci
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
@@ -206,6 +208,19 @@ def mgemm_run_variant(h, kernel, ksplit, layoutA, layoutB, M, N, K, alpha, A, ld
                                   _enum(epilogue, _EPILOGUE), _stream(stream))
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_run_variant(%s, %d)" % (kernel, ksplit))
+
+
+def mgemm_run_noalloc(kernel, ksplit, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                      ldc, dtype, epilogue="none", stream=None) -> None:
+    """mgemm_run_variant without a handle or any allocation (the library's
+    static scratch array on the current device)."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    v = MgemmVariant(k, int(ksplit))
+    st = load().mgemm_run_noalloc(ctypes.byref(v), *_args(layoutA, layoutB, M, N, K, alpha, A, lda,
+                                                          B, ldb, beta, C, ldc, dtype),
+                                  _enum(epilogue, _EPILOGUE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_noalloc(%s, %d)" % (kernel, ksplit))
 
 
 def mgemm_run_gated_ex(h, ksplit, M, N, K, X, ldx, Wg, Wu, ldw, Z, ldz, dtype, stream=None) -> None:

@@ -63,7 +63,22 @@ int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k
 Choice model_choice(const Problem& p, const mgemm::Workspace& ws);
 // Table entry, else the model.
 Choice choose(mgemm_handle_t h, const Problem& p);
+Choice choose_in(const Table* table, const mgemm::Workspace& ws, const Problem& p);
 mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s);
+mgemm_status_t launch_ws(const mgemm::Workspace& ws, const Problem& p, Choice c, hipStream_t s);
 bool splittable(mgemm_kernel_t k);
+mgemm_status_t make_problem_on(int num_cu, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                               int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                               int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                               int64_t ldc, mgemm_dtype_t dtype, Problem* out);
+// The body of mgemm_run_variant for a device with num_cu compute units, a
+// workspace and an optional dispatch table.  A forced variant whose split
+// (or stream-K) form needs more workspace than ws holds returns too_big.
+mgemm_status_t run_core(int num_cu, const mgemm::Workspace& ws, const Table* table,
+                        mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
+                        mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                        void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                        hipStream_t stream, mgemm_status_t too_big);
 
 }  // namespace mgemm_host

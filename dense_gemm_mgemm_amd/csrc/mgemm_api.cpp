@@ -16,12 +16,13 @@ inline bool valid_dtype(mgemm_dtype_t d) { return d == MGEMM_F32 || d == MGEMM_F
 inline int64_t max1(int64_t x) { return x > 1 ? x : 1; }
 }  // namespace
 
-// Checks the rules of mgemm_run and builds the canonical problem.
-mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
-                            int64_t M, int64_t N, int64_t K, float alpha, const void* A,
-                            int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-                            int64_t ldc, mgemm_dtype_t dtype, Problem* out) {
-    if (!h || !valid_layout(layoutA) || !valid_layout(layoutB) || !valid_dtype(dtype))
+// Checks the rules of mgemm_run and builds the canonical problem for a
+// device with num_cu compute units.
+mgemm_status_t make_problem_on(int num_cu, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                               int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                               int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                               int64_t ldc, mgemm_dtype_t dtype, Problem* out) {
+    if (!valid_layout(layoutA) || !valid_layout(layoutB) || !valid_dtype(dtype))
         return MGEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return MGEMM_ERR_INVALID_ARG;
     const bool rowA = layoutA == MGEMM_ROW_MAJOR, rowB = layoutB == MGEMM_ROW_MAJOR;
@@ -45,7 +46,7 @@ mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layo
     p.C = C;
     p.ldc = ldc;
     p.dtype = (int)dtype;
-    p.num_cu = h->num_cu;
+    p.num_cu = num_cu;
     p.epilogue = mgemm::EPI_NONE;
     p.B2 = nullptr;
     p.ldb2 = 0;
@@ -66,6 +67,15 @@ mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layo
     }
     *out = p;
     return MGEMM_SUCCESS;
+}
+
+mgemm_status_t make_problem(mgemm_handle_t h, mgemm_layout_t layoutA, mgemm_layout_t layoutB,
+                            int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                            int64_t ldc, mgemm_dtype_t dtype, Problem* out) {
+    if (!h) return MGEMM_ERR_INVALID_ARG;
+    return make_problem_on(h->num_cu, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                           ldc, dtype, out);
 }
 
 bool variant_supports(const Problem& p, mgemm_kernel_t k) {
@@ -250,25 +260,31 @@ int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k
 
 // A table entry for the problem (exact shape first, then its bucket) if its
 // variant can run it; otherwise the model.
-Choice choose(mgemm_handle_t h, const Problem& p) {
-    const auto& tab = h->table.entries;
-    if (!tab.empty()) {
+Choice choose_in(const Table* table, const mgemm::Workspace& ws, const Problem& p) {
+    if (table && !table->entries.empty()) {
+        const auto& tab = table->entries;
         for (const TableKey& key : {exact_key(p), bucket_key(p)}) {
             auto it = tab.find(key);
             if (it == tab.end()) continue;
             const mgemm_kernel_t k = (mgemm_kernel_t)it->second.kernel;
             if (!variant_supports(p, k)) continue;
-            const int ks = forced_splits(p, h->ws, k, it->second.ksplit);
+            const int ks = forced_splits(p, ws, k, it->second.ksplit);
             if (ks >= 1) return {k, ks};
         }
     }
-    return model_choice(p, h->ws);
+    return model_choice(p, ws);
 }
 
+Choice choose(mgemm_handle_t h, const Problem& p) { return choose_in(&h->table, h->ws, p); }
+
 mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t s) {
+    return launch_ws(h->ws, p, c, s);
+}
+
+mgemm_status_t launch_ws(const mgemm::Workspace& ws, const Problem& p, Choice c, hipStream_t s) {
     hipError_t e;
     switch (c.k) {
-    case MGEMM_KERNEL_SKINNY_SK: e = mgemm::launch_skinny_sk(p, h->ws, c.ksplit, s); break;
+    case MGEMM_KERNEL_SKINNY_SK: e = mgemm::launch_skinny_sk(p, ws, c.ksplit, s); break;
     case MGEMM_KERNEL_GENERAL: e = mgemm::launch_general(p, s); break;
     case MGEMM_KERNEL_F32_MFMA: e = mgemm::launch_f32_mfma(p, s); break;
     case MGEMM_KERNEL_H_256x256:
@@ -277,26 +293,25 @@ mgemm_status_t launch(mgemm_handle_t h, const Problem& p, Choice c, hipStream_t 
     case MGEMM_KERNEL_SKINNY: e = mgemm::launch_skinny(p, s); break;
     case MGEMM_KERNEL_F32_FAST: e = mgemm::launch_f32_fast(p, true, s); break;
     case MGEMM_KERNEL_F32_FAST_128: e = mgemm::launch_f32_fast(p, false, s); break;
-    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, c.ksplit, h->ws, s); break;
-    case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, c.ksplit, h->ws, s); break;
-    case MGEMM_KERNEL_H_DMA_128: e = mgemm::launch_h_dma(p, 192, c.ksplit, h->ws, s, 128); break;
+    case MGEMM_KERNEL_H_DMA_256: e = mgemm::launch_h_dma(p, 256, c.ksplit, ws, s); break;
+    case MGEMM_KERNEL_H_DMA_192: e = mgemm::launch_h_dma(p, 192, c.ksplit, ws, s); break;
+    case MGEMM_KERNEL_H_DMA_128: e = mgemm::launch_h_dma(p, 192, c.ksplit, ws, s, 128); break;
     case MGEMM_KERNEL_F32_FAST_U: e = mgemm::launch_f32_unaligned(p, s); break;
-    case MGEMM_KERNEL_F32_SK: e = mgemm::launch_f32_sk(p, h->ws, s); break;
+    case MGEMM_KERNEL_F32_SK: e = mgemm::launch_f32_sk(p, ws, s); break;
     default: return MGEMM_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
-namespace {
-
-mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
+mgemm_status_t run_core(int num_cu, const mgemm::Workspace& ws, const Table* table,
+                        mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
                         void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
-                        hipStream_t stream) {
+                        hipStream_t stream, mgemm_status_t too_big) {
     Problem p;
-    mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                                     ldc, dtype, &p);
+    mgemm_status_t st = make_problem_on(num_cu, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb,
+                                        beta, C, ldc, dtype, &p);
     if (st != MGEMM_SUCCESS) return st;
     if (forced != MGEMM_KERNEL_AUTO && (forced <= 0 || forced >= MGEMM_KERNEL_COUNT))
         return MGEMM_ERR_INVALID_ARG;
@@ -312,13 +327,33 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mge
     }
     Choice c;
     if (forced == MGEMM_KERNEL_AUTO) {
-        c = choose(h, p);
+        c = choose_in(table, ws, p);
     } else {
         if (!variant_supports(p, forced)) return MGEMM_ERR_UNSUPPORTED;
-        c = {forced, forced_splits(p, h->ws, forced, ksplit)};
-        if (c.ksplit < 1) return MGEMM_ERR_UNSUPPORTED;
+        c = {forced, forced_splits(p, ws, forced, ksplit)};
+        if (c.ksplit < 1) {
+            // Tell a split (or stream-K) form that the workspace cannot hold
+            // apart from a variant that cannot run the shape at all: ask again
+            // with an unbounded workspace (sizes only; nothing is launched).
+            const mgemm::Workspace unbounded{(void*)256, (int64_t)1 << 62, (unsigned*)256,
+                                             (int64_t)1 << 40};
+            return forced_splits(p, unbounded, forced, ksplit) >= 1 ? too_big
+                                                                     : MGEMM_ERR_UNSUPPORTED;
+        }
     }
-    return launch(h, p, c, stream);
+    return launch_ws(ws, p, c, stream);
+}
+
+namespace {
+
+mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mgemm_layout_t layoutA,
+                        mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                        void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                        hipStream_t stream) {
+    if (!h) return MGEMM_ERR_INVALID_ARG;
+    return run_core(h->num_cu, h->ws, &h->table, forced, ksplit, layoutA, layoutB, M, N, K, alpha,
+                    A, lda, B, ldb, beta, C, ldc, dtype, epilogue, stream, MGEMM_ERR_UNSUPPORTED);
 }
 
 }  // namespace
@@ -586,6 +621,7 @@ const char* mgemm_status_string(mgemm_status_t s) {
     case MGEMM_ERR_UNSUPPORTED: return "unsupported";
     case MGEMM_ERR_HIP: return "HIP error";
     case MGEMM_ERR_ALLOC: return "allocation failed";
+    case MGEMM_ERR_SCRATCH: return "needs more scratch memory than the no-allocation entry point holds";
     }
     return "unknown";
 }

@@ -37,7 +37,9 @@ typedef enum {
     MGEMM_ERR_INVALID_ARG = 1,   /* bad size, enum, leading dimension or null pointer */
     MGEMM_ERR_UNSUPPORTED = 2,   /* device is not gfx950, or a forced kernel cannot run the problem */
     MGEMM_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed */
-    MGEMM_ERR_ALLOC = 4          /* host allocation failed */
+    MGEMM_ERR_ALLOC = 4,         /* host allocation failed */
+    MGEMM_ERR_SCRATCH = 5        /* mgemm_run_noalloc: the forced variant needs more scratch
+                                    memory than the library's static array holds */
 } mgemm_status_t;
 
 typedef enum {
@@ -421,6 +423,37 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
                              const float* sa, const void* B, int64_t ldb, const float* sb,
                              float beta, void* C, int64_t ldc, mgemm_dtype_t ctype,
                              hipStream_t stream);
+
+/*
+ * mgemm_run_noalloc -- mgemm_run_variant without a handle and without any
+ * device allocation, for callers that cannot allocate: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, validation, results and errors are those of mgemm_run_variant
+ * on the CURRENT HIP device (no dispatch table: the built-in model chooses
+ * when v is NULL or AUTO).  The split-K and stream-K forms take their FP32
+ * partial results and arrival counters from a static device array inside the
+ * library (MGEMM_NOALLOC_SCRATCH_BYTES of partials plus
+ * MGEMM_NOALLOC_COUNTERS counters, held on every GPU the library runs on
+ * until the process ends) instead of a handle's workspace; the first call on
+ * a device looks the array up and enqueues a small kernel on `stream` that
+ * zeroes the counters (every later call leaves them at zero).  With AUTO the
+ * model only picks forms that fit the array; a forced variant whose partials
+ * do not fit returns MGEMM_ERR_SCRATCH and enqueues nothing.
+ * Calls that overlap in time on one GPU (different streams, or different
+ * host threads) share the array and race: order them on one stream.
+ * Errors: as mgemm_run_variant; MGEMM_ERR_UNSUPPORTED also when the current
+ * device is not gfx950; MGEMM_ERR_HIP when the device cannot be queried or
+ * the array cannot be looked up.
+ */
+#define MGEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define MGEMM_NOALLOC_COUNTERS 16384u
+mgemm_status_t mgemm_run_noalloc(const mgemm_variant_t* v, mgemm_layout_t layoutA,
+                                 mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                                 float alpha, const void* A, int64_t lda, const void* B,
+                                 int64_t ldb, float beta, void* C, int64_t ldc,
+                                 mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
+                                 hipStream_t stream);
 
 /* Static strings; never NULL (unknown values give "unknown"). */
 const char* mgemm_status_string(mgemm_status_t s);
