@@ -12,8 +12,10 @@ inputs.
 
 Prints ONE JSON line.  `roofline` is measured live with HIP events around the
 timed launches on the stream the kernel runs on, and put against both the
-published peak and the peak at the shader clock read from the GPU while the
-timed launches ran (amdsmi); `cpu_baseline` times the CPU oracle on a bounded
+published peak and the peak at the shader clock the kernel ran at (read
+inside the kernel: the library's clock stamps over 20 further launches;
+amdsmi's firmware readings, which lag the fast clock changes under
+matrix-core load, are reported beside it); `cpu_baseline` times the CPU oracle on a bounded
 row sample of the same workload, and `parity_sample` checks the GPU output
 against the oracle (for the headline: four points in every 64 x 64 block,
 every tile-boundary row and column, and no unwritten output anywhere).  The
@@ -429,15 +431,56 @@ def measure(h, case, steps, warmup, rotate=1, settle_s=0.0, monitor=None):
     if monitor is not None:
         monitor.stop()
     per = sorted(a.elapsed_time(b) for a, b in ev)
+    clock = clock_window(h, launch, stream, total_ms / steps, host_s)
     return {
         "kernel": kname, "ms_per_step": total_ms / steps,
         "wall_ms_per_step": (wall1 - wall0) * 1e3 / steps,
         "host_ms_per_step": host_s * 1e3, "launch_ms_mean": total_ms / steps,
         "launch_ms_single_median": per[len(per) // 2],
         "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
-        "untimed_launches": n_pre, "window": (gpu0, wall1),
+        "untimed_launches": n_pre, "window": (gpu0, wall1), "clock_window": clock,
         "inputs": (A, B, C0), "out": dC[(steps - 1) % len(dC)],
     }
+
+
+def clock_window(h, launch, stream, ms_per_step, host_s, n_launch=20, cap=4096):
+    """The clock the kernel runs at, read inside it: `n_launch` more launches
+    after the timed ones, back to back behind a stream hold, each with its own
+    buffer for the library's clock stamps (every workgroup's shader-clock
+    cycles and 100 MHz real-time ticks at its start and end).  The MI355X
+    lowers its clock within microseconds under matrix-core load and raises it
+    as soon as the load ends, so a reading from outside the kernel (the
+    firmware's metrics, or a probe after it) does not give this clock.
+    Returns None when the workload's kernel records no stamps."""
+    import numpy as np
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    if h is None:
+        return None
+    buf = torch.zeros(n_launch * 4 * cap, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    hold_stream(stream, 1.5 * host_s * n_launch + 1e-4)
+    for i in range(n_launch):
+        mg.mgemm_set_clock_stamps(h, buf[i * 4 * cap:], cap)
+        launch(i)
+    mg.mgemm_set_clock_stamps(h, None, 0)
+    torch.cuda.synchronize()
+    st = buf.view(n_launch, cap, 4).cpu().numpy().astype(np.float64)
+    ok = st[:, :, 3] > st[:, :, 2]
+    if not ok.any():
+        return None
+    cyc = st[:, :, 1] - st[:, :, 0]
+    tck = st[:, :, 3] - st[:, :, 2]
+    mhz = np.where(ok, 100.0 * cyc / np.maximum(tck, 1), np.nan)
+    per_launch = np.nanmedian(mhz, axis=1)
+    wg_us = tck[ok] / 100.0
+    return {"sclk_mhz_median": round(float(np.nanmedian(per_launch)), 1),
+            "sclk_mhz_min": round(float(np.nanmin(mhz)), 1),
+            "sclk_mhz_max": round(float(np.nanmax(mhz)), 1),
+            "workgroups_per_launch": int(ok[-1].sum()), "launches": n_launch,
+            "workgroup_us_median": round(float(np.median(wg_us)), 2),
+            "method": "in-kernel stamps: s_memtime cycles over s_memrealtime 100 MHz ticks per "
+                      "workgroup (mgemm_set_clock_stamps), median over workgroups and launches"}
 
 
 def measure_mix(h, steps=20):
@@ -739,7 +782,8 @@ def print_summary(rows, kind):
 
 # ---------------------------------------------------------------------------
 def roofline_entry(case, r, hbm, clock):
-    """Achieved rate, peaks (published and at the measured clock) and fractions."""
+    """Achieved rate, peaks (published and at the measured clock) and fractions.
+    `clock` is measure()'s clock window (the probe's median clock)."""
     from dense_gemm_mgemm_amd import costmodel as cm
     flops, nbytes = algorithmic(case)
     s = r["launch_ms_mean"] * 1e-3
@@ -750,9 +794,10 @@ def roofline_entry(case, r, hbm, clock):
         unit, bound = "TFLOP/s", "mfma"
     e = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4)}
-    if not hbm and clock and clock.get("available"):
-        pk = peak * clock["sclk_mhz_median"] / PEAK_SCLK_MHZ
-        e.update(sclk_mhz=clock["sclk_mhz_median"], peak_at_sclk=round(pk, 1),
+    ik = (clock or {}).get("in_kernel")
+    if not hbm and ik and ik.get("sclk_mhz_median"):
+        pk = peak * ik["sclk_mhz_median"] / PEAK_SCLK_MHZ
+        e.update(sclk_mhz=ik["sclk_mhz_median"], peak_at_sclk=round(pk, 1),
                  frac_at_sclk=round(achieved / pk, 4))
     return e, flops, nbytes
 
@@ -807,7 +852,7 @@ def main():
     log("headline:", case.name)
     r = measure(h, case, args.steps, args.warmup, rotate=4 if hbm else 1, settle_s=args.settle,
                 monitor=monitor)
-    clock = monitor.summary(*r["window"])
+    clock = {"in_kernel": r["clock_window"], "amdsmi": monitor.summary(*r["window"])}
     case.inputs = r["inputs"]
     log("headline timed: %.5f ms per step, %d untimed launches before" % (
         r["ms_per_step"], r["untimed_launches"]))
@@ -875,8 +920,8 @@ def main():
             hb = is_hbm_bound(c)
             log("workload:", name)
             rr = measure(h, c, 20, 5, rotate=4 if hb else 1, settle_s=0.25, monitor=monitor)
-            ck = monitor.summary(*rr["window"])
-            rf, _, _ = roofline_entry(c, rr, hb, ck)
+            ck = rr["clock_window"]
+            rf, _, _ = roofline_entry(c, rr, hb, {"in_kernel": ck})
             ent = {"kernel": rr["kernel"], "launch_ms_mean": round(rr["launch_ms_mean"], 5),
                    "dtype": arith_dtype(c)}
             if hb:
@@ -885,8 +930,9 @@ def main():
                 ent.update(TFLOPs=rf["achieved"], frac_peak=rf["frac"])
                 if "frac_at_sclk" in rf:
                     ent.update(sclk_mhz=rf["sclk_mhz"], frac_at_sclk=rf["frac_at_sclk"])
-            if ck.get("available"):
-                ent["power_w"] = ck.get("power_w_median")
+            if ck is None:
+                am = monitor.summary(*rr["window"])
+                ent["sclk_mhz_amdsmi"] = am.get("sclk_mhz_median")
             cnt = counters_for(rr["kernel"], name)
             if cnt:
                 ent.update(traffic=cnt.get("bytes_per_launch"), mfma_busy=cnt.get("mfma_busy"))

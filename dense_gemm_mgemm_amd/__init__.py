@@ -37,7 +37,7 @@ EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "m
             "mgemm_select_variant", "mgemm_tune", "mgemm_table_export", "mgemm_table_import",
             "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_quantize_fp8", "mgemm_run_fp8",
             "mgemm_status_string",
-            "mgemm_kernel_name", "mgemm_num_cu", "mgemm_run_noalloc"]
+            "mgemm_kernel_name", "mgemm_num_cu", "mgemm_run_noalloc", "mgemm_set_clock_stamps"]
 
 
 class MgemmError(RuntimeError):
@@ -109,6 +109,8 @@ def load(path: str | None = None):
     lib.mgemm_kernel_name.restype = ctypes.c_char_p
     lib.mgemm_num_cu.argtypes = [vp]
     lib.mgemm_num_cu.restype = ci
+    lib.mgemm_set_clock_stamps.argtypes = [vp, vp, i64]
+    lib.mgemm_set_clock_stamps.restype = ci
     if path is None:
         _lib = lib
     return lib
@@ -339,3 +341,11 @@ def mgemm_kernel_name(k: int) -> str:
 
 def mgemm_num_cu(h) -> int:
     return load().mgemm_num_cu(h)
+
+
+def mgemm_set_clock_stamps(h, buf, nblocks: int) -> None:
+    """Measurement hook: buf (device, 4*nblocks int64, or None) receives each
+    workgroup's (cycles at start, at end, 100 MHz ticks at start, at end)."""
+    st = load().mgemm_set_clock_stamps(h, _ptr(buf), int(nblocks))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_set_clock_stamps")

@@ -33,7 +33,34 @@ struct Problem {
     int epilogue;    // Epilogue below, applied to alpha*acc + beta*C before the final rounding
     const void* B2;  // gated pair only: second B' (N-contiguous, leading dimension ldb2)
     int64_t ldb2;
+    // Clock stamps (measurement hook, off when null): workgroup b < stamps_cap
+    // of a kernel that records them stores 4 values at stamps[4b]: shader-clock
+    // cycles (s_memtime) at its start and end, and 100 MHz real-time ticks
+    // (s_memrealtime) at its start and end, taken by its first wave.
+    unsigned long long* stamps = nullptr;
+    int64_t stamps_cap = 0;
 };
+
+struct ClockStamp {
+    unsigned long long cycles, ticks;
+};
+__device__ __forceinline__ ClockStamp clock_stamp_begin() {
+    ClockStamp s;
+    s.ticks = __builtin_amdgcn_s_memrealtime();
+    s.cycles = __builtin_amdgcn_s_memtime();
+    return s;
+}
+// Thread 0 of the workgroup stores its stamps if the hook is on.
+__device__ __forceinline__ void clock_stamp_end(const Problem& p, const ClockStamp& s0) {
+    if (p.stamps == nullptr || (int64_t)blockIdx.x >= p.stamps_cap || threadIdx.x != 0) return;
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long* o = p.stamps + 4 * (int64_t)blockIdx.x;
+    o[0] = s0.cycles;
+    o[1] = c1;
+    o[2] = s0.ticks;
+    o[3] = r1;
+}
 
 // Device workspace of a handle: FP32 partial results and per-block arrival
 // counters (zero between calls) for kernels that split K over workgroups.

@@ -47,6 +47,8 @@ struct mgemm_handle_s {
     int num_cu;
     mgemm::Workspace ws;          // device memory owned by the handle
     mgemm_host::Table table;      // measured choices (mgemm_tune / mgemm_table_import)
+    unsigned long long* stamps;   // clock-stamp buffer (mgemm_set_clock_stamps), or null
+    int64_t stamps_cap;           // workgroups it has room for
 };
 
 namespace mgemm_host {
@@ -79,6 +81,7 @@ mgemm_status_t run_core(int num_cu, const mgemm::Workspace& ws, const Table* tab
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
                         void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
-                        hipStream_t stream, mgemm_status_t too_big);
+                        hipStream_t stream, mgemm_status_t too_big,
+                        unsigned long long* stamps = nullptr, int64_t stamps_cap = 0);
 
 }  // namespace mgemm_host

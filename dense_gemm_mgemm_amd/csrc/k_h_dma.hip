@@ -190,6 +190,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     constexpr int B_ROW = G::B_ROW, OUT = G::OUT;
     using Fr = Frags<TM, TN>;
     extern __shared__ __align__(16) unsigned char smem[];
+    const ClockStamp stamp0 = clock_stamp_begin();
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -451,6 +452,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
                     const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                     *(f32x4*)(dst + (int64_t)((tm * TN + tn) * 4 + q) * NT * 4) = v;
                 }
+        clock_stamp_end(p, stamp0);
         return;
     }
 
@@ -492,6 +494,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
             }
         }
     }
+    clock_stamp_end(p, stamp0);
 }
 
 // Second split-K phase: one thread per 16-byte chunk of one tile's

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     constexpr int SLOT = W_BYTES + X_BYTES;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int last_flag;
+    const ClockStamp stamp0 = clock_stamp_begin();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -299,7 +300,10 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
             last_flag = old == (unsigned)(sa.ksplit - 1);
         }
         __syncthreads();
-        if (!last_flag) return;
+        if (!last_flag) {
+            clock_stamp_end(p, stamp0);
+            return;
+        }
         if (tid == 0) sa.cnt[blk] = 0u;
         // Last arrival: every partial of the block is complete.  Each row is
         // summed over ranges 0, 1, ..., ksplit-1 in that order (own range from
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     // ---- epilogue: alpha, beta, one rounding, row-contiguous stores ----------
     uint16_t* C = (uint16_t*)p.C;
     const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
-    if (n >= nlim) return;
+    if (n >= nlim) return;              // never thread 0: n = 0 < nlim
     with_epilogue(p.epilogue, [&](auto E) {
         constexpr int EPI = decltype(E)::value;
         for (int m = w; m < M; m += 4) {
@@ -389,6 +393,7 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
             store_out4<DT, EPI>(crow, n, nlim, vec_ok, p.beta, v);
         }
     });
+    clock_stamp_end(p, stamp0);
 }
 
 template <int DT, int MT, bool BKC>

@@ -308,11 +308,14 @@ mgemm_status_t run_core(int num_cu, const mgemm::Workspace& ws, const Table* tab
                         mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K, float alpha,
                         const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
                         void* C, int64_t ldc, mgemm_dtype_t dtype, mgemm_epilogue_t epilogue,
-                        hipStream_t stream, mgemm_status_t too_big) {
+                        hipStream_t stream, mgemm_status_t too_big,
+                        unsigned long long* stamps, int64_t stamps_cap) {
     Problem p;
     mgemm_status_t st = make_problem_on(num_cu, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb,
                                         beta, C, ldc, dtype, &p);
     if (st != MGEMM_SUCCESS) return st;
+    p.stamps = stamps;
+    p.stamps_cap = stamps ? stamps_cap : 0;
     if (forced != MGEMM_KERNEL_AUTO && (forced <= 0 || forced >= MGEMM_KERNEL_COUNT))
         return MGEMM_ERR_INVALID_ARG;
     if (ksplit < 0 || ksplit > MGEMM_MAX_KSPLIT || (forced == MGEMM_KERNEL_AUTO && ksplit != 0))
@@ -353,7 +356,8 @@ mgemm_status_t run_impl(mgemm_handle_t h, mgemm_kernel_t forced, int ksplit, mge
                         hipStream_t stream) {
     if (!h) return MGEMM_ERR_INVALID_ARG;
     return run_core(h->num_cu, h->ws, &h->table, forced, ksplit, layoutA, layoutB, M, N, K, alpha,
-                    A, lda, B, ldb, beta, C, ldc, dtype, epilogue, stream, MGEMM_ERR_UNSUPPORTED);
+                    A, lda, B, ldb, beta, C, ldc, dtype, epilogue, stream, MGEMM_ERR_UNSUPPORTED,
+                    h->stamps, h->stamps_cap);
 }
 
 }  // namespace
@@ -375,6 +379,8 @@ mgemm_status_t mgemm_create(mgemm_handle_t* out) {
     if (!h) return MGEMM_ERR_ALLOC;
     h->device = dev;
     h->num_cu = prop.multiProcessorCount;
+    h->stamps = nullptr;
+    h->stamps_cap = 0;
     h->ws = mgemm::Workspace{nullptr, 0, nullptr, 0};
     const int64_t part_bytes = (int64_t)128 << 20, ncounters = (int64_t)1 << 16;
     void* part = nullptr;
@@ -463,6 +469,8 @@ mgemm_status_t mgemm_run_gated_ex(mgemm_handle_t h, int32_t ksplit, int64_t M, i
     if (p.M == 0 || p.N == 0) return MGEMM_SUCCESS;
     p.B2 = Wu;
     p.ldb2 = ldw;
+    p.stamps = h->stamps;
+    p.stamps_cap = h->stamps ? h->stamps_cap : 0;
     if (p.K == 0) {
         // G = U = 0, so Z = SiLU(0) * 0 = 0.
         p.beta = 0.0f;
@@ -652,5 +660,12 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
 }
 
 int mgemm_num_cu(mgemm_handle_t h) { return h ? h->num_cu : 0; }
+
+mgemm_status_t mgemm_set_clock_stamps(mgemm_handle_t h, uint64_t* buf, int64_t nblocks) {
+    if (!h || nblocks < 0 || (buf != nullptr && nblocks == 0)) return MGEMM_ERR_INVALID_ARG;
+    h->stamps = (unsigned long long*)buf;
+    h->stamps_cap = buf ? nblocks : 0;
+    return MGEMM_SUCCESS;
+}
 
 }  // extern "C"

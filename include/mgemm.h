@@ -462,6 +462,31 @@ const char* mgemm_kernel_name(mgemm_kernel_t k);
 /* Number of compute units of the handle's device (0 if h is NULL). */
 int mgemm_num_cu(mgemm_handle_t h);
 
+/*
+ * mgemm_set_clock_stamps -- measurement hook: the shader clock a kernel
+ * actually ran at.  The MI355X lowers its clock within microseconds under
+ * heavy matrix-core load, so the clock that sets a kernel's peak can only be
+ * read inside the kernel (the SGEMM report, "how the cuBLAS denominator was
+ * fixed": the peak is re-derived at the clock measured while running).
+ * With buf non-NULL, every later launch through this handle of the
+ * direct-to-LDS FP16/BF16 kernels (MGEMM_KERNEL_H_DMA_256/_192/_128 and the
+ * gated pair; for a split of K, its first launch) and of
+ * MGEMM_KERNEL_SKINNY_SK has each
+ * workgroup b < nblocks store, from its first wave,
+ *     buf[4b]   shader-clock cycles at its start, buf[4b+1] at its end,
+ *     buf[4b+2] 100 MHz real-time ticks at its start, buf[4b+3] at its end,
+ * so its clock is 100 MHz * (buf[4b+1] - buf[4b]) / (buf[4b+3] - buf[4b+2]).
+ * Other kernels leave buf alone.  buf NULL (nblocks 0) turns the hook off.
+ *   buf : device buffer of 4 * nblocks uint64 values, owned by the caller,
+ *         alive while launches that use it are pending.
+ * The setting is read when a call is enqueued, so changing it between calls
+ * (for a buffer per call) is fine.  Costs two scalar reads at the start and
+ * one store at the end of each workgroup.
+ * Errors: MGEMM_ERR_INVALID_ARG for a NULL handle, nblocks < 0, or buf
+ * non-NULL with nblocks 0.
+ */
+mgemm_status_t mgemm_set_clock_stamps(mgemm_handle_t h, uint64_t* buf, int64_t nblocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,3 +84,7 @@ def test_create_without_gpu_fails_cleanly():
     st = mg.load().mgemm_create(ctypes.byref(h))
     assert st in (mg.MGEMM_ERR_HIP, mg.MGEMM_ERR_UNSUPPORTED)
     assert h.value is None
+
+
+def test_set_clock_stamps_needs_a_handle():
+    assert mg.load().mgemm_set_clock_stamps(None, None, 0) == mg.MGEMM_ERR_INVALID_ARG
