@@ -95,11 +95,13 @@ constexpr int A_ROW = BK * 2;                               // bytes per A row o
 // blocks of the same outputs in matching registers.
 // BMT = 128 halves the tile height for short M (the four waves then hold
 // 64 x BN/2 each): a 128-row problem no longer pays for 256 rows of MFMA work.
+// BMT = 64 (four waves of 32 x BN/2) is for 32 < M <= 64, where the product
+// streams B from HBM and half of a 128-row tile's rows would be padding.
 template <int BN, bool DUAL, int BMT = 256>
 struct Cfg {
     static_assert(BN == 256 || BN == 192, "tile width");
     static_assert(!DUAL || BN == 192, "the gated pair uses the 192-wide slot");
-    static_assert(BMT == 256 || BMT == 128, "tile height");
+    static_assert(BMT == 256 || BMT == 128 || BMT == 64, "tile height");
     static constexpr int BM = BMT;
     static constexpr int A_BYTES = BM * A_ROW;              // 16 or 8 KiB
     static constexpr int A_COPIES = BM / 64;                // 1 KiB A copies per wave per slice
@@ -439,11 +441,14 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     }
 
     if constexpr (EPI == EPI_PARTIAL) {
-        // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3].
+        // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3], all of
+        // one output row (lane & 31 of block tm); rows past M are not stored
+        // (the second phase reads only rows below M).
         float* dst = sp.part + ((int64_t)(tmi * tiles_n + tni) * sp.ksplit + split) *
                                    (int64_t)(NT * TM * TN * 16) + 4 * tid;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
+        for (int tm = 0; tm < TM; ++tm) {
+            if (G::WROWS * wm + 32 * tm + (lane & 31) >= mlim) continue;
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
@@ -452,6 +457,7 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
                     const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                     *(f32x4*)(dst + (int64_t)((tm * TN + tn) * 4 + q) * NT * 4) = v;
                 }
+        }
         clock_stamp_end(p, stamp0);
         return;
     }
@@ -608,7 +614,8 @@ hipError_t launch_dt(const Problem& p, int ksplit, const Workspace& ws, hipStrea
 
 bool h_dma_supports(const Problem& p, int bn, int bm) {
     if (bn != 256 && bn != 192) return false;
-    if (bm != 256 && (bm != 128 || bn != 192 || !p.a_kc)) return false;   // 128 rows: 128x192, A' K-contiguous
+    // 128 or 64 rows: BN = 192 with A' K-contiguous only.
+    if (bm != 256 && ((bm != 128 && bm != 64) || bn != 192 || !p.a_kc)) return false;
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (!p.a_kc && p.b_kc) return false;
     // N-contiguous B' rows (M-contiguous A' columns) are read as 8-element
@@ -625,7 +632,8 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
     const int out = dual ? 96 : bn;
     const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + out - 1) / out);
     const int64_t nk = p.K / BK;
-    const int64_t tile_bytes = bm == 128 ? tile_part_bytes<192, false, 128>()
+    const int64_t tile_bytes = bm == 64    ? tile_part_bytes<192, false, 64>()
+                               : bm == 128 ? tile_part_bytes<192, false, 128>()
                                : (bn == 256 ? tile_part_bytes<256, false>() : tile_part_bytes<192, false>());
     if (requested <= 1 || nk < 2) return 1;
     int64_t ks = requested < nk ? requested : nk;
@@ -637,6 +645,13 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
 
 hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s,
                         int bm) {
+    if (bm == 64) {
+        if (p.b_kc)
+            return p.dtype == F16 ? launch_dt<F16, 192, false, true, false, 64>(p, ksplit, ws, s)
+                                  : launch_dt<BF16, 192, false, true, false, 64>(p, ksplit, ws, s);
+        return p.dtype == F16 ? launch_dt<F16, 192, false, false, false, 64>(p, ksplit, ws, s)
+                              : launch_dt<BF16, 192, false, false, false, 64>(p, ksplit, ws, s);
+    }
     if (bm == 128) {
         if (p.b_kc)
             return p.dtype == F16 ? launch_dt<F16, 192, false, true, false, 128>(p, ksplit, ws, s)

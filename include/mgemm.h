@@ -82,7 +82,9 @@ typedef enum {
                                     shares of all (tile, K slice) pairs, deterministic fix-up */
     MGEMM_KERNEL_H_DMA_128 = 18, /* FP16/BF16, A' K-contiguous (row-major A), 128x192 tiles, 4 waves
                                     of 64x96, direct-to-LDS ring (short M) */
-    MGEMM_KERNEL_COUNT = 19
+    MGEMM_KERNEL_H_DMA_64 = 19,  /* FP16/BF16, A' K-contiguous, 64x192 tiles, 4 waves of 32x96,
+                                    direct-to-LDS ring (32 < M <= 64: streams B from HBM) */
+    MGEMM_KERNEL_COUNT = 20
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */
@@ -200,8 +202,8 @@ mgemm_status_t mgemm_run_ex(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layou
  * Runtime", section 5.2.4: the order of a floating-point sum changes its last
  * bits), so a given variant gives the same bits on every run; different
  * splits round differently (within the tolerance of the sum).
- * Only MGEMM_KERNEL_H_DMA_256, MGEMM_KERNEL_H_DMA_192, MGEMM_KERNEL_H_DMA_128
- * and MGEMM_KERNEL_SKINNY_SK take ksplit > 1 (MGEMM_KERNEL_F32_SK balances K
+ * Only MGEMM_KERNEL_H_DMA_256, MGEMM_KERNEL_H_DMA_192, MGEMM_KERNEL_H_DMA_128,
+ * MGEMM_KERNEL_H_DMA_64 and MGEMM_KERNEL_SKINNY_SK take ksplit > 1 (MGEMM_KERNEL_F32_SK balances K
  * itself and takes 0 or 1); the number of ranges used is
  * ceil(S / ceil(S / ksplit)) for S = K / 32 slices.  The direct-to-LDS kernels
  * then run in two launches on `stream` (partial products, then the sum and

@@ -23,7 +23,7 @@ from workloads import CANARY, Case, c_initial, storage_view
 
 KERNELS_F32 = ["general", "f32_mfma", "f32_fast", "f32_fast_128", "f32_fast_u", "f32_sk"]
 KERNELS_16 = ["general", "h_mfma_256x256", "h_mfma_256x192", "h_mfma_128x128",
-              "h_dma_256x256", "h_dma_256x192", "h_dma_128x192"]
+              "h_dma_256x256", "h_dma_256x192", "h_dma_128x192", "h_dma_64x192"]
 
 
 def run_gpu(h, case: Case, kernel: str = "auto", inputs=None, stream=None, epilogue="none",

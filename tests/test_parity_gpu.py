@@ -389,9 +389,9 @@ def test_h_dma_split_k_bit_exact(h, M, N, K):
         case = W.Case("hsplit", M, N, K, dtype, kindA="int", kindB="int", kindC="int",
                       alpha=1.0, beta=-0.5, seeds=(M, N, K))
         inputs = case.make()
-        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192"):
+        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192", "h_dma_64x192"):
             bn = 256 if kernel.endswith("256") else 192
-            bm = 128 if "_128x" in kernel else 256
+            bm = 128 if "_128x" in kernel else (64 if "_64x" in kernel else 256)
             tiles = -(-M // bm) * -(-N // bn)
             for ks in (1, 2, 3, 5, 8, 32):
                 say("h_dma split", dtype, (M, N, K), kernel, ks)
@@ -420,7 +420,7 @@ def test_h_dma_b_k_contiguous_bit_exact(h, M, N, K):
         case = W.Case("hbkc", M, N, K, dtype, layoutB="col", kindA="int", kindB="int",
                       kindC="int", alpha=1.0, beta=-0.5, seeds=(M, N, K + 1))
         inputs = case.make()
-        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192"):
+        for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192", "h_dma_64x192"):
             for ks in (1, 3):
                 say("h_dma B K-contiguous", dtype, (M, N, K), kernel, ks)
                 P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks))
@@ -473,7 +473,7 @@ def test_skinny_weights_out_by_in_ffn_sampled(h, M):
     sel = mg.mgemm_select_variant(h, "row", "col", M, 12288, 4096, 1.0, 256, 4096, 256, 4096,
                                   0.0, 256, 12288, "bf16")
     say("skinny W^T ffn", M, sel)
-    assert sel[0] == ("skinny_sk" if M <= 32 else "h_dma_128x192")
+    assert sel[0] == ("skinny_sk" if M <= 32 else "h_dma_64x192")
     out = P.run_gpu(h, case)
     P.check_tolerance(case, *out, cols=[0, 255, 256, 12287])
 
@@ -692,7 +692,7 @@ def test_dispatch_choices(h):
     assert sel(W.ragged_f32()) == "f32_sk"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x192"
-    assert all(sel(W.ffn_bf16(m)) == ("skinny_sk" if m <= 32 else "h_dma_128x192")
+    assert all(sel(W.ffn_bf16(m)) == ("skinny_sk" if m <= 32 else "h_dma_64x192")
                for m in W.SKINNY_M)
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
