@@ -291,8 +291,11 @@ struct Frags {
 __device__ __forceinline__ f32x16 mfma8(const i32x4 (&x)[2], const i32x4 (&y)[2], f32x16 c) {
     const i32x8 xa = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 ya = __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    // Both operands E4M3 (format 0), unit block scales (E8M0 127 = 2^0).
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, c, 0, 0, 0, 127, 0, 127);
+    // Both operands E4M3 (format 0), no block scales: with both scale
+    // operands 0 the compiler emits the unscaled v_mfma_f32_32x32x64_f8f6f4
+    // (plain E4M3 products; the parity tests compare against the oracle bit
+    // for bit on integer codes).
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, c, 0, 0, 0, 0, 0, 0);
 }
 
 struct F8Args {
@@ -391,6 +394,7 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
     using Fr = Frags<TN>;
     extern __shared__ __align__(16) unsigned char smem[];
+    const ClockStamp stamp0 = clock_stamp_begin();
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -543,9 +547,11 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
                     const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                     *(f32x4*)(dst + (int64_t)((tm * TN + tn) * 4 + q) * NT * 4) = v;
                 }
+        clock_stamp_end(p, stamp0);
         return;
     }
     f8_epilogue<CT, BN>(acc, p, f.sa, f.sb, p.C, lane, wm, wn, m0, n0, mlim, nlim);
+    clock_stamp_end(p, stamp0);
 }
 
 // Second split-K phase: one thread per 16-byte chunk of a tile's

@@ -551,6 +551,8 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
     p.epilogue = mgemm::EPI_NONE;
     p.B2 = nullptr;
     p.ldb2 = 0;
+    p.stamps = h->stamps;
+    p.stamps_cap = h->stamps ? h->stamps_cap : 0;
     if (K == 0 || alpha == 0.f) {
         hipError_t e = mgemm::launch_scale(p, stream);
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;

@@ -472,8 +472,8 @@ int mgemm_num_cu(mgemm_handle_t h);
  * fixed": the peak is re-derived at the clock measured while running).
  * With buf non-NULL, every later launch through this handle of the
  * direct-to-LDS FP16/BF16 kernels (MGEMM_KERNEL_H_DMA_256/_192/_128 and the
- * gated pair; for a split of K, its first launch) and of
- * MGEMM_KERNEL_SKINNY_SK has each
+ * gated pair; for a split of K, its first launch), of MGEMM_KERNEL_SKINNY_SK
+ * and of the FP8 MFMA kernels (mgemm_run_fp8) has each
  * workgroup b < nblocks store, from its first wave,
  *     buf[4b]   shader-clock cycles at its start, buf[4b+1] at its end,
  *     buf[4b+2] 100 MHz real-time ticks at its start, buf[4b+3] at its end,
