@@ -74,7 +74,7 @@ KERNEL_SOURCE = {
     "h_dma_256x256": "k_h_dma.hip", "skinny": "k_skinny.hip",
     "skinny_sk": "k_skinny_sk.hip", "h_dma_256x192": "k_h_dma.hip", "f32_fast_u": "k_f32_mfma.hip",
     "h_dma_gated": "k_h_dma.hip", "fp8_quant+fp8_gemm": "k_f8.hip", "f32_sk": "k_f32_mfma.hip",
-    "h_dma_128x192": "k_h_dma.hip",
+    "h_dma_128x192": "k_h_dma.hip", "h_dma_64x192": "k_h_dma.hip",
 }
 
 
@@ -758,7 +758,8 @@ def summarize_pmc(path: str, steady_after_s: float):
         out.append({"kernel": name, "dispatches": len(ds), "steady": len(st),
                     "mean_us": statistics.fmean((d["end"] - d["start"]) / 1e3 for d in st),
                     "counters": {c: statistics.fmean(d["c"].get(c, 0.0) for d in st)
-                                 for c in names}})
+                                 for c in names},
+                    "counters_max": {c: max(d["c"].get(c, 0.0) for d in ds) for c in names}})
     return out
 
 
@@ -775,9 +776,54 @@ def print_summary(rows, kind):
                 f(r["steady_max_us"])))
     else:
         for r in rows:
-            print("`%s`: %d dispatches (%d settled), mean %.2f us; %s" % (
+            print("`%s`: %d dispatches (%d settled), mean %.2f us; %s; largest dispatch: %s" % (
                 r["kernel"][:110], r["dispatches"], r["steady"], r["mean_us"],
-                ", ".join("%s %.6g" % kv for kv in r["counters"].items())))
+                ", ".join("%s %.6g" % kv for kv in r["counters"].items()),
+                ", ".join("%s %.6g" % kv for kv in r["counters_max"].items())))
+
+
+def record_counters(workload: str, prof_dir: str, steady_after_s: float) -> dict:
+    """The counter entry of one workload from its rocprofv3 runs under
+    prof_dir (FETCH_SIZE/, WRITE_SIZE/ and SQ_VALU_MFMA_BUSY_CYCLES/, each a
+    --pmc run of `bench.py --workload W --only-headline --copy-probe 256`):
+    per step, the library kernels' settled per-dispatch FETCH_SIZE and
+    WRITE_SIZE (KiB) summed over the step's kernels and scaled by what the same
+    counters read for the 256 MiB device copy and the 256 MiB random fill of
+    the same run; the matrix-core busy share of the longest kernel.  Stored
+    in profiles/traffic.json under kernel/workload with the kernel source's
+    hash."""
+    def lib_rows(rows):
+        return [r for r in rows if r["kernel"].startswith("void mgemm::")]
+    fetch = summarize_pmc(os.path.join(prof_dir, "FETCH_SIZE"), steady_after_s)
+    write = summarize_pmc(os.path.join(prof_dir, "WRITE_SIZE"), steady_after_s)
+    mf = summarize_pmc(os.path.join(prof_dir, "SQ_VALU_MFMA_BUSY_CYCLES"), steady_after_s)
+    copy_kib = max(r["counters_max"].get("FETCH_SIZE", 0.0) for r in fetch
+                   if "copyBuffer" in r["kernel"])
+    fill_kib = max(r["counters_max"].get("WRITE_SIZE", 0.0) for r in write
+                   if not r["kernel"].startswith("void mgemm::"))
+    fs, ws = 262144.0 / copy_kib, 262144.0 / fill_kib
+    rd = sum(r["counters"]["FETCH_SIZE"] for r in lib_rows(fetch)) * 1024 * fs
+    wr = sum(r["counters"]["WRITE_SIZE"] for r in lib_rows(write)) * 1024 * ws
+    main = max(lib_rows(mf), key=lambda r: r["mean_us"])
+    c = main["counters"]
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024)
+    bj = [f for f in sorted(glob.glob(os.path.join(prof_dir, "bench_*.json")))]
+    kernel = json.loads(open(bj[0]).read().strip().splitlines()[-1])["config"]["kernel"]
+    return {"workload": workload, "kernel": kernel, "src_hash": src_hash(kernel),
+            "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "mfma_busy": round(busy, 4),
+            # GRBM_GUI_ACTIVE over a dispatch also counts its start-up: a clock
+            # from it means something only for long kernels.
+            "mfma_clock_ghz": round(c["GRBM_GUI_ACTIVE"] / 8 / (main["mean_us"] * 1e3), 3)
+            if main["mean_us"] > 200 else None,
+            "valu_per_mfma": round(c["SQ_INSTS_VALU"] / max(c["SQ_INSTS_MFMA"], 1), 2),
+            "kernels": [r["kernel"][:100] for r in lib_rows(fetch)],
+            "counters": "FETCH_SIZE, WRITE_SIZE (KiB per dispatch, one rocprofv3 --pmc run each, "
+                        "dispatches started at least %.1f s after the kernel's first) summed over the "
+                        "step's kernels, scaled by a 256 MiB device copy / random fill of the same "
+                        "run; busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 "
+                        "SIMDs) of the longest kernel" % steady_after_s}
 
 
 # ---------------------------------------------------------------------------
@@ -821,7 +867,25 @@ def main():
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--steady-after", type=float, default=1.0,
                     help="summaries: seconds after a kernel's first call before calls count as settled")
+    ap.add_argument("--record-counters", nargs=2, metavar=("WORKLOAD", "PROF_DIR"),
+                    help="write the workload's counter entry into profiles/traffic.json")
+    ap.add_argument("--merge-record", metavar="JSON",
+                    help="add an entry printed by --record-counters to profiles/traffic.json")
     args = ap.parse_args()
+    if args.record_counters or args.merge_record:
+        if args.record_counters:
+            e = record_counters(args.record_counters[0], args.record_counters[1],
+                                args.steady_after)
+        else:
+            e = json.load(open(args.merge_record))
+        p = os.path.join(ROOT, "profiles", "traffic.json")
+        tab = json.load(open(p)) if os.path.exists(p) else {}
+        tab["%s/%s" % (e["kernel"], e["workload"])] = e
+        with open(p, "w") as f:
+            json.dump(dict(sorted(tab.items())), f, indent=1)
+            f.write("\n")
+        print(json.dumps(e, indent=1))
+        return
     if args.summarize_trace or args.summarize_pmc:
         if args.summarize_trace:
             print_summary(summarize_trace(args.summarize_trace, args.steady_after), "trace")
