@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s and % of MFMA/FP32 peak (HBM GB/s for M≤64) vs CPU oracle, 1 GPU"
 DEFAULT_WORKLOAD = "hgemm_col_8192x8192x16384"
 PEAK_SCLK_MHZ = 2400.0          # the clock the published peaks are quoted at
+MAX_CV = 0.05                   # single-launch coefficient of variation accepted
 
 # The pages' own numbers for some workloads (other machines: context only,
 # never a target).
@@ -159,11 +160,12 @@ class GpuMonitor:
                 "accumulation_counter": m.get("accumulation_counter")}
 
     def health(self) -> dict | None:
-        """One reading before any timing, with the clock limits."""
+        """One reading (taken before and after the headline's timing), with the
+        clock limit; not ok when the hotspot is at 95 C or above."""
         r = self.read()
         if r is None:
             return {"available": False, "why": self.error}
-        out = {"available": True, "sclk_mhz_idle": r["sclk_mhz"], "power_w_idle": r["power_w"],
+        out = {"available": True, "sclk_mhz": r["sclk_mhz"], "power_w": r["power_w"],
                "temp_hotspot_c": r["temp_hotspot_c"], "temp_mem_c": r["temp_mem_c"],
                "throttle_status": r["throttle_status"]}
         try:
@@ -178,7 +180,7 @@ class GpuMonitor:
     def start(self, period_s: float = 0.002):
         if self.handle is None:
             return
-        self.samples = []
+        # Samples of earlier windows are kept: summary() selects by time.
         self._stop = threading.Event()
 
         def run():
@@ -431,6 +433,8 @@ def measure(h, case, steps, warmup, rotate=1, settle_s=0.0, monitor=None):
     if monitor is not None:
         monitor.stop()
     per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_single = sum(per) / len(per)
+    cv = (sum((x - mean_single) ** 2 for x in per) / len(per)) ** 0.5 / mean_single
     clock = clock_window(h, launch, stream, total_ms / steps, host_s)
     return {
         "kernel": kname, "ms_per_step": total_ms / steps,
@@ -438,7 +442,7 @@ def measure(h, case, steps, warmup, rotate=1, settle_s=0.0, monitor=None):
         "host_ms_per_step": host_s * 1e3, "launch_ms_mean": total_ms / steps,
         "launch_ms_single_median": per[len(per) // 2],
         "launch_ms_p10": per[len(per) // 10], "launch_ms_p90": per[(len(per) * 9) // 10],
-        "untimed_launches": n_pre, "window": (gpu0, wall1), "clock_window": clock,
+        "launch_cv": cv, "untimed_launches": n_pre, "window": (gpu0, wall1), "clock_window": clock,
         "inputs": (A, B, C0), "out": dC[(steps - 1) % len(dC)],
     }
 
@@ -916,7 +920,18 @@ def main():
     log("headline:", case.name)
     r = measure(h, case, args.steps, args.warmup, rotate=4 if hbm else 1, settle_s=args.settle,
                 monitor=monitor)
+    # A run whose single launches spread by more than 5% (coefficient of
+    # variation) is measured once more; the steadier of the two is reported.
+    attempts = 1
+    if r["launch_cv"] > MAX_CV:
+        log("single-launch CV %.3f above %.2f: measuring again" % (r["launch_cv"], MAX_CV))
+        r2 = measure(h, case, args.steps, 0, rotate=4 if hbm else 1, settle_s=args.settle,
+                     monitor=monitor)
+        attempts = 2
+        if r2["launch_cv"] < r["launch_cv"]:
+            r = r2
     clock = {"in_kernel": r["clock_window"], "amdsmi": monitor.summary(*r["window"])}
+    health_after = monitor.health()
     case.inputs = r["inputs"]
     log("headline timed: %.5f ms per step, %d untimed launches before" % (
         r["ms_per_step"], r["untimed_launches"]))
@@ -938,8 +953,11 @@ def main():
                 mfma_busy=cnt.get("mfma_busy"),
                 algorithmic_per_launch=flops if not hbm else nbytes,
                 launch_ms_mean=round(r["launch_ms_mean"], 5),
+                single_launch_ms_median=round(r["launch_ms_single_median"], 5),
                 single_launch_ms_p10=round(r["launch_ms_p10"], 5),
-                single_launch_ms_p90=round(r["launch_ms_p90"], 5))
+                single_launch_ms_p90=round(r["launch_ms_p90"], 5),
+                single_launch_cv=round(r["launch_cv"], 4),
+                cv_ok=r["launch_cv"] <= MAX_CV, attempts=attempts)
     value = flops / (r["ms_per_step"] * 1e-3) / 1e12 if not hbm else \
         nbytes / (r["ms_per_step"] * 1e-3) / 1e9
     line = {
@@ -956,7 +974,7 @@ def main():
                    "pages_context": PAGES_CONTEXT.get(case.name)},
         "roofline": roof,
         "clock": clock,
-        "health": health,
+        "health": health, "health_after": health_after,
         "cpu_baseline": None,
         "src_hash": src_hash(),
     }
@@ -987,7 +1005,8 @@ def main():
             ck = rr["clock_window"]
             rf, _, _ = roofline_entry(c, rr, hb, {"in_kernel": ck})
             ent = {"kernel": rr["kernel"], "launch_ms_mean": round(rr["launch_ms_mean"], 5),
-                   "dtype": arith_dtype(c)}
+                   "single_launch_ms_median": round(rr["launch_ms_single_median"], 5),
+                   "single_launch_cv": round(rr["launch_cv"], 4), "dtype": arith_dtype(c)}
             if hb:
                 ent.update(GBs=rf["achieved"], frac_hbm=rf["frac"])
             else:
