@@ -471,7 +471,7 @@ int mgemm_num_cu(mgemm_handle_t h);
  * read inside the kernel (the SGEMM report, "how the cuBLAS denominator was
  * fixed": the peak is re-derived at the clock measured while running).
  * With buf non-NULL, every later launch through this handle of the
- * direct-to-LDS FP16/BF16 kernels (MGEMM_KERNEL_H_DMA_256/_192/_128 and the
+ * direct-to-LDS FP16/BF16 kernels (MGEMM_KERNEL_H_DMA_256/_192/_128/_64 and the
  * gated pair; for a split of K, its first launch), of MGEMM_KERNEL_SKINNY_SK
  * and of the FP8 MFMA kernels (mgemm_run_fp8) has each
  * workgroup b < nblocks store, from its first wave,
