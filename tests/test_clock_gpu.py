@@ -42,6 +42,8 @@ CASES = [
      "h_dma_128x192", 4, 8 * 8 * 4),
     (W.Case("skinny", 16, 4096, 4096, "bf16", kindA="int", kindB="int", seeds=(7, 8, 9)),
      "skinny_sk", 4, 16 * 4),
+    (W.Case("m64", 64, 3072, 4096, "bf16", kindA="int", kindB="int", seeds=(10, 11, 12)),
+     "h_dma_64x192", 4, 16 * 4),
 ]
 
 
@@ -90,3 +92,38 @@ def test_set_clock_stamps_rejects_bad_arguments(h):
         with pytest.raises(mg.MgemmError) as ei:
             mg.mgemm_set_clock_stamps(h, *args)
         assert ei.value.status == mg.MGEMM_ERR_INVALID_ARG
+
+
+def test_fp8_stamps_cover_the_grid_and_leave_results_alone(h):
+    """The FP8 MFMA kernel (256x192 tiles: 2 x 4 workgroups here) records
+    stamps; its codes and scaled output are the same bits with the hook on."""
+    M, N, K = 512, 768, 1024
+    g = torch.Generator().manual_seed(21)
+    x = (torch.rand(M, K, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    w = (torch.rand(N, K, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    qx = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+    qw = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda")
+    mg.mgemm_quantize_fp8(h, M, K, x, K, "bf16", qx, K, sx)
+    mg.mgemm_quantize_fp8(h, N, K, w, K, "bf16", qw, K, sw)
+
+    def run(out):
+        mg.mgemm_run_fp8(h, "f8_mfma_256x192", M, N, K, 1.0, qx, K, sx, qw, K, sw, 0.0, out, N,
+                         "bf16", ksplit=1)
+
+    ref = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    run(ref)
+    wgs, cap = 2 * 4, 16
+    buf = torch.zeros(4 * cap, dtype=torch.int64, device="cuda")
+    got = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    mg.mgemm_set_clock_stamps(h, buf, cap)
+    try:
+        run(got)
+    finally:
+        mg.mgemm_set_clock_stamps(h, None, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    st = buf.view(cap, 4).cpu()
+    written = (st[:, 3] > st[:, 2]) & (st[:, 1] > st[:, 0])
+    assert int(written[:wgs].sum()) == wgs and int(written[wgs:].sum()) == 0, st
