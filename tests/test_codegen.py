@@ -20,17 +20,29 @@ HIPCC = "/opt/rocm/bin/hipcc"
 _BUILT = {}
 
 
+def _compile(name, out_dir):
+    out = os.path.join(out_dir, name + ".s")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-S", "-O3",
+                        "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-Rpass-analysis=kernel-resource-usage",
+                        "-I" + os.path.join(ROOT, "include"), os.path.join(CSRC, name),
+                        "-o", out], check=True, capture_output=True, text=True)
+    with open(out) as f:
+        return f.read(), r.stderr
+
+
 def device_build(name, tmp_path):
     """gfx950 assembly of one source and the compiler's per-kernel resource
-    remarks, from a single compile shared by every test of this module."""
+    remarks, from a single compile shared by every test of this module.  The
+    first call compiles every kernel source at once, a few at a time."""
+    if not _BUILT:
+        from concurrent.futures import ThreadPoolExecutor
+        names = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+        with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+            for n, res in zip(names, ex.map(lambda n: _compile(n, str(tmp_path)), names)):
+                _BUILT[n] = res
     if name not in _BUILT:
-        out = tmp_path / (name + ".s")
-        r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-S", "-O3",
-                            "-std=c++17", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                            "-Rpass-analysis=kernel-resource-usage",
-                            "-I" + os.path.join(ROOT, "include"), os.path.join(CSRC, name),
-                            "-o", str(out)], check=True, capture_output=True, text=True)
-        _BUILT[name] = (out.read_text(), r.stderr)
+        _BUILT[name] = _compile(name, str(tmp_path))
     return _BUILT[name]
 
 
