@@ -72,6 +72,66 @@ def operand(kind: str, seed: int, rows: int, cols: int, layout: str, ld: int, dt
     return cast(buf.reshape(-1)[: max(outer, 1) * ld], dtype)
 
 
+# ---------------------------------------------------------------------------
+# Operands too large to draw on the host (more than 2^31 elements): element
+# (r, c) of a matrix with `cols` columns is a function of the counter
+# r * cols + c and a seed, so a device fills the whole buffer and the host
+# recomputes only the rows and columns it checks.  Values are -1, 0 or 1
+# (exact in every storage type; integer sums stay exact in FP32).  The mixing
+# steps are the 32-bit finaliser of MurmurHash3 (Appleby), applied to the
+# counter's low and high words.
+# ---------------------------------------------------------------------------
+_M32 = 0xFFFFFFFF
+
+
+def _fmix32_np(h):
+    h = h & _M32
+    h ^= h >> 16
+    h = (h * 0x85EBCA6B) & _M32
+    h ^= h >> 13
+    h = (h * 0xC2B2AE35) & _M32
+    h ^= h >> 16
+    return h
+
+
+def hashed_values(rows: np.ndarray, cols: np.ndarray, ncols: int, seed: int) -> np.ndarray:
+    """float64 values of elements (rows[i], cols[j]) of a counter-hashed
+    matrix with `ncols` columns (an outer grid, len(rows) x len(cols))."""
+    n = (np.asarray(rows, np.uint64)[:, None] * np.uint64(ncols) +
+         np.asarray(cols, np.uint64)[None, :])
+    h = _fmix32_np((n & np.uint64(_M32)) ^ np.uint64(seed & _M32))
+    h = _fmix32_np(h ^ (n >> np.uint64(32)))
+    return (h % np.uint64(3)).astype(np.float64) - 1.0
+
+
+def _fmix32_torch(h):
+    h = h & _M32
+    h = h ^ (h >> 16)
+    h = (h * 0x85EBCA6B) & _M32
+    h = h ^ (h >> 13)
+    h = (h * 0xC2B2AE35) & _M32
+    h = h ^ (h >> 16)
+    return h
+
+
+def hashed_operand(nrows: int, ncols: int, seed: int, dtype: str, device,
+                   chunk: int = 1 << 26) -> torch.Tensor:
+    """The whole nrows x ncols counter-hashed matrix, row-major, filled on
+    `device` a few rows at a time (int64 arithmetic: every product of a
+    32-bit value and a 32-bit constant fits, and only its low 32 bits are
+    kept)."""
+    out = torch.empty(nrows * ncols, dtype=TORCH_DTYPES[dtype], device=device)
+    step = max(1, chunk // max(ncols, 1))
+    c = torch.arange(ncols, dtype=torch.int64, device=device)
+    for r0 in range(0, nrows, step):
+        r = torch.arange(r0, min(nrows, r0 + step), dtype=torch.int64, device=device)
+        n = r[:, None] * ncols + c[None, :]
+        h = _fmix32_torch((n & _M32) ^ (seed & _M32))
+        h = _fmix32_torch(h ^ (n >> 32))
+        out[r0 * ncols:(r0 + len(r)) * ncols] = ((h % 3) - 1).reshape(-1).to(out.dtype)
+    return out
+
+
 # Canary bit patterns written into C before a call whose beta is 0 (quiet
 # NaNs): an output the library never wrote still holds one afterwards.
 CANARY = {"f32": 0x7FA5A5A5, "f16": 0x7E5A, "bf16": 0x7FA5}
