@@ -706,6 +706,42 @@ def stratified_sample(case, out_cpu):
     return rep
 
 
+def accumulation_check(h, case, out_cpu, kernel):
+    """The headline kernel's FP32 sums (mgemm_run_acc32) before the output
+    rounding: their error at four oracle points in every 64 x 64 block against
+    the bare 16-bit tolerance, and whether the timed 16-bit output is exactly
+    those sums rounded to nearest even everywhere in C."""
+    import numpy as np
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    import oracle
+    from tests import parity as P
+    from workloads import storage_view, TORCH_DTYPES
+    A, B, _ = case.inputs
+    if kernel not in ("h_dma_256x256", "h_dma_256x192") or case.dtype == "f32" or case.beta != 0:
+        return None
+    t0 = time.perf_counter()
+    dA, dB = A.cuda(), B.cuda()
+    C32 = torch.full((case.c_numel(),), float("nan"), dtype=torch.float32, device="cuda")
+    mg.mgemm_run_acc32(h, kernel, case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha,
+                       dA, case.lda, dB, case.ldb, C32, case.ldc, case.dtype)
+    r16 = C32.to(TORCH_DTYPES[case.dtype]).view(torch.int16).cpu().numpy().view(np.uint16)
+    c32 = C32.cpu().numpy()
+    del dA, dB, C32
+    mask = ~P.padding_mask(case)
+    same = int(np.count_nonzero(r16[mask] == storage_view(out_cpu)[mask]))
+    pi, pj = P.block_points(case.M, case.N, 64, 4, seed=11)
+    exact = oracle.gemm_points(case.layoutA, case.layoutB, case.M, case.N, case.K, case.alpha,
+                               storage_view(A), case.lda, storage_view(B), case.ldb, 0.0, None,
+                               case.ldc, case.dtype, pi, pj)
+    err = np.abs(P.logical(case, c32)[pi, pj].astype(np.float64) - exact)
+    tol = P.tol_half(case.K)
+    return {"points": int(pi.size), "fp32_max_err": float(err.max()), "bare_tol": tol,
+            "ok": bool(err.max() <= tol) and same == int(mask.sum()),
+            "output_is_rounded_sums": same == int(mask.sum()), "outputs": int(mask.sum()),
+            "s": round(time.perf_counter() - t0, 2)}
+
+
 # ---------------------------------------------------------------------------
 # Committed counter summaries
 # ---------------------------------------------------------------------------
@@ -1022,6 +1058,10 @@ def main():
                 and case.extra.get("epilogue", "none") == "none":
             chk["stratified"] = stratified_sample(case, out_cpu)
             chk["ok"] = chk["ok"] and chk["stratified"]["ok"]
+            acc = accumulation_check(h, case, out_cpu, line["config"]["kernel"])
+            if acc is not None:
+                chk["fp32_sums"] = acc
+                chk["ok"] = chk["ok"] and acc["ok"]
         line["parity_sample"] = chk
         if not chk["ok"]:
             log("PARITY FAILURE on the sample:", chk)

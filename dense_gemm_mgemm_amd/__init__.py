@@ -38,7 +38,8 @@ EXPORTED = ["mgemm_create", "mgemm_destroy", "mgemm_run", "mgemm_run_kernel", "m
             "mgemm_select_variant", "mgemm_tune", "mgemm_table_export", "mgemm_table_import",
             "mgemm_table_clear", "mgemm_weighted_choice", "mgemm_quantize_fp8", "mgemm_run_fp8",
             "mgemm_status_string",
-            "mgemm_kernel_name", "mgemm_num_cu", "mgemm_run_noalloc", "mgemm_set_clock_stamps"]
+            "mgemm_kernel_name", "mgemm_num_cu", "mgemm_run_noalloc", "mgemm_set_clock_stamps",
+            "mgemm_run_acc32"]
 
 
 class MgemmError(RuntimeError):
@@ -102,8 +103,10 @@ def load(path: str | None = None):
                  "mgemm_run_gated", "mgemm_run_gated_ex", "mgemm_run_variant",
                  "mgemm_select_variant", "mgemm_select_kernel", "mgemm_tune", "mgemm_table_export",
                  "mgemm_table_import", "mgemm_table_clear", "mgemm_quantize_fp8",
-                 "mgemm_run_fp8", "mgemm_run_noalloc"):
+                 "mgemm_run_fp8", "mgemm_run_noalloc", "mgemm_run_acc32"):
         getattr(lib, name).restype = ci
+    lib.mgemm_run_acc32.argtypes = [vp, ci, ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, vp, i64,
+                                    ci, vp]
     lib.mgemm_status_string.argtypes = [ci]
     lib.mgemm_status_string.restype = ctypes.c_char_p
     lib.mgemm_kernel_name.argtypes = [ci]
@@ -181,6 +184,19 @@ def mgemm_run_kernel(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb
                                               beta, C, ldc, dtype), _stream(stream))
     if st != MGEMM_SUCCESS:
         raise MgemmError(st, "mgemm_run_kernel(%s)" % KERNELS[k] if 0 <= k < len(KERNELS) else k)
+
+
+def mgemm_run_acc32(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, C32, ldc, dtype,
+                    stream=None) -> None:
+    """C32 (FP32, layoutA's order) = alpha*op(A)op(B): the 16-bit direct-to-LDS
+    kernel's sums before the output rounding ("auto", "h_dma_256x256" or
+    "h_dma_256x192")."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    st = load().mgemm_run_acc32(h, k, _enum(layoutA, _LAYOUT), _enum(layoutB, _LAYOUT), int(M),
+                                int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb),
+                                _ptr(C32), int(ldc), _enum(dtype, _DTYPE), _stream(stream))
+    if st != MGEMM_SUCCESS:
+        raise MgemmError(st, "mgemm_run_acc32")
 
 
 def mgemm_run_ex(h, kernel, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype,

@@ -320,6 +320,9 @@ int h_dma_splits(const Problem& p, int bn, bool dual, int requested, const Works
                  int bm = 256);
 hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& ws, hipStream_t s,
                         int bm = 256);
+// alpha * the FP32 accumulators of the 256-row direct-to-LDS kernel (one K
+// range) into p.C as FP32 with leading dimension p.ldc.
+hipError_t launch_h_dma_acc32(const Problem& p, int bn, hipStream_t s);
 bool h_gated_supports(const Problem& p);
 hipError_t launch_h_gated(const Problem& p, int ksplit, const Workspace& ws, hipStream_t s,
                           int bm = 256);

@@ -73,6 +73,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Epilogue of the first split-K phase: FP32 accumulators to the workspace.
 constexpr int EPI_PARTIAL = 2;
+// alpha times the FP32 accumulators, stored as FP32 in C's place with C's
+// leading dimension (mgemm_run_acc32): the same sums the 16-bit epilogue
+// rounds once.
+constexpr int EPI_ACC32 = 3;
 
 // K-range arguments.  Without a split: ksplit = 1, nks = K / 32, part unused.
 struct HSplit {
@@ -465,6 +469,36 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
         return;
     }
 
+    if constexpr (EPI == EPI_ACC32) {
+        static_assert(!DUAL, "plain products only");
+        float* C32 = (float*)p.C;
+        const bool vec4 = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 15) == 0);
+        const int fr = lane & 31, nq = 4 * (lane >> 5);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int mi = G::WROWS * wm + 32 * tm + fr;
+            if (mi >= mlim) continue;
+            float* crow = C32 + (m0 + mi) * p.ldc + n0;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ni = G::WN * wn + 32 * tn + 8 * q + nq;
+                    const f32x4 v = {p.alpha * acc[tm][tn][4 * q], p.alpha * acc[tm][tn][4 * q + 1],
+                                     p.alpha * acc[tm][tn][4 * q + 2], p.alpha * acc[tm][tn][4 * q + 3]};
+                    if (vec4 && ni + 4 <= nlim) {
+                        *(f32x4*)(crow + ni) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (ni + e < nlim) crow[ni + e] = v[e];
+                    }
+                }
+        }
+        clock_stamp_end(p, stamp0);
+        return;
+    }
+
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
     uint16_t* C = (uint16_t*)p.C;
     const bool vec_ok = (p.ldc % 4 == 0) && (((uintptr_t)p.C & 7) == 0);
@@ -681,6 +715,29 @@ hipError_t launch_h_dma(const Problem& p, int bn, int ksplit, const Workspace& w
                               : launch_dt<BF16, 192, false>(p, ksplit, ws, s);
     return p.dtype == F16 ? launch_dt<F16, 256, false>(p, ksplit, ws, s)
                           : launch_dt<BF16, 256, false>(p, ksplit, ws, s);
+}
+
+hipError_t launch_h_dma_acc32(const Problem& p, int bn, hipStream_t s) {
+    const HSplit sp{nullptr, 1, (int)(p.K / BK)};
+    if (!p.a_kc) {
+        if (bn == 192)
+            return p.dtype == F16 ? launch_epi<F16, 192, false, EPI_ACC32, false, true, 256>(p, sp, s)
+                                  : launch_epi<BF16, 192, false, EPI_ACC32, false, true, 256>(p, sp, s);
+        return p.dtype == F16 ? launch_epi<F16, 256, false, EPI_ACC32, false, true, 256>(p, sp, s)
+                              : launch_epi<BF16, 256, false, EPI_ACC32, false, true, 256>(p, sp, s);
+    }
+    if (p.b_kc) {
+        if (bn == 192)
+            return p.dtype == F16 ? launch_epi<F16, 192, false, EPI_ACC32, true, false, 256>(p, sp, s)
+                                  : launch_epi<BF16, 192, false, EPI_ACC32, true, false, 256>(p, sp, s);
+        return p.dtype == F16 ? launch_epi<F16, 256, false, EPI_ACC32, true, false, 256>(p, sp, s)
+                              : launch_epi<BF16, 256, false, EPI_ACC32, true, false, 256>(p, sp, s);
+    }
+    if (bn == 192)
+        return p.dtype == F16 ? launch_epi<F16, 192, false, EPI_ACC32, false, false, 256>(p, sp, s)
+                              : launch_epi<BF16, 192, false, EPI_ACC32, false, false, 256>(p, sp, s);
+    return p.dtype == F16 ? launch_epi<F16, 256, false, EPI_ACC32, false, false, 256>(p, sp, s)
+                          : launch_epi<BF16, 256, false, EPI_ACC32, false, false, 256>(p, sp, s);
 }
 
 bool h_gated_supports(const Problem& p) {

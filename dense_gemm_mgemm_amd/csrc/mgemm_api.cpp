@@ -618,6 +618,34 @@ mgemm_status_t mgemm_select_kernel(mgemm_handle_t h, mgemm_layout_t layoutA,
     return MGEMM_SUCCESS;
 }
 
+mgemm_status_t mgemm_run_acc32(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
+                               mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                               float alpha, const void* A, int64_t lda, const void* B,
+                               int64_t ldb, float* C32, int64_t ldc, mgemm_dtype_t dtype,
+                               hipStream_t stream) {
+    if (kernel != MGEMM_KERNEL_AUTO && kernel != MGEMM_KERNEL_H_DMA_256 &&
+        kernel != MGEMM_KERNEL_H_DMA_192)
+        return MGEMM_ERR_INVALID_ARG;
+    Problem p;
+    mgemm_status_t st = make_problem(h, layoutA, layoutB, M, N, K, alpha, A, lda, B, ldb, 0.0f,
+                                     C32, ldc, dtype, &p);
+    if (st != MGEMM_SUCCESS) return st;
+    if (dtype != MGEMM_F16 && dtype != MGEMM_BF16) return MGEMM_ERR_UNSUPPORTED;
+    if (p.M == 0 || p.N == 0) return MGEMM_SUCCESS;
+    if (p.K == 0 || alpha == 0.f) return MGEMM_ERR_UNSUPPORTED;
+    int bn = kernel == MGEMM_KERNEL_H_DMA_192 ? 192 : 256;
+    if (kernel == MGEMM_KERNEL_AUTO) {
+        const Choice c = model_choice(p, h->ws);
+        bn = c.k == MGEMM_KERNEL_H_DMA_192 ? 192 : 256;
+        if (!mgemm::h_dma_supports(p, bn)) bn = bn == 256 ? 192 : 256;
+    }
+    if (!mgemm::h_dma_supports(p, bn)) return MGEMM_ERR_UNSUPPORTED;
+    p.stamps = h->stamps;
+    p.stamps_cap = h->stamps ? h->stamps_cap : 0;
+    const hipError_t e = mgemm::launch_h_dma_acc32(p, bn, stream);
+    return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
+}
+
 mgemm_status_t mgemm_select_variant(mgemm_handle_t h, mgemm_layout_t layoutA,
                                     mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
                                     float alpha, const void* A, int64_t lda, const void* B,

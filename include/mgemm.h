@@ -221,6 +221,33 @@ mgemm_status_t mgemm_run_variant(mgemm_handle_t h, const mgemm_variant_t* v,
                                  hipStream_t stream);
 
 /*
+ * mgemm_run_acc32 -- the FP32 sums behind a 16-bit product, before the output
+ * rounding: C32 = alpha * op(A) * op(B) in FP32, from the same direct-to-LDS
+ * kernel and tile mgemm_run uses for large 16-bit products, unsplit.  The
+ * MTT S4000 FP16 GEMM write-up grades FP16 outputs against an absolute
+ * tolerance (0.01 * sqrt(K/512)) that the FP16 spacing itself exceeds for
+ * large outputs; these sums let a check hold the accumulation to that bare
+ * tolerance apart from the output format's rounding.  mgemm_run_variant with
+ * the same kernel, one K range and beta = 0 stores exactly these values
+ * rounded once to dtype (round to nearest even).
+ *   kernel : MGEMM_KERNEL_AUTO (the tile width mgemm_run would pick for an
+ *            unsplit product), MGEMM_KERNEL_H_DMA_256 or MGEMM_KERNEL_H_DMA_192.
+ *   A, B   : dtype MGEMM_F16 or MGEMM_BF16, layouts and leading dimensions as
+ *            for mgemm_run.
+ *   C32    : device FP32 M x N in layoutA's order with leading dimension ldc
+ *            (elements), written only; beta is not applied.
+ * Errors: MGEMM_ERR_INVALID_ARG as mgemm_run, or for another kernel;
+ * MGEMM_ERR_UNSUPPORTED for MGEMM_F32, K not a positive multiple of 32,
+ * alpha = 0, or operands the kernel cannot read (leading dimensions not
+ * multiples of 8, bases not 16-byte aligned).  M or N = 0 is a no-op.
+ */
+mgemm_status_t mgemm_run_acc32(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
+                               mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
+                               float alpha, const void* A, int64_t lda, const void* B,
+                               int64_t ldb, float* C32, int64_t ldc, mgemm_dtype_t dtype,
+                               hipStream_t stream);
+
+/*
  * mgemm_select_variant -- the variant (kernel and number of K ranges)
  * mgemm_run would launch; validation as mgemm_select_kernel.  out->kernel is
  * MGEMM_KERNEL_AUTO (and out->ksplit 0) when nothing or only a scaling of C
