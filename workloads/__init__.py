@@ -39,6 +39,8 @@ def draw(kind: str, seed: int, n: int, scale: float = 1.0) -> np.ndarray:
         return rng.integers(-4, 5, n).astype(np.float64)
     if kind == "smallint":                        # U{-2..2}: keeps long sums tiny
         return rng.integers(-2, 3, n).astype(np.float64)
+    if kind == "f16sub":                          # FP16 subnormals (and zero): j * 2^-24, |j| < 1024
+        return rng.integers(-1023, 1024, n).astype(np.float64) * 2.0 ** -24
     raise ValueError(kind)
 
 
