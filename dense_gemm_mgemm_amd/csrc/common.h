@@ -41,6 +41,23 @@ struct Problem {
     int64_t stamps_cap = 0;
 };
 
+// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l), the
+// direct-to-LDS staging of the streaming kernels.  Issued through inline asm
+// (m0 set in the same statement) so that the compiler does not treat the LDS
+// reads that follow as dependent on it: it would otherwise wait for every
+// copy in flight before each such read.  Completion is tracked by hand with
+// the vmcnt waits of each kernel's schedule.  Naming m0 as clobbered draws a
+// warning because m0 is reserved to the compiler; this is sound only while
+// the compiler keeps no value of its own in m0 in these kernels, which
+// tests/test_codegen.py checks on the generated code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 struct ClockStamp {
     unsigned long long cycles, ticks;
 };

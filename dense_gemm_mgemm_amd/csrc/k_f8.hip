@@ -265,13 +265,6 @@ __device__ __forceinline__ void wait_slices(int n) {
     else if (n == 2) wait_vm<2 * L>();
     else wait_vm<3 * L>();
 }
-// Global -> LDS copy of 16 bytes per lane (lane l lands at lds + 16*l).  Inline
-// asm: the compiler would otherwise drain every copy in flight before any LDS
-// read it cannot prove disjoint.
-__device__ __forceinline__ void copy_to_lds(const void* src, unsigned lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds) : "memory", "m0");
-}
 __device__ __forceinline__ void fence_sched() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
