@@ -190,10 +190,11 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // partial rows costs more than the wider segments save, most of all for
     // 64-row blocks (BF16, K = 2048, M = 64: 17.4 us whole-K against 19.1 us
     // at the best split; K = 1024: 9.4 against 15.7).
-    // Above 32 rows the skinny kernel's 64-row blocks lose to the 128-row
-    // tiles of the direct-to-LDS kernel with a K split, which the time model
-    // below picks (BF16 x W[4096 x N]: M = 64, N = 12288: 28.9 against 31.4 us;
-    // N = 4096: 17.9 against 26.4 us; M = 48 ties at N = 12288).
+    // Above 32 rows the skinny kernel's 64-row blocks lose to the 64- and
+    // 128-row tiles of the direct-to-LDS kernel with a K split, which the time
+    // model below picks (BF16 x W[4096 x 12288]: M = 64 27.2 us on 64-row
+    // tiles, 27.9 on 128-row tiles, 31.4 on the skinny kernel; M = 33: 24.8
+    // against 25.9).
     const bool short_k = p.K <= 1024 || (p.M > 32 && p.K <= 2048);
     if (p.M <= 64 && short_k && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
     const bool tiles128 = p.M > 32 && mgemm::h_dma_supports(p, 192, 128);
