@@ -88,3 +88,8 @@ def test_create_without_gpu_fails_cleanly():
 
 def test_set_clock_stamps_needs_a_handle():
     assert mg.load().mgemm_set_clock_stamps(None, None, 0) == mg.MGEMM_ERR_INVALID_ARG
+
+
+def test_acc32_needs_a_handle():
+    assert mg.load().mgemm_run_acc32(None, 0, 0, 0, 4, 4, 32, 1.0, None, 32, None, 4, None, 4, 1,
+                                     None) == mg.MGEMM_ERR_INVALID_ARG

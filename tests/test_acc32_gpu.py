@@ -110,3 +110,27 @@ def test_acc32_within_the_bare_tolerance_at_full_size(h, make, kernel):
     say(case.name, "points", pi.size, "FP32 sums max err %.3g (bare tol %.3g);" % (err.max(), tol),
         "rounded to", case.dtype, ":", over16, "points over the bare tol")
     assert err.max() <= tol, (case.name, float(err.max()), tol)
+
+
+def test_acc32_argument_errors(h):
+    dA = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    dB = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    C32 = torch.full((64 * 64,), 7.0, dtype=torch.float32, device="cuda")
+
+    def call(kernel="auto", M=64, N=64, K=64, alpha=1.0, dtype="f16", lda=64, ldc=64):
+        mg.mgemm_run_acc32(h, kernel, "row", "row", M, N, K, alpha, dA, lda, dB, 64, C32, ldc, dtype)
+
+    for kw, status in [({"kernel": "f32_fast"}, mg.MGEMM_ERR_INVALID_ARG),
+                       ({"lda": 32}, mg.MGEMM_ERR_INVALID_ARG),
+                       ({"ldc": 32}, mg.MGEMM_ERR_INVALID_ARG),
+                       ({"M": -1}, mg.MGEMM_ERR_INVALID_ARG),
+                       ({"dtype": "f32"}, mg.MGEMM_ERR_UNSUPPORTED),
+                       ({"K": 48}, mg.MGEMM_ERR_UNSUPPORTED),
+                       ({"K": 0}, mg.MGEMM_ERR_UNSUPPORTED),
+                       ({"alpha": 0.0}, mg.MGEMM_ERR_UNSUPPORTED)]:
+        with pytest.raises(mg.MgemmError) as ei:
+            call(**kw)
+        assert ei.value.status == status, kw
+    call(M=0)                                   # empty: a no-op
+    torch.cuda.synchronize()
+    assert bool((C32 == 7.0).all())             # nothing written by any of the above
