@@ -120,12 +120,14 @@ __global__ __launch_bounds__(NT, 1) void k_skinny_sk(Problem p, SplitArgs sa) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool has_x = w < MB;           // waves 0..MB-1 also copy X
 
-    // Workgroup -> (column block, K range); consecutive numbers share an XCD
-    // and a K range, so they share X rows in that XCD's L2.
-    const int blocks = (int)((p.N + BNS - 1) / BNS);
+    // Workgroup -> (column block, K range): the K ranges of one column block
+    // take consecutive positions, which the workgroup numbering places on one
+    // XCD, so each XCD streams whole column blocks of W over all of K (with
+    // weights stored out x in: whole 8 KiB rows of W', 25.0 against 26.5 us
+    // at M = 16 when the ranges of a block were spread over the XCDs).
     int tz, t;
     tile_of_block(blockIdx.x, gridDim.x, 1, gridDim.x, 1, tz, t);
-    const int blk = t % blocks, split = t / blocks;
+    const int blk = t / sa.ksplit, split = t % sa.ksplit;
     const int64_t nk = p.K / KS;
     const int64_t s_begin = (int64_t)split * sa.per;
     const int64_t s_end = s_begin + sa.per < nk ? s_begin + sa.per : nk;
