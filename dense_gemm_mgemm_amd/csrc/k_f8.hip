@@ -298,6 +298,9 @@ struct F8Args {
     int ksplit;           // K ranges (1: no split)
     int nks;              // 64-slices per range (the last range may hold fewer)
 };
+// Tile order of split launches: groups two M-tiles deep, so an XCD that holds
+// all K ranges of its tiles streams little of A twice.
+constexpr int SPLIT_GROUP_M = 2;
 
 template <int CT>
 __device__ __forceinline__ void store4(void* C, int64_t ldc, int64_t m, int64_t n, int nlim_n,
@@ -392,13 +395,13 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-    // Position range * tiles + tile in an order where each XCD's workgroups
-    // are consecutive (as in k_h_dma.hip's split of K).
-    const int ntiles = tiles_m * tiles_n;
+    // Position tile * ksplit + range in an order where each XCD's workgroups
+    // are consecutive: all K ranges of a tile run on one XCD, and the second
+    // phase sums each tile on that XCD (as in k_h_dma.hip's split of K).
     const int pos = xcd_linear(blockIdx.x, gridDim.x);
-    const int split = pos / ntiles;
+    const int split = pos % f.ksplit;
     int tmi, tni;
-    tile_from_linear(pos - split * ntiles, tiles_m, tiles_n, 8, tmi, tni);
+    tile_from_linear(pos / f.ksplit, tiles_m, tiles_n, f.ksplit > 1 ? SPLIT_GROUP_M : 8, tmi, tni);
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
@@ -558,16 +561,19 @@ __global__ __launch_bounds__(NT) void k_f8_reduce(Problem p, F8Args f) {
     constexpr int64_t TILE_FLOATS = (int64_t)NT * TM * TN * 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (int)((p.N + BN - 1) / BN);
-    const int t = blockIdx.x / CH, c = blockIdx.x % CH;
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+    const int pos = xcd_linear(blockIdx.x, gridDim.x);   // the first phase's tile order
+    const int t = pos / CH, c = pos % CH;
+    int tmi, tni;
+    tile_from_linear(t, tiles_m, tiles_n, SPLIT_GROUP_M, tmi, tni);
     const int tm = c / (TN * 4), tn = (c / 4) % TN, q = c % 4;
-    const int64_t m0 = (int64_t)(t / tiles_n) * BM, n0 = (int64_t)(t % tiles_n) * BN;
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
     const int mi = 128 * wm + 32 * tm + (lane & 31);
     const int ni = BN / 2 * wn + 32 * tn + 8 * q + 4 * (lane >> 5);
     if (mi >= mlim || ni >= nlim) return;
-    const float* src = f.part + (int64_t)t * f.ksplit * TILE_FLOATS + (int64_t)c * NT * 4 + 4 * tid;
+    const float* src = f.part + (int64_t)(tmi * tiles_n + tni) * f.ksplit * TILE_FLOATS + (int64_t)c * NT * 4 + 4 * tid;
     f32x4 a = *(const f32x4*)src;
     int s = 1;
     for (; s + 4 <= f.ksplit; s += 4) {

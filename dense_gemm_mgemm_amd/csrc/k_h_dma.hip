@@ -84,6 +84,11 @@ struct HSplit {
     int ksplit;     // number of K ranges
     int nks;        // 32-slices per range (the last range may hold fewer)
 };
+// Tile order of split launches: groups two M-tiles deep.  Each XCD holds all
+// K ranges of its tiles, and a deeper group would make it stream more of A
+// over the whole K (FFN share 1024x1536x4096: 24.8 us at 2, 26.2 at 8, the
+// unsplit order of 8 tiles kept per range 26.0).
+constexpr int SPLIT_GROUP_M = 2;
 
 #ifndef MGEMM_DMA_SLOTS
 #define MGEMM_DMA_SLOTS 4
@@ -195,13 +200,14 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
 
     const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + OUT - 1) / OUT);
     // Workgroups of one XCD take consecutive positions; a position is
-    // range * tiles + tile, so an XCD works on few K ranges at a time and its
-    // L2 holds their A and B panels.
-    const int ntiles = tiles_m * tiles_n;
+    // tile * ksplit + range, so all K ranges of a tile run on one XCD and the
+    // second phase, which places each tile on the same XCD, reads their
+    // partials from that XCD's L2.  Split launches group tiles two M-tiles
+    // deep (an XCD's tiles then share A and B panels over the whole K).
     const int pos = xcd_linear(blockIdx.x, gridDim.x);
-    const int split = pos / ntiles;
+    const int split = pos % sp.ksplit;
     int tmi, tni;
-    tile_from_linear(pos - split * ntiles, tiles_m, tiles_n, 8, tmi, tni);
+    tile_from_linear(pos / sp.ksplit, tiles_m, tiles_n, sp.ksplit > 1 ? SPLIT_GROUP_M : 8, tmi, tni);
     const int j0 = split * sp.nks;                        // first 32-slice of this range
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
@@ -545,9 +551,13 @@ __global__ __launch_bounds__(NT) void k_h_dma_reduce(Problem p, HSplit sp) {
     constexpr int64_t TILE_FLOATS = (int64_t)NT * TM * TN * 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = DUAL ? wave : wave >> 1, wn = DUAL ? 0 : wave & 1;
-    const int tiles_n = (int)((p.N + OUT - 1) / OUT);
-    const int t = blockIdx.x / CH, c = blockIdx.x % CH;
-    const int tmi = t / tiles_n, tni = t % tiles_n;
+    const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + OUT - 1) / OUT);
+    // CH consecutive positions per tile, in the first phase's tile order: a
+    // tile's sum runs on the XCD that computed its partials.
+    const int pos = xcd_linear(blockIdx.x, gridDim.x);
+    const int t = pos / CH, c = pos % CH;
+    int tmi, tni;
+    tile_from_linear(t, tiles_m, tiles_n, SPLIT_GROUP_M, tmi, tni);
     const int tm = c / (TNO * 4), tn = (c / 4) % TNO, q = c % 4;
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
@@ -555,7 +565,7 @@ __global__ __launch_bounds__(NT) void k_h_dma_reduce(Problem p, HSplit sp) {
     const int mi = G::WROWS * wm + 32 * tm + (lane & 31);
     const int ni = G::WN * wn + 32 * tn + 8 * q + 4 * (lane >> 5);
     if (mi >= mlim || ni >= nlim) return;
-    const float* tile = sp.part + (int64_t)t * sp.ksplit * TILE_FLOATS + 4 * tid;
+    const float* tile = sp.part + (int64_t)(tmi * tiles_n + tni) * sp.ksplit * TILE_FLOATS + 4 * tid;
     auto sum = [&](int chunk) {
         const float* src = tile + (int64_t)chunk * NT * 4;
         f32x4 a = *(const f32x4*)src;
