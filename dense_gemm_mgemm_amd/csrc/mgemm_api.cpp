@@ -108,16 +108,22 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
 // 512x4096x8192 BF16 over every split from 1 to 16; `speed` is a kernel's
 // per-CU rate relative to the register-staged kernel (the direct-to-LDS
 // kernel runs a full 256x256 tile 1.4x as fast: 1024 NN tiles in 2.12 vs
-// 2.58 ms).
+// 2.58 ms).  A slice never takes less than its operand bytes ((bm + bn) x 32
+// 16-bit values) at 60 KB/us per CU: the rate one CU's copies reach (128-
+// and 64-row tiles of 1024^3, 512x1024x2048 and 256x1536x4096 spend 0.33 and
+// 0.25-0.27 us per slice, above their share of the MFMA time).
 double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int per_cu, int ks) {
     constexpr double SLICE_US = 0.98, WG_US = 2.0, PASS_US = 4.0, PART_BYTES_PER_US = 2.6e6;
+    constexpr double CU_BYTES_PER_US = 60e3;
     const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
     const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + out_n - 1) / out_n);
     const int64_t nk = (p.K + 31) / 32;
     const int64_t cap = slots * per_cu;
     const int64_t waves = (tiles * ks + cap - 1) / cap;
     const int64_t nks = (nk + ks - 1) / ks;
-    const double slice = SLICE_US * (double)(bm * bn) / 65536.0 / speed * per_cu;
+    const double mfma = SLICE_US * (double)(bm * bn) / 65536.0 / speed * per_cu;
+    const double copy = (double)(bm + bn) * 64.0 * per_cu / CU_BYTES_PER_US;
+    const double slice = mfma > copy ? mfma : copy;
     double t = (double)waves * ((double)nks * slice + WG_US);
     if (ks > 1) t += PASS_US + (double)tiles * ks * bm * bn * 4.0 / PART_BYTES_PER_US;
     return t;
@@ -227,7 +233,10 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // of a 128-row split (BF16 x W[4096 x N], N = 12288: M = 64 / 48 / 33 in
     // 27.2 / 26.0 / 24.8 us against 27.9 / 26.7 us on 128-row tiles and 25.9
     // on the skinny kernel at M = 33; N = 4096, M = 64: 13.1 against 13.7).
-    if (p.M <= 64 && mgemm::h_dma_supports(p, 192, 64)) {
+    // Above 64 rows, under the same small-B rule as the 128-row tiles: small
+    // grids gain CUs at the per-CU copy rate (BF16 1024^3 11.8 against 15.3
+    // us, 512^3 7.9 against 10.3, 512x1024x2048 11.6 against 12.6).
+    if ((p.M <= 64 || b_small) && mgemm::h_dma_supports(p, 192, 64)) {
         double t;
         const int ks = auto_split(p, 192, false, ws, &t, 64);
         if (t < best_t) { best_t = t; best = {MGEMM_KERNEL_H_DMA_64, ks}; }
