@@ -268,6 +268,35 @@ def test_small_shape_sweep_bit_exact(h, dtype):
     assert ran["auto"] > 0 and ran["general"] > 0
 
 
+# Mid-size shapes through the library's own choice of kernel, tile height and
+# split of K (the time model's branches: 64-, 128- and 256-row tiles, split
+# and unsplit, tile grids with an odd number of M-tiles), integer data, whole
+# C bit-exact.  K values that are not a multiple of 32 reach the register-
+# staged kernels.
+MID_M = [65, 96, 130, 200, 256, 300, 384, 512, 640, 777, 1000, 1024, 1536]
+MID_N = [64, 96, 192, 200, 384, 520, 1000, 1024, 1536, 2048]
+MID_K = [64, 96, 256, 512, 640, 1000, 1024, 2048]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_mid_shape_auto_dispatch_bit_exact(h, dtype):
+    rng = np.random.default_rng({"f32": 41, "f16": 42, "bf16": 43}[dtype])
+    chosen = {}
+    for si in range(8 if dtype == "f32" else 12):
+        M, N, K = int(rng.choice(MID_M)), int(rng.choice(MID_N)), int(rng.choice(MID_K))
+        la, lb = (["row", "col"][int(i)] for i in rng.integers(0, 2, 2))
+        beta = [0.0, -0.5][si % 2]
+        case = W.Case("mid", M, N, K, dtype, layoutA=la, layoutB=lb, alpha=1.0, beta=beta,
+                      kindA="int", kindB="int", kindC="int", seeds=(900 + si, 950 + si, 990 + si))
+        say("mid auto", dtype, (M, N, K), la, lb, beta)
+        inputs = case.make()
+        sel = mg.mgemm_select_variant(h, la, lb, M, N, K, 1.0, 256, case.lda, 256, case.ldb,
+                                      beta, 256, case.ldc, dtype)
+        chosen["%dx%dx%d %s/%s" % (M, N, K, la, lb)] = "%s/k%d" % sel
+        P.check_bit_exact(case, *P.run_gpu(h, case, "auto", inputs=inputs))
+    say("mid auto choices", dtype, chosen)
+
+
 # ---------------------------------------------------------------------------
 # Fused SiLU epilogue (mgemm_run_ex): every variant, small shapes with integer
 # data (exact GEMM), the pages' FFN projection Y = SiLU(XW) and a skinny case
