@@ -83,7 +83,8 @@ typedef enum {
     MGEMM_KERNEL_H_DMA_128 = 18, /* FP16/BF16, A' K-contiguous (row-major A), 128x192 tiles, 4 waves
                                     of 64x96, direct-to-LDS ring (short M) */
     MGEMM_KERNEL_H_DMA_64 = 19,  /* FP16/BF16, A' K-contiguous, 64x192 tiles, 4 waves of 32x96,
-                                    direct-to-LDS ring (32 < M <= 64: streams B from HBM) */
+                                    direct-to-LDS ring (32 < M <= 64: streams B from HBM;
+                                    also small grids with a small B) */
     MGEMM_KERNEL_COUNT = 20
 } mgemm_kernel_t;
 
