@@ -965,7 +965,7 @@ def main():
             print_summary(summarize_pmc(args.summarize_pmc, args.steady_after), "pmc")
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libmgemm has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
