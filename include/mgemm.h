@@ -60,9 +60,11 @@ typedef enum {
     MGEMM_KERNEL_AUTO = 0,
     MGEMM_KERNEL_GENERAL = 1,    /* any dtype/layout/alignment, VALU FMA, 64x64 tiles */
     MGEMM_KERNEL_F32_MFMA = 2,   /* FP32 on v_mfma_f32_32x32x2_f32, 128x128 tiles, any layout */
-    MGEMM_KERNEL_H_256x256 = 3,  /* FP16/BF16 MFMA, 256x256 tiles */
-    MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles */
-    MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles */
+    MGEMM_KERNEL_H_256x256 = 3,  /* FP16/BF16 MFMA, 256x256 tiles, any layout; operands
+                                    4-byte aligned (16-byte: vector loads, else buffer loads) */
+    MGEMM_KERNEL_H_256x192 = 4,  /* FP16/BF16 MFMA, 256x192 tiles, as above */
+    MGEMM_KERNEL_H_128x128 = 5,  /* FP16/BF16 MFMA, 128x128 tiles, any layout; operands 2-byte
+                                    aligned (2-byte loads where not 4-byte aligned) */
     MGEMM_KERNEL_SKINNY = 6,     /* FP16/BF16, M <= 64, streams B once (memory bound) */
     MGEMM_KERNEL_RESERVED_7 = 7, /* no longer built (an 8-wave variant that no shape chose);
                                     forcing it returns MGEMM_ERR_UNSUPPORTED */
@@ -142,7 +144,9 @@ mgemm_status_t mgemm_destroy(mgemm_handle_t h);
  * synchronisation.  The caller owns A, B, C and keeps them alive until the
  * stream's work has completed.  No alignment is required: operands that are
  * not 16-byte aligned (or whose leading dimension breaks the alignment of a
- * row) take a narrower load path.
+ * row) take a narrower load path (FP16/BF16: the register-staged MFMA kernel
+ * with buffer loads while A and B are at least 2-byte aligned and their
+ * leading dimensions below 2^22; FP32: narrower loads by alignment).
  * Errors: MGEMM_ERR_INVALID_ARG for a violated rule above (nothing enqueued);
  * MGEMM_ERR_HIP if the launch fails.
  */

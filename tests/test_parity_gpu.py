@@ -297,6 +297,79 @@ def test_mid_shape_auto_dispatch_bit_exact(h, dtype):
     say("mid auto choices", dtype, chosen)
 
 
+# 16-bit operands that are not 16-byte aligned run the register-staged kernel
+# with buffer loads: every tile form when they are dword-aligned, the 128x128
+# form when only 2-byte aligned.  Sizes are multiples of 8 and every leading
+# dimension is padded by `pad` elements, so the alignment is fixed: pad 4 ->
+# 8 bytes, 2 or 6 -> 4, 1 or 3 -> 2.  Every layout pair, edge tiles, ragged
+# K, beta != 0; the library's own choice and every forced form; integer data,
+# whole C bit-exact.
+UNALIGNED_16 = [(264, 136, 104, 4), (520, 392, 200, 2), (136, 264, 328, 1), (1000, 600, 512, 4),
+                (648, 1000, 1000, 1), (392, 520, 72, 6), (200, 72, 136, 3)]
+
+
+def load_width(*lds):
+    bits = 16
+    for ld in lds:
+        bits |= 2 * ld
+    return bits & -bits
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K,pad", UNALIGNED_16)
+def test_h_mfma_unaligned_bit_exact(h, dtype, M, N, K, pad):
+    for si, (la, lb) in enumerate(itertools.product(["row", "col"], ["row", "col"])):
+        lda = (K if la == "row" else M) + pad
+        ldb = (N if lb == "row" else K) + pad
+        ldc = (N if la == "row" else M) + pad
+        case = W.Case("h_unaligned", M, N, K, dtype, layoutA=la, layoutB=lb, lda=lda, ldb=ldb,
+                      ldc=ldc, alpha=1.0, beta=-0.5, kindA="int", kindB="int", kindC="int",
+                      seeds=(M + si, N + si, K + pad))
+        aw = load_width(lda, ldb)
+        assert aw == {4: 8, 2: 4, 6: 4, 1: 2, 3: 2}[pad]
+        sel = mg.mgemm_select_variant(h, la, lb, M, N, K, 1.0, 256, lda, 256, ldb, -0.5, 256, ldc,
+                                      dtype)
+        wide = ("h_mfma_256x256", "h_mfma_256x192")
+        assert sel[0] == "h_mfma_128x128" or (aw >= 4 and sel[0] in wide), sel
+        inputs = case.make()
+        for kernel in ("auto", "h_mfma_128x128") + (wide if aw >= 4 else ()):
+            say("h_mfma unaligned", dtype, (M, N, K), la, lb, "pad", pad, "width", aw, kernel)
+            P.check_bit_exact(case, *P.run_gpu(h, case, kernel, inputs=inputs))
+        if aw < 4:
+            for kernel in wide:
+                with pytest.raises(mg.MgemmError) as ei:
+                    P.run_gpu(h, case, kernel, inputs=inputs)
+                assert ei.value.status == mg.MGEMM_ERR_UNSUPPORTED
+
+
+# Base addresses 2, 4 and 8 bytes past a 16-byte boundary (views into larger
+# buffers), aligned leading dimensions: load widths 2, 4 and 8 bytes.
+@pytest.mark.parametrize("offset", [1, 2, 4])
+def test_h_mfma_unaligned_base_bit_exact(h, offset):
+    M, N, K = 264, 200, 96
+    case = W.Case("h_base", M, N, K, "bf16", alpha=1.0, beta=-0.5, kindA="int", kindB="int",
+                  kindC="int", seeds=(7 + offset, 8, 9))
+    A, B, C0 = case.make()
+    Cin = W.c_initial(case, C0)
+
+    def at_offset(t):
+        big = torch.zeros(t.numel() + 16, dtype=t.dtype, device="cuda")
+        view = big[offset:offset + t.numel()]
+        view.copy_(t.reshape(-1).cuda())
+        return big, view
+
+    keep_a, dA = at_offset(A)
+    keep_b, dB = at_offset(B)
+    dC = Cin.cuda()
+    assert dA.data_ptr() % 16 == 2 * offset % 16
+    say("h_mfma unaligned base", offset)
+    mg.mgemm_run(h, "row", "row", M, N, K, 1.0, dA, case.lda, dB, case.ldb, -0.5, dC, case.ldc,
+                 "bf16")
+    torch.cuda.synchronize()
+    P.check_bit_exact(case, A, B, C0, Cin, dC.cpu())
+    del keep_a, keep_b
+
+
 # ---------------------------------------------------------------------------
 # Fused SiLU epilogue (mgemm_run_ex): every variant, small shapes with integer
 # data (exact GEMM), the pages' FFN projection Y = SiLU(XW) and a skinny case
