@@ -327,8 +327,6 @@ bool f32_sk_fits(const Problem& p, const Workspace& ws);
 hipError_t launch_f32_sk(const Problem& p, const Workspace& ws, hipStream_t s);
 hipError_t launch_h_mfma(const Problem& p, int variant, hipStream_t s);
 bool h_mfma_supports(const Problem& p, int variant);
-int h_mfma_load_width(const Problem& p);
-hipError_t launch_h_mfma_narrow(const Problem& p, int variant, int aw, hipStream_t s);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 // Direct-to-LDS FP16/BF16 kernel.  ksplit > 1 cuts K into that many ranges
 // (two launches, partials in ws); h_dma_splits gives the number of ranges a

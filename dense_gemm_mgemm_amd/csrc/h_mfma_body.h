@@ -319,4 +319,9 @@ hipError_t dispatch_layout(const Problem& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// The forms with buffer loads (k_h_mfma_u.hip) for operands that are not
+// 16-byte aligned; aw is their common alignment in bytes (2, 4 or 8).
+hipError_t launch_h_mfma_narrow(const Problem& p, int variant, int aw, hipStream_t s);
+
 }  // namespace mgemm

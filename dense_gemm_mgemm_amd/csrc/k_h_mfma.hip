@@ -42,7 +42,7 @@ namespace mgemm {
 // Alignment (bytes, at most 16) shared by every run of 8 elements of A and B:
 // the largest power of two dividing both base addresses and both leading
 // dimensions in bytes (tile and slice origins add multiples of 16 bytes).
-int h_mfma_load_width(const Problem& p) {
+static int h_mfma_load_width(const Problem& p) {
     const uint64_t bits = (uint64_t)(uintptr_t)p.A | (uint64_t)(uintptr_t)p.B |
                           (uint64_t)(2 * p.lda) | (uint64_t)(2 * p.ldb) | 16u;
     return (int)(bits & (~bits + 1));
