@@ -58,8 +58,9 @@
 //
 // Restrictions (host-checked): A' K-contiguous, or M-contiguous with M % 8 ==
 // 0 (the AMC form, with an N-contiguous B'); B' N-contiguous (N % 8 == 0) or
-// K-contiguous (the BKC form); K % 32 == 0, lda and ldb multiples of 8,
-// 16-byte aligned bases.
+// K-contiguous (the BKC form); K >= 32 (a last partial slice is staged by
+// ordinary loads with zeros past K), lda and ldb multiples of 8, 16-byte
+// aligned bases.
 #include "common.h"
 
 namespace mgemm {
@@ -444,6 +445,60 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
         kstep(f1, f0, next, j + 1, 0, false, 0, 0, 1);
     }
 
+    // K tail (K not a multiple of 32): the range that ends at the last whole
+    // slice adds one more slice holding k in [32*nk_all, K).  It is staged by
+    // ordinary loads into the LDS positions the copies would fill (lane l's
+    // 16 bytes of copy i at dst[i] + 16*l, so the swizzled layout is the
+    // copies' own), with zeros for k >= K in both operands, so the two usual
+    // K-steps add exact zeros there.  Only k < K is ever read.  No copy is in
+    // flight any more (the loop above waited for the last slice), so a
+    // barrier frees the ring; a second one, after the LDS writes have
+    // completed, publishes the slice.
+    const int ktail = (int)(p.K - (int64_t)nk_all * BK);
+    if (ktail > 0 && j0 + nk == nk_all) {
+        const int ts = nk;                          // slice index after the range's last
+        __syncthreads();
+        unsigned char* slot = smem + (ts % SLOTS) * SLOT_BYTES;
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) {
+            const bool is_a = i < A_COPIES;
+            const uint16_t* s = src[i] + (int64_t)ts * (is_a ? a_kstep : b_kstep);
+            // K-contiguous copies (A rows, or B' columns in the BKC form)
+            // hold 8 consecutive k from 8c; the others one K-row of 8
+            // consecutive m or n.
+            const bool k_runs = is_a ? !AMC : BKC;
+            int kfirst;
+            if (k_runs) {
+                const int r = is_a ? (BM / 4) * wave + 16 * i + (lane >> 2)
+                                   : (BN / 4) * wave + 16 * (i - A_COPIES) + (lane >> 2);
+                kfirst = 8 * ((lane & 3) ^ a_swz(r));
+            } else {
+                const int jj = is_a ? wave * A_COPIES + i : wave * G::B_COPIES + (i - A_COPIES);
+                kfirst = (64 * jj + lane) / (is_a ? 32 : G::B_CHUNKS);
+            }
+            i32x4 v = i32x4{0, 0, 0, 0};
+            if (!k_runs) {
+                if (kfirst < ktail) v = *(const i32x4*)s;
+            } else if (kfirst + 8 <= ktail) {
+                v = *(const i32x4*)s;
+            } else if (kfirst < ktail) {
+                uint16_t e[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) e[q] = kfirst + q < ktail ? s[q] : (uint16_t)0;
+                v = __builtin_bit_cast(i32x4, e);
+            }
+            *(i32x4*)(slot + dst[i] + 16 * lane) = v;
+        }
+        __syncthreads();
+        read_a(f0, ts, 0, 0);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) read_b(f0, ts, 0, tn);
+#pragma unroll
+        for (int tm = 1; tm < TM; ++tm) read_a(f0, ts, 0, tm);
+        kstep(f0, f1, true, ts, 1, false, 0, 0, 1);
+        kstep(f1, f0, false, 0, 0, false, 0, 0, 1);
+    }
+
     if constexpr (EPI == EPI_PARTIAL) {
         // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3], all of
         // one output row (lane & 31 of block tm); rows past M are not stored
@@ -657,8 +712,9 @@ bool h_dma_supports(const Problem& p, int bn, int bm) {
     if (p.dtype != F16 && p.dtype != BF16) return false;
     if (!p.a_kc && p.b_kc) return false;
     // N-contiguous B' rows (M-contiguous A' columns) are read as 8-element
-    // chunks; K-contiguous operands as 32-element K slices.
-    if (p.K <= 0 || p.K % BK != 0 || p.K / BK > 0x7fffffff || (!p.b_kc && p.N % 8 != 0)) return false;
+    // chunks; K-contiguous operands as 32-element K slices, the last one
+    // (K not a multiple of 32) staged by ordinary loads.
+    if (p.K < BK || p.K / BK > 0x7fffffff || (!p.b_kc && p.N % 8 != 0)) return false;
     if (!p.a_kc && p.M % 8 != 0) return false;
     if (p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;

@@ -242,9 +242,10 @@ mgemm_status_t mgemm_run_variant(mgemm_handle_t h, const mgemm_variant_t* v,
  *   C32    : device FP32 M x N in layoutA's order with leading dimension ldc
  *            (elements), written only; beta is not applied.
  * Errors: MGEMM_ERR_INVALID_ARG as mgemm_run, or for another kernel;
- * MGEMM_ERR_UNSUPPORTED for MGEMM_F32, K not a positive multiple of 32,
- * alpha = 0, or operands the kernel cannot read (leading dimensions not
- * multiples of 8, bases not 16-byte aligned).  M or N = 0 is a no-op.
+ * MGEMM_ERR_UNSUPPORTED for MGEMM_F32, K = 0 or below 32 (K need not be a
+ * multiple of 32), alpha = 0, or operands the kernel cannot read (leading
+ * dimensions not multiples of 8, bases not 16-byte aligned).  M or N = 0 is a
+ * no-op.
  */
 mgemm_status_t mgemm_run_acc32(mgemm_handle_t h, mgemm_kernel_t kernel, mgemm_layout_t layoutA,
                                mgemm_layout_t layoutB, int64_t M, int64_t N, int64_t K,
@@ -280,7 +281,7 @@ mgemm_status_t mgemm_select_variant(mgemm_handle_t h, mgemm_layout_t layoutA,
  * gives Z = 0.  Asynchronous on `stream`, like mgemm_run.
  * Errors: MGEMM_ERR_INVALID_ARG for a violated size/leading-dimension rule or
  * a NULL pointer with a nonzero extent; MGEMM_ERR_UNSUPPORTED for MGEMM_F32,
- * K % 32 != 0, N % 8 != 0, leading dimensions that are not multiples of 8
+ * 0 < K < 32, N % 8 != 0, leading dimensions that are not multiples of 8
  * or bases that are not 16-byte aligned (nothing enqueued);
  * MGEMM_ERR_HIP if the launch fails.
  */

@@ -57,7 +57,8 @@ def _rounded_equals_16bit(h, case, kernel, dA, dB, C32):
     assert diff == 0, "%s %s: %d outputs differ from the rounded sums" % (case.name, kernel, diff)
 
 
-SHAPES = [(296, 200, 640), (256, 192, 1024), (520, 776, 320), (40, 104, 160)]
+SHAPES = [(296, 200, 640), (256, 192, 1024), (520, 776, 320), (40, 104, 160),
+          (296, 200, 648), (40, 104, 168)]          # K tails of 8
 LAYOUTS = [("row", "row"), ("row", "col"), ("col", "col"), ("col", "row")]
 
 
@@ -125,7 +126,7 @@ def test_acc32_argument_errors(h):
                        ({"ldc": 32}, mg.MGEMM_ERR_INVALID_ARG),
                        ({"M": -1}, mg.MGEMM_ERR_INVALID_ARG),
                        ({"dtype": "f32"}, mg.MGEMM_ERR_UNSUPPORTED),
-                       ({"K": 48}, mg.MGEMM_ERR_UNSUPPORTED),
+                       ({"K": 16}, mg.MGEMM_ERR_UNSUPPORTED),      # under one 32-wide slice
                        ({"K": 0}, mg.MGEMM_ERR_UNSUPPORTED),
                        ({"alpha": 0.0}, mg.MGEMM_ERR_UNSUPPORTED)]:
         with pytest.raises(mg.MgemmError) as ei:

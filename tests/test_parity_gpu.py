@@ -271,8 +271,8 @@ def test_small_shape_sweep_bit_exact(h, dtype):
 # Mid-size shapes through the library's own choice of kernel, tile height and
 # split of K (the time model's branches: 64-, 128- and 256-row tiles, split
 # and unsplit, tile grids with an odd number of M-tiles), integer data, whole
-# C bit-exact.  K values that are not a multiple of 32 reach the register-
-# staged kernels.
+# C bit-exact.  K = 1000 (not a multiple of 32: rows of 1000 elements are not
+# 16-byte aligned) reaches the register-staged kernel's buffer loads.
 MID_M = [65, 96, 130, 200, 256, 300, 384, 512, 640, 777, 1000, 1024, 1536]
 MID_N = [64, 96, 192, 200, 384, 520, 1000, 1024, 1536, 2048]
 MID_K = [64, 96, 256, 512, 640, 1000, 1024, 2048]
@@ -295,6 +295,48 @@ def test_mid_shape_auto_dispatch_bit_exact(h, dtype):
         chosen["%dx%dx%d %s/%s" % (M, N, K, la, lb)] = "%s/k%d" % sel
         P.check_bit_exact(case, *P.run_gpu(h, case, "auto", inputs=inputs))
     say("mid auto choices", dtype, chosen)
+
+
+# K not a multiple of 32 on the direct-to-LDS kernel: the range that ends at
+# the last whole slice stages one more, partial slice by ordinary loads with
+# zeros past K.  Tails of 1, 7, 8, 9 and 31 elements (partial and whole
+# 8-element runs of K-contiguous operands), every tile form, the four layout
+# pairs (NN, B' K-contiguous, A' M-contiguous, and the transposed NN),
+# unsplit and split; beta != 0; integer data, whole C bit-exact.
+KTAIL_SHAPES = [(296, 200, 33), (264, 392, 103), (136, 520, 72), (520, 264, 255),
+                (48, 776, 161), (1000, 600, 1001)]
+
+
+def _up8(x):
+    return (x + 7) // 8 * 8
+
+
+@pytest.mark.parametrize("M,N,K", KTAIL_SHAPES)
+def test_h_dma_k_tail_bit_exact(h, M, N, K):
+    ran = {}
+    for dtype in ("bf16", "f16"):
+        for la, lb in itertools.product(["row", "col"], ["row", "col"]):
+            # Leading dimensions rounded up to multiples of 8 (the kernel's
+            # alignment rule), so K-contiguous rows end inside an 8-element run.
+            case = W.Case("ktail", M, N, K, dtype, layoutA=la, layoutB=lb,
+                          lda=_up8(K if la == "row" else M), ldb=_up8(N if lb == "row" else K),
+                          alpha=1.0, beta=-0.5, kindA="int", kindB="int", kindC="int",
+                          seeds=(M + 1, N + 2, K + 3))
+            inputs = case.make()
+            for kernel in ("h_dma_256x256", "h_dma_256x192", "h_dma_128x192", "h_dma_64x192"):
+                for ks in (1, 2, 3):
+                    try:
+                        out = P.run_gpu(h, case, kernel, inputs=inputs, ksplit=ks)
+                    except mg.MgemmError as e:
+                        assert e.status == mg.MGEMM_ERR_UNSUPPORTED
+                        continue
+                    say("k tail", dtype, (M, N, K), la, lb, kernel, ks)
+                    P.check_bit_exact(case, *out)
+                    ran[(la, lb)] = ran.get((la, lb), 0) + 1
+            say("k tail auto", dtype, (M, N, K), la, lb)
+            P.check_bit_exact(case, *P.run_gpu(h, case, "auto", inputs=inputs))
+    say("k tail forced runs per layout pair", ran)
+    assert len(ran) == 4, ran
 
 
 # 16-bit operands that are not 16-byte aligned run the register-staged kernel
@@ -442,7 +484,8 @@ def _run_gated(h, case, inputs, ksplit=None):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(300, 200, 64), (256, 96, 32), (130, 520, 96), (37, 104, 160)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 64), (256, 96, 32), (130, 520, 96), (37, 104, 160),
+                                   (300, 200, 72), (136, 520, 40)])
 def test_gated_pair_integer(h, dtype, M, N, K):
     case = W.Case("gated", M, N, K, dtype, kindA="int", kindB="int", seeds=(M, N, K),
                   extra={"gated": True, "seed_u": K + 7})
@@ -615,7 +658,7 @@ def test_ffn_share_split_auto(h):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(300, 200, 160), (130, 520, 96), (37, 104, 160)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 160), (130, 520, 96), (37, 104, 160), (300, 200, 104)])
 def test_gated_pair_split_k_integer(h, dtype, M, N, K):
     # K stays small: G and U grow with K and their product must stay inside
     # the FP16 range for most outputs.
