@@ -66,6 +66,12 @@ GEMM_CASES = [
     (W.Case("graph_mid_m", 128, 12288, 4096, "bf16", kindA="normal", kindB="normal",
             seeds=(27, 28, 29)), "h_dma_128x192", 4),
     (W.Case("graph_sk_short_m", 16, 6000, 2000, "f32", lda=2001, seeds=(30, 31, 32)), "f32_sk", 1),
+    # A K tail (K = 1000) on the split direct-to-LDS kernel, and FP16 rows that
+    # are not 16-byte aligned (buffer loads) through the library's choice.
+    (W.Case("graph_ktail", 520, 1536, 1000, "bf16", kindA="normal", kindB="normal",
+            seeds=(33, 34, 35)), "h_dma_128x192", 3),
+    (W.Case("graph_unaligned", 600, 700, 1002, "f16", kindA="normal", kindB="normal",
+            lda=1002, ldb=702, seeds=(36, 37, 38)), "auto", 0),
 ]
 
 

@@ -64,6 +64,9 @@ PAIRS = [
     (_int_case("col", 1024, 1024, 2048, "f16", la="col", lb="col", seeds=(31, 32, 33)),
      _int_case("col_small", 512, 256, 512, "f16", la="col", lb="col", seeds=(34, 35, 36)),
      "h_dma_256x256", 3),
+    (_int_case("ktail", 520, 1536, 1000, "bf16", seeds=(71, 72, 73)),
+     _int_case("ktail_small", 300, 520, 104, "bf16", beta=-0.5, seeds=(74, 75, 76)),
+     "h_dma_128x192", 3),
     (_int_case("m64", 64, 12288, 4096, "bf16", seeds=(61, 62, 63)),
      _int_case("m40", 40, 1000, 1024, "bf16", beta=-1.0, seeds=(64, 65, 66)),
      "h_dma_64x192", 4),
