@@ -30,7 +30,8 @@
 // waves of 128x96) exists for grids that a 256-wide tile fills badly: the
 // 1024x12288 FFN projection is 192 tiles of 256x256 on 256 CUs but 256 of
 // 256x192.
-// Restrictions of the MFMA kernel (host-checked): K % 64 == 0, lda and ldb
+// Restrictions of the MFMA kernel (host-checked): K >= 64 (a last partial
+// slice is staged by ordinary loads with zero codes past K), lda and ldb
 // multiples of 16, 16-byte aligned code buffers; k_f8_general takes the rest.
 #include "common.h"
 
@@ -530,6 +531,40 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         step(f1, f0, j + 2 < nk, j + 2, j + 1 + AHEAD < nk, j + 1 + AHEAD);
     }
 
+    // K tail (K not a multiple of 64), as in k_h_dma.hip: the range that ends
+    // at the last whole slice stages one more slice with ordinary loads into
+    // the LDS positions of the copies (lane l's 16 codes of copy i at dst[i] +
+    // 16*l: codes 16c .. 16c+15 of its row, c the swizzled chunk), zero codes
+    // (+0.0) for k >= K in both operands, then one more step.  Only k < K is
+    // read; no copy is in flight after the loop above.
+    const int ktail = (int)(p.K - (int64_t)nk_all * BK);
+    if (ktail > 0 && split * f.nks + nk == nk_all) {
+        const int ts = nk;
+        __syncthreads();
+        unsigned char* slot = smem + (ts % SLOTS) * SLOT_BYTES;
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) {
+            const int r = i < A_COPIES ? 64 * wave + 16 * i + (lane >> 2)
+                                       : BN / 4 * wave + 16 * (i - A_COPIES) + (lane >> 2);
+            const int kfirst = 16 * ((lane & 3) ^ swz(r));
+            const uint8_t* s = src[i] + (int64_t)ts * BK;
+            i32x4 v = i32x4{0, 0, 0, 0};
+            if (kfirst + 16 <= ktail) {
+                v = *(const i32x4*)s;
+            } else if (kfirst < ktail) {
+                uint8_t e[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) e[q] = kfirst + q < ktail ? s[q] : (uint8_t)0;
+                v = __builtin_bit_cast(i32x4, e);
+            }
+            *(i32x4*)(slot + dst[i] + 16 * lane) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read(f0, ts, r);
+        step(f0, f1, false, 0, false, 0);
+    }
+
     // Epilogue: lane holds C(m, n..n+3), m = row within the 32x32 block.
     if constexpr (PARTIAL) {
         // Chunk c = (tm * TN + tn) * 4 + q holds acc[tm][tn][4q .. 4q+3].
@@ -674,7 +709,9 @@ hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx,
 
 bool f8_mfma_supports(const Problem& p, int bn) {
     if (bn != 256 && bn != 192) return false;
-    if (p.K <= 0 || p.K % BK != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0) return false;
+    // K >= 64; a last partial slice (K not a multiple of 64) is staged by
+    // ordinary loads with zero codes past K.
+    if (p.K < BK || p.lda % 16 != 0 || p.ldb % 16 != 0) return false;
     if (((uintptr_t)p.A & 15) != 0 || ((uintptr_t)p.B & 15) != 0) return false;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
     return tiles > 0 && tiles <= 0x7fffffff;

@@ -436,8 +436,9 @@ mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const 
  *   C  : M x N, row-major, ldc >= max(1, N), element type ctype (F32, F16,
  *        BF16); beta == 0 never reads C.
  *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA or
- *        MGEMM_KERNEL_F8_MFMA_192 (K % 64 == 0, lda and ldb multiples of 16,
- *        16-byte aligned A and B) or MGEMM_KERNEL_F8_GENERAL (anything).
+ *        MGEMM_KERNEL_F8_MFMA_192 (K >= 64, lda and ldb multiples of 16,
+ *        16-byte aligned A and B; a K that is not a multiple of 64 ends with
+ *        a partial slice) or MGEMM_KERNEL_F8_GENERAL (anything).
  *        AUTO takes the MFMA tile width and split of K with the smallest
  *        predicted time.
  *   ksplit : 0 = the library's choice, 1 = no split, 2 .. MGEMM_MAX_KSPLIT =
