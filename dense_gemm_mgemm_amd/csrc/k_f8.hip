@@ -629,19 +629,64 @@ __global__ __launch_bounds__(NT) void k_f8_reduce(Problem p, F8Args f) {
     store4<CT>(p.C, p.ldc, m0 + mi, n0 + ni, nn, vec_ok, p.beta, v);
 }
 
-// Any K, alignment and leading dimension: one thread per output, codes
-// decoded one by one, FP32 accumulation in K order.
+// Any K, alignment and leading dimension: 64x64 output tiles of 256 threads,
+// 64 x 16 slices of both code matrices decoded to FP32 in LDS (zeros past the
+// edges), a 4x4 register block per thread.  Every output accumulates its
+// products with fmaf in K order over k < K only, then alpha and the row and
+// column scales are applied as in the MFMA kernels' epilogue.
+constexpr int FG_T = 64, FG_BK = 16;
+
 template <int CT>
 __global__ __launch_bounds__(256) void k_f8_general(Problem p, F8Args f) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= p.M * p.N) return;
-    const int64_t m = idx / p.N, n = idx % p.N;
-    const uint8_t* a = (const uint8_t*)p.A + m * p.lda;
-    const uint8_t* b = (const uint8_t*)p.B + n * p.ldb;
-    float acc = 0.0f;
-    for (int64_t k = 0; k < p.K; ++k) acc = fmaf(e4m3_value(a[k]), e4m3_value(b[k]), acc);
-    float v[4] = {p.alpha * ((acc * f.sa[m]) * f.sb[n]), 0.f, 0.f, 0.f};
-    store4<CT>(p.C, p.ldc, m, n, 1, false, p.beta, v);
+    __shared__ float As[FG_BK][FG_T + 4];
+    __shared__ float Bs[FG_BK][FG_T + 4];
+    const int tid = threadIdx.x;
+    const int tiles_m = (int)((p.M + FG_T - 1) / FG_T), tiles_n = (int)((p.N + FG_T - 1) / FG_T);
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, 8, tm, tn);
+    const int64_t m0 = (int64_t)tm * FG_T, n0 = (int64_t)tn * FG_T;
+    const uint8_t* A = (const uint8_t*)p.A;
+    const uint8_t* B = (const uint8_t*)p.B;
+    float acc[4][4] = {};
+    const int ty = tid / 16, tx = tid % 16;
+    for (int64_t k0 = 0; k0 < p.K; k0 += FG_BK) {
+        // 64 rows x 16 codes of each operand, 4 per thread; consecutive
+        // threads walk K (both code matrices are K-contiguous).
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + r * 256, ri = e / FG_BK, ki = e % FG_BK;
+            const int64_t k = k0 + ki, m = m0 + ri, n = n0 + ri;
+            As[ki][ri] = (m < p.M && k < p.K) ? e4m3_value(A[m * p.lda + k]) : 0.0f;
+            Bs[ki][ri] = (n < p.N && k < p.K) ? e4m3_value(B[n * p.ldb + k]) : 0.0f;
+        }
+        __syncthreads();
+        const int kn = p.K - k0 < FG_BK ? (int)(p.K - k0) : FG_BK;
+        for (int kk = 0; kk < kn; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty * 4 + i;
+        if (m >= p.M) continue;
+        const float sam = f.sa[m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx * 4 + j;
+            if (n >= p.N) continue;
+            float v[4] = {p.alpha * ((acc[i][j] * sam) * f.sb[n]), 0.f, 0.f, 0.f};
+            store4<CT>(p.C, p.ldc, m, n, 1, false, p.beta, v);
+        }
+    }
 }
 
 template <int XT>
@@ -693,8 +738,8 @@ hipError_t launch_f8_ct(const Problem& p, const F8Args& f, int bn, hipStream_t s
         return f.ksplit > 1 ? launch_f8_dma<CT, 256, true>(p, f, s) : launch_f8_dma<CT, 256, false>(p, f, s);
     if (bn == 192)
         return f.ksplit > 1 ? launch_f8_dma<CT, 192, true>(p, f, s) : launch_f8_dma<CT, 192, false>(p, f, s);
-    const int64_t n = p.M * p.N;
-    hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, f);
+    const int64_t tiles = ((p.M + FG_T - 1) / FG_T) * ((p.N + FG_T - 1) / FG_T);
+    hipLaunchKernelGGL(k_f8_general<CT>, dim3((unsigned)tiles), dim3(256), 0, s, p, f);
     return hipGetLastError();
 }
 
@@ -717,7 +762,9 @@ bool f8_mfma_supports(const Problem& p, int bn) {
     return tiles > 0 && tiles <= 0x7fffffff;
 }
 
-bool f8_general_supports(const Problem& p) { return (p.M * p.N + 255) / 256 <= 0x7fffffff; }
+bool f8_general_supports(const Problem& p) {
+    return ((p.M + FG_T - 1) / FG_T) * ((p.N + FG_T - 1) / FG_T) <= 0x7fffffff;
+}
 
 int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
