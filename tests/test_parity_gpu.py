@@ -807,6 +807,44 @@ def test_non_default_stream(h):
     P.check_bit_exact(case, *out)
 
 
+def test_two_handles_on_two_streams(h):
+    # Each handle owns its split-K workspace and arrival counters, so split
+    # calls of two handles on two streams may run at the same time: the
+    # two-launch split and the skinny last-arrival split, interleaved without
+    # synchronisation, both give the oracle's bits.
+    h2 = mg.mgemm_create()
+    try:
+        jobs = [(h, W.Case("two_share", 1024, 1536, 4096, "bf16", kindA="int", kindB="int",
+                           kindC="int", beta=-0.5, seeds=(81, 82, 83)), "h_dma_128x192", 4),
+                (h2, W.Case("two_skinny", 16, 6144, 4096, "bf16", kindA="int", kindB="int",
+                            kindC="int", beta=-0.5, seeds=(84, 85, 86)), "skinny_sk", 4)]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        state = []
+        for hh, case, kernel, ks in jobs:
+            A, B, C0 = case.make()
+            Cin = P.c_initial(case, C0)
+            state.append((A, B, C0, Cin, A.cuda(), B.cuda(), C0.cuda()))
+        torch.cuda.synchronize()
+        outs = [None, None]
+        for rep in range(4):
+            for j, ((hh, case, kernel, ks), s) in enumerate(zip(jobs, streams)):
+                A, B, C0, Cin, dA, dB, dC0 = state[j]
+                with torch.cuda.stream(s):
+                    dC = Cin.cuda()          # fresh C each time: beta reads it
+                    mg.mgemm_run_variant(hh, kernel, ks, case.layoutA, case.layoutB, case.M,
+                                         case.N, case.K, case.alpha, dA, case.lda, dB, case.ldb,
+                                         case.beta, dC, case.ldc, case.dtype, stream=s)
+                    outs[j] = dC
+        torch.cuda.synchronize()
+        for j, (hh, case, kernel, ks) in enumerate(jobs):
+            A, B, C0, Cin = state[j][:4]
+            say("two handles", case.name, kernel, ks)
+            P.check_bit_exact(case, A, B, C0, Cin, outs[j].cpu())
+    finally:
+        torch.cuda.synchronize()
+        mg.mgemm_destroy(h2)
+
+
 def test_unaligned_16bit_operands(h):
     # Operands one element past a 16-byte boundary, odd leading dimensions.
     M, N, K = 130, 70, 90
