@@ -90,6 +90,13 @@ struct HSplit {
 // over the whole K (FFN share 1024x1536x4096: 24.8 us at 2, 26.2 at 8, the
 // unsplit order of 8 tiles kept per range 26.0).
 constexpr int SPLIT_GROUP_M = 2;
+// Tile order of unsplit launches: groups four M-tiles deep (each XCD's 32
+// resident tiles a 4 x 8 block).  Against groups of 8 (8 x 4 blocks), BF16
+// 4096x16384x4096 483 against 604 us, 4096^3 123 against 129, the FP16
+// 8192x8192x16384 problem 1.756 against 1.779 ms at a higher clock; never
+// slower on the square and tall shapes tried (groups of 2: as 8; 16: 30%
+// slower on the 8k problem).
+constexpr int UNSPLIT_GROUP_M = 4;
 
 #ifndef MGEMM_DMA_SLOTS
 #define MGEMM_DMA_SLOTS 4
@@ -204,11 +211,13 @@ __global__ __launch_bounds__(NT, 1) void k_h_dma(Problem p, HSplit sp) {
     // tile * ksplit + range, so all K ranges of a tile run on one XCD and the
     // second phase, which places each tile on the same XCD, reads their
     // partials from that XCD's L2.  Split launches group tiles two M-tiles
-    // deep (an XCD's tiles then share A and B panels over the whole K).
+    // deep (an XCD's tiles then share A and B panels over the whole K),
+    // unsplit ones four deep.
     const int pos = xcd_linear(blockIdx.x, gridDim.x);
     const int split = pos % sp.ksplit;
     int tmi, tni;
-    tile_from_linear(pos / sp.ksplit, tiles_m, tiles_n, sp.ksplit > 1 ? SPLIT_GROUP_M : 8, tmi, tni);
+    tile_from_linear(pos / sp.ksplit, tiles_m, tiles_n, sp.ksplit > 1 ? SPLIT_GROUP_M : UNSPLIT_GROUP_M,
+                     tmi, tni);
     const int j0 = split * sp.nks;                        // first 32-slice of this range
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * OUT;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
