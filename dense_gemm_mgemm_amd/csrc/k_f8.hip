@@ -302,6 +302,10 @@ struct F8Args {
 // Tile order of split launches: groups two M-tiles deep, so an XCD that holds
 // all K ranges of its tiles streams little of A twice.
 constexpr int SPLIT_GROUP_M = 2;
+// Unsplit launches group tiles four M-tiles deep, as in k_h_dma.hip (FP8
+// 4096x16384x4096 267 against 321 us with groups of 8, 4096^3 68 against
+// 71, 16384x4096x4096 260 against 272; 8192^3 and 4096x1536x4096 1-2%).
+constexpr int UNSPLIT_GROUP_M = 4;
 
 template <int CT>
 __device__ __forceinline__ void store4(void* C, int64_t ldc, int64_t m, int64_t n, int nlim_n,
@@ -402,7 +406,8 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     const int pos = xcd_linear(blockIdx.x, gridDim.x);
     const int split = pos % f.ksplit;
     int tmi, tni;
-    tile_from_linear(pos / f.ksplit, tiles_m, tiles_n, f.ksplit > 1 ? SPLIT_GROUP_M : 8, tmi, tni);
+    tile_from_linear(pos / f.ksplit, tiles_m, tiles_n, f.ksplit > 1 ? SPLIT_GROUP_M : UNSPLIT_GROUP_M,
+                     tmi, tni);
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
