@@ -188,25 +188,30 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         }
         return {MGEMM_KERNEL_F32_MFMA, 1};
     }
-    // M <= 64 streams B once: 256-column blocks with K split over workgroups
-    // read B in 512-byte row segments (about 5.1 TB/s in copy-only
-    // measurements, against 4.2 TB/s for the 128-byte segments of the
-    // whole-K kernel).
-    // Short K is the exception: with few steps per range the exchange of
-    // partial rows costs more than the wider segments save, most of all for
-    // 64-row blocks (BF16, K = 2048, M = 64: 17.4 us whole-K against 19.1 us
-    // at the best split; K = 1024: 9.4 against 15.7).
-    // Above 32 rows the skinny kernel's 64-row blocks lose to the 64- and
-    // 128-row tiles of the direct-to-LDS kernel with a K split, which the time
-    // model below picks (BF16 x W[4096 x 12288]: M = 64 27.2 us on 64-row
-    // tiles, 27.9 on 128-row tiles, 31.4 on the skinny kernel; M = 33: 24.8
-    // against 25.9).
-    const bool short_k = p.K <= 1024 || (p.M > 32 && p.K <= 2048);
-    if (p.M <= 64 && short_k && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
-    const bool tiles128 = p.M > 32 && mgemm::h_dma_supports(p, 192, 128);
-    if (p.M <= 64 && mgemm::skinny_sk_supports(p) && !tiles128)
+    // M <= 64 streams B once.  Short K (at most 64 slices) runs whole-K: with
+    // few steps per range the exchange of partial rows costs more than a split
+    // saves (BF16, K = 2048: M = 64 17.4 us whole-K against 19.1 us at the best
+    // split; M = 1 / 16 / 32 x 1024 columns 6.8 / 6.7 / 8.0 against 7.2 / 8.7 /
+    // 11.5 on the split skinny kernel; K = 1024, M = 64: 9.4 against 15.7).
+    // Longer K splits over workgroups.  The split skinny kernel reads B in
+    // 512-byte row segments of 256-column blocks; it wins only for M <= 16
+    // and only where at most 16 ranges of those blocks still give three
+    // quarters of the CUs a workgroup (BF16 x W[4096 x 12288], M = 1 / 16: 21.0
+    // / 22.4 us against 22.2 / 22.8 on 64-row tiles).  Narrower B, or more
+    // rows (whose cost the skinny kernel's 16-row MFMA blocks pay in full),
+    // go to the time model below, which picks the 64- or 128-row tiles of the
+    // direct-to-LDS kernel with a K split (M = 1 / 16 / 32 x W[4096 x 1536]:
+    // 7.6 / 7.9 / 8.5 us against 8.8 / 11.4 / 16.3 on the skinny kernel; M =
+    // 32 x W[4096 x 4096] 15.0 against 17.1; M = 64 x W[4096 x 12288] 26.0
+    // against 31.5).
+    if (p.M <= 64 && p.K <= 2048 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
+    const int64_t sk_blocks = (p.N + 255) / 256;
+    if (p.M <= 16 && sk_blocks * 16 * 4 >= slots * 3 && mgemm::skinny_sk_supports(p))
         return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
-    if (p.M <= 64 && !tiles128 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
+    if (p.M <= 64 && !mgemm::h_dma_supports(p, 192, 64)) {
+        if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
+        if (mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
+    }
     // 16-bit: the variant (and split of K) with the smallest predicted time.
     Choice best{MGEMM_KERNEL_GENERAL, 1};
     double best_t = 1e300;

@@ -618,7 +618,7 @@ def test_skinny_weights_out_by_in_ffn_sampled(h, M):
     sel = mg.mgemm_select_variant(h, "row", "col", M, 12288, 4096, 1.0, 256, 4096, 256, 4096,
                                   0.0, 256, 12288, "bf16")
     say("skinny W^T ffn", M, sel)
-    assert sel[0] == ("skinny_sk" if M <= 32 else "h_dma_64x192")
+    assert sel[0] == ("skinny_sk" if M <= 16 else "h_dma_64x192")
     out = P.run_gpu(h, case)
     P.check_tolerance(case, *out, cols=[0, 255, 256, 12287])
 
@@ -875,7 +875,7 @@ def test_dispatch_choices(h):
     assert sel(W.ragged_f32()) == "f32_sk"
     assert sel(W.hgemm_colmajor(8192, 8192, 16384)) == "h_dma_256x256"
     assert sel(W.ffn_bf16()) == "h_dma_256x192"
-    assert all(sel(W.ffn_bf16(m)) == ("skinny_sk" if m <= 32 else "h_dma_64x192")
+    assert all(sel(W.ffn_bf16(m)) == ("skinny_sk" if m <= 16 else "h_dma_64x192")
                for m in W.SKINNY_M)
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
