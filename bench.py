@@ -547,6 +547,137 @@ def measure_mix(h, steps=20):
 
 
 # ---------------------------------------------------------------------------
+# Dispatch sweep: the built-in model's pick against every variant, timed
+# ---------------------------------------------------------------------------
+SWEEP_SPLITS = [1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32]
+SWEEP_TILES = {"h_dma_256x256": (256, 256), "h_dma_256x192": (256, 192),
+               "h_dma_128x192": (128, 192), "h_dma_64x192": (64, 192)}
+
+
+def sweep_shapes():
+    """16-bit shapes of the dispatch sweep: projections x W[K x N] of common
+    widths at 1 to 4096 rows, square column-major FP16 products, and a few
+    x W^T (B column-major) skinny shapes."""
+    out = []
+    for n, k in [(1536, 4096), (4096, 4096), (12288, 4096), (4096, 12288), (4096, 1024),
+                 (1024, 2048)]:
+        for m in (1, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+            out.append(("bf16", "row", "row", m, n, k))
+    for s in (512, 768, 1024, 1536, 2048, 3072, 4096, 6144):
+        out.append(("f16", "col", "col", s, s, s))
+    for m, n, k in [(1, 12288, 2048), (16, 12288, 2048), (32, 12288, 2048), (32, 4096, 2048),
+                    (16, 1536, 2048), (8, 1536, 4096), (8, 4096, 4096), (24, 4096, 4096),
+                    (48, 4096, 4096), (24, 12288, 4096), (8, 2048, 4096), (16, 3072, 4096),
+                    (1, 8192, 4096), (16, 8192, 4096), (64, 8192, 4096), (256, 8192, 4096),
+                    (1024, 8192, 4096), (1, 4096, 8192), (32, 4096, 8192), (64, 4096, 8192),
+                    (256, 4096, 8192), (16, 2048, 4096), (64, 2048, 8192), (1, 4096, 14336),
+                    (32, 4096, 14336), (64, 4096, 14336), (512, 4096, 14336), (1, 14336, 4096),
+                    (32, 14336, 4096), (8, 8192, 8192), (1, 4096, 6144), (16, 4096, 6144)]:
+        out.append(("bf16", "row", "row", m, n, k))
+    for m, n, k in [(1, 4096, 4096), (16, 4096, 4096), (32, 4096, 4096), (16, 1536, 4096),
+                    (16, 12288, 4096), (32, 12288, 4096)]:
+        out.append(("bf16", "row", "col", m, n, k))
+    return out
+
+
+def dispatch_sweep(h):
+    """Time the model's pick (kernel 'auto') and every direct-to-LDS and
+    skinny variant at each split on every sweep shape.  Each candidate: three
+    warm-up launches, then 10-40 launches back to back behind a stream hold,
+    between two HIP events.  Operands whose B has at least 16 MiB rotate over
+    four copies; smaller ones stay resident (warm last-level cache, as in the
+    workloads above)."""
+    import torch
+    import dense_gemm_mgemm_amd as mg
+    s = torch.cuda.current_stream()
+
+    def ranges(req, nk):
+        if req <= 1 or nk < 2:
+            return 1
+        ks = min(req, nk)
+        return -(-nk // -(-nk // ks))
+
+    def time_one(launch, est_us):
+        for i in range(3):
+            launch(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(8):
+            launch(i)
+        host = (time.perf_counter() - t1) / 8
+        torch.cuda.synchronize()
+        steps = int(max(10, min(40, 4000.0 / max(est_us, 1.0))))
+        hold_stream(s, 1.5 * host * steps + 1e-4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for i in range(steps):
+            launch(i)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    rows = []
+    shapes = sweep_shapes()
+    for si, (dtype, la, lb, M, N, K) in enumerate(shapes):
+        td = torch.float16 if dtype == "f16" else torch.bfloat16
+        rot = 4 if K * N * 2 >= 16 * 2 ** 20 else 1
+        g = torch.Generator(device="cuda").manual_seed(M * 7 + N * 3 + K)
+        A = [(torch.rand((M * K,), generator=g, device="cuda") - 0.5).to(td) for _ in range(rot)]
+        B = [(torch.rand((K * N,), generator=g, device="cuda") * 0.04 - 0.02).to(td)
+             for _ in range(rot)]
+        C = [torch.zeros((M * N,), device="cuda", dtype=td) for _ in range(rot)]
+        lda, ldb, ldc = (K if la == "row" else M), (N if lb == "row" else K), (N if la == "row" else M)
+        model = mg.mgemm_select_variant(h, la, lb, M, N, K, 1.0, A[0], lda, B[0], ldb, 0.0, C[0],
+                                        ldc, dtype)
+        est = 2.0 * M * N * K / 1e9 + 8.0
+        nk = K // 32
+        cands = [("auto", 0)]
+        for kern, (bm, bn) in SWEEP_TILES.items():
+            seen = set()
+            for req in SWEEP_SPLITS:
+                ks = ranges(req, nk)
+                if ks not in seen and -(-M // bm) * -(-N // bn) * ks <= 6144:
+                    seen.add(ks)
+                    cands.append((kern, req))
+        if M <= 64:
+            seen = set()
+            for req in SWEEP_SPLITS:
+                ks = ranges(req, nk)
+                if ks not in seen:
+                    seen.add(ks)
+                    cands.append(("skinny_sk", req))
+            cands.append(("skinny", 1))
+        times = {}
+        for kern, req in cands:
+            def launch(i, kern=kern, req=req):
+                j = i % rot
+                mg.mgemm_run_variant(h, kern, req, la, lb, M, N, K, 1.0, A[j], lda, B[j], ldb, 0.0,
+                                     C[j], ldc, dtype, stream=s)
+            try:
+                us = time_one(launch, est)
+            except mg.MgemmError:
+                continue                        # the variant does not run this shape
+            key = model if kern == "auto" else (kern, ranges(req, nk) if kern != "skinny" else 1)
+            times[key] = min(us, times.get(key, float("inf")))
+        best = min(times.items(), key=lambda kv: kv[1])
+        rows.append([dtype, la, lb, M, N, K, model[0], model[1], round(times[model], 2),
+                     best[0][0], best[0][1], round(best[1], 2)])
+        log("sweep %d/%d %s %s%s %dx%dx%d: model %s/%d %.2f us, best %s/%d %.2f us" % (
+            si + 1, len(shapes), dtype, la, lb, M, N, K, model[0], model[1], times[model],
+            best[0][0], best[0][1], best[1]))
+        del A, B, C
+        torch.cuda.empty_cache()
+    ratios = [r[8] / r[11] for r in rows]
+    worst = sorted(rows, key=lambda r: -r[8] / r[11])[:10]
+    return {"shapes": len(rows), "mean_model_over_best": round(statistics.mean(ratios), 4),
+            "max_model_over_best": round(max(ratios), 3),
+            "model_over_best_above_1.05": sum(x > 1.05 for x in ratios),
+            "columns": ["dtype", "layoutA", "layoutB", "M", "N", "K", "model_kernel", "model_ks",
+                        "model_us", "best_kernel", "best_ks", "best_us"],
+            "worst": worst, "rows": rows}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline and parity samples (the only part of this file that uses the
 # oracle)
 # ---------------------------------------------------------------------------
@@ -943,6 +1074,9 @@ def main():
                     help="write the workload's counter entry into profiles/traffic.json")
     ap.add_argument("--merge-record", metavar="JSON",
                     help="add an entry printed by --record-counters to profiles/traffic.json")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="instead of the workloads: time the built-in model's pick against every "
+                         "direct-to-LDS and skinny variant on a sweep of 16-bit shapes")
     args = ap.parse_args()
     if args.record_counters or args.merge_record:
         if args.record_counters:
@@ -982,6 +1116,10 @@ def main():
     if not health.get("ok", True):
         log("GPU health warning before timing:", health)
     h = mg.mgemm_create()
+    if args.dispatch_sweep:
+        print(json.dumps({"dispatch_sweep": dispatch_sweep(h)}), flush=True)
+        mg.mgemm_destroy(h)
+        return
     table = workload_table()
     case = table[args.workload]
     hbm = is_hbm_bound(case)
