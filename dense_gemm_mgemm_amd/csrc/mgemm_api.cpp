@@ -129,9 +129,29 @@ double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int
     return t;
 }
 
+// True when a split of K into ks ranges (of ceil((K/32)/ks) 32-row slices)
+// makes the ranges of a streamed 16-bit B start a multiple of 2 MiB apart
+// while B's row pitch is a power of two of at least 8 KiB.  The ranges then
+// read addresses that agree in their low 21 bits at every step, and B
+// streams from HBM markedly slower (per-workgroup stamps, BF16 M = 32 x
+// W[K x 4096]: K = 8192 in 11 ranges, 6 MiB apart, 0.62 us per slice and
+// 4.1 TB/s against 0.43 us and 5.2 TB/s in 10 ranges, 6.5 MiB apart; K =
+// 4096 in 8 ranges 0.57 against 0.49 us in 10; the split skinny kernel at
+// 16 ranges, 2 MiB apart, 1.29 us per slice against 0.54 at 12).  A 24 KiB
+// pitch (W[K x 12288]) streams at full rate at 24 MiB apart.  Only M <= 64
+// is affected: larger M re-reads B from the caches, and there such splits
+// measured fastest (BF16 2048x4096x12288 in 2 ranges 177 us, 240 without).
+bool conflicting_split(const Problem& p, int ks) {
+    if (ks <= 1 || p.b_kc || p.M > 64 || p.dtype == mgemm::F32) return false;
+    const int64_t pitch = p.ldb * 2;
+    if (pitch < 8192 || (pitch & (pitch - 1)) != 0) return false;
+    const int64_t nk = p.K / 32, nks = (nk + ks - 1) / ks;
+    return (nks * 32 * pitch) % ((int64_t)2 << 20) == 0;
+}
+
 // Split of K with the smallest predicted time for the direct-to-LDS kernel
 // (tile width bn; the gated pair's tile holds 96 output columns), among the
-// splits that fit the workspace.
+// splits that fit the workspace and do not conflict as above.
 int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, double* t_out,
                int bm = 256) {
     const double speed = bn == 256 ? 1.4 : 1.3;
@@ -143,6 +163,7 @@ int auto_split(const Problem& p, int bn, bool dual, const mgemm::Workspace& ws, 
         const int ks = mgemm::h_dma_splits(p, bn, dual, req, ws, bm);
         if (ks <= last) continue;          // same number of ranges as a smaller request
         last = ks;
+        if (conflicting_split(p, ks)) continue;
         const double t = predict_us(p, bm, bn, out_n, speed, 1, ks);
         if (t < best_t) { best_t = t; best = ks; }
     }
@@ -206,10 +227,23 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // against 31.5).
     if (p.M <= 64 && p.K <= 2048 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
     const int64_t sk_blocks = (p.N + 255) / 256;
+    // The split skinny kernel's own choice of ranges, moved to the nearest
+    // count (within one round of workgroups) whose ranges do not conflict.
+    auto sk_split = [&]() {
+        const int ks = mgemm::skinny_sk_splits(p, ws, 0);
+        if (!conflicting_split(p, ks)) return ks;
+        for (int d : {-1, 1, -2, 2, -3, 3}) {
+            const int r = ks + d;
+            if (r < 2 || sk_blocks * r > slots) continue;
+            const int k2 = mgemm::skinny_sk_splits(p, ws, r);
+            if (k2 >= 2 && !conflicting_split(p, k2)) return k2;
+        }
+        return ks;
+    };
     if (p.M <= 16 && sk_blocks * 16 * 4 >= slots * 3 && mgemm::skinny_sk_supports(p))
-        return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
+        return {MGEMM_KERNEL_SKINNY_SK, sk_split()};
     if (p.M <= 64 && !mgemm::h_dma_supports(p, 192, 64)) {
-        if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, mgemm::skinny_sk_splits(p, ws, 0)};
+        if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, sk_split()};
         if (mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
     }
     // 16-bit: the variant (and split of K) with the smallest predicted time.
