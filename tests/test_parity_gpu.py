@@ -879,3 +879,27 @@ def test_dispatch_choices(h):
                for m in W.SKINNY_M)
     say("dispatch:", {c.name: sel(c) for c in [W.hgemm_colmajor(*s) for s in W.HGEMM_SHAPES]
                       + [W.ffn_bf16()] + [W.ffn_bf16(m) for m in W.SKINNY_M]})
+
+
+def test_skinny_dispatch_rules(h):
+    # The model's choices for M <= 64: whole-K for K <= 2048; the split skinny
+    # kernel only for M <= 16 on a B wide enough for its ranges to fill the
+    # CUs; 64-row tiles otherwise; and no K split whose ranges start a multiple
+    # of 2 MiB apart in a B with a power-of-two row pitch (8 KiB here).  Each
+    # choice is then run through mgemm_run and compared bit for bit with the
+    # oracle on integer data.
+    def sel(M, N, K):
+        return mg.mgemm_select_variant(h, "row", "row", M, N, K, 1.0, 256, K, 256, N, 0.0, 256, N,
+                                       "bf16")
+    assert sel(16, 1024, 2048) == ("skinny", 1)
+    assert sel(1, 12288, 4096)[0] == "skinny_sk"
+    assert sel(32, 1536, 4096)[0] == "h_dma_64x192"
+    for M, N, K in ((32, 4096, 4096), (32, 4096, 8192), (1, 4096, 12288), (64, 4096, 4096)):
+        name, ks = sel(M, N, K)
+        nks = -(-(K // 32) // ks)
+        say("skinny rule", (M, N, K), name, ks)
+        assert ks > 1 and (nks * 32 * N * 2) % (2 << 20) != 0, (M, N, K, name, ks)
+    for M, N, K in ((32, 1536, 4096), (32, 4096, 8192), (1, 4096, 12288), (16, 1024, 2048)):
+        case = W.Case("skinny_rule", M, N, K, "bf16", kindA="int", kindB="int", seeds=(M, N, K))
+        say("skinny rule parity", (M, N, K), sel(M, N, K))
+        P.check_bit_exact(case, *P.run_gpu(h, case))
