@@ -215,12 +215,12 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // split; M = 1 / 16 / 32 x 1024 columns 6.8 / 6.7 / 8.0 against 7.2 / 8.7 /
     // 11.5 on the split skinny kernel; K = 1024, M = 64: 9.4 against 15.7).
     // Longer K splits over workgroups.  The split skinny kernel reads B in
-    // 512-byte row segments of 256-column blocks; it wins only for M <= 16
-    // and only where at most 16 ranges of those blocks still give three
-    // quarters of the CUs a workgroup (BF16 x W[4096 x 12288], M = 1 / 16: 21.0
-    // / 22.4 us against 22.2 / 22.8 on 64-row tiles).  Narrower B, or more
-    // rows (whose cost the skinny kernel's 16-row MFMA blocks pay in full),
-    // go to the time model below, which picks the 64- or 128-row tiles of the
+    // 512-byte row segments of 256-column blocks; it wins only for M <= 16,
+    // only where at most 16 ranges of those blocks still give three quarters
+    // of the CUs a workgroup, and above 4 rows only where 6 ranges do (BF16 x
+    // W[4096 x 12288], M = 1 / 16: 21.0 / 22.4 us against 22.2 / 22.8 on
+    // 64-row tiles).  Narrower B, or more rows (whose cost the skinny
+    // kernel's 16-row MFMA blocks pay in full), go to the time model below, which picks the 64- or 128-row tiles of the
     // direct-to-LDS kernel with a K split (M = 1 / 16 / 32 x W[4096 x 1536]:
     // 7.6 / 7.9 / 8.5 us against 8.8 / 11.4 / 16.3 on the skinny kernel; M =
     // 32 x W[4096 x 4096] 15.0 against 17.1; M = 64 x W[4096 x 12288] 26.0
@@ -240,8 +240,18 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         }
         return ks;
     };
-    if (p.M <= 16 && sk_blocks * 16 * 4 >= slots * 3 && mgemm::skinny_sk_supports(p))
-        return {MGEMM_KERNEL_SKINNY_SK, sk_split()};
+    // Its last-arriving workgroup per block sums the other ranges' partial
+    // rows (M of them, through device-scope memory): cheap for a few rows or
+    // ranges, but for 8-16 rows over 8-16 ranges the 64-row tiles' separate
+    // sum pass is faster (M = 16 x W[4096 x 4096]: 13.2 us in 12 ranges
+    // against 11.5; M = 8: 12.1 against 11.4; M = 16 x W[4096 x 3072] 13.2
+    // against 10.2; but M = 16 x W[4096 x 8192] in 6 ranges 16.3 against 16.8,
+    // M = 8 x W[8192 x 8192] 27.5 against 29.2, M = 1 x W[4096 x 4096] in 10
+    // ranges 10.9 against 11.2).
+    if (p.M <= 16 && sk_blocks * 16 * 4 >= slots * 3 && mgemm::skinny_sk_supports(p)) {
+        const int ks = sk_split();
+        if (p.M <= 4 || ks <= 6) return {MGEMM_KERNEL_SKINNY_SK, ks};
+    }
     if (p.M <= 64 && !mgemm::h_dma_supports(p, 192, 64)) {
         if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, sk_split()};
         if (mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
