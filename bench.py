@@ -555,9 +555,10 @@ SWEEP_TILES = {"h_dma_256x256": (256, 256), "h_dma_256x192": (256, 192),
 
 
 def sweep_shapes():
-    """16-bit shapes of the dispatch sweep: projections x W[K x N] of common
-    widths at 1 to 4096 rows, square column-major FP16 products, and a few
-    x W^T (B column-major) skinny shapes."""
+    """Shapes of the dispatch sweep: BF16 projections x W[K x N] of common
+    widths at 1 to 4096 rows, square column-major FP16 products, a few x W^T
+    (B column-major) skinny shapes, and FP32 products (square, ragged and
+    short M)."""
     out = []
     for n, k in [(1536, 4096), (4096, 4096), (12288, 4096), (4096, 12288), (4096, 1024),
                  (1024, 2048)]:
@@ -577,12 +578,18 @@ def sweep_shapes():
     for m, n, k in [(1, 4096, 4096), (16, 4096, 4096), (32, 4096, 4096), (16, 1536, 4096),
                     (16, 12288, 4096), (32, 12288, 4096)]:
         out.append(("bf16", "row", "col", m, n, k))
+    for m, n, k in [(256, 256, 256), (512, 512, 512), (1000, 1000, 1000), (1024, 1024, 1024),
+                    (2048, 2048, 2048), (3000, 3000, 3000), (4096, 4096, 4096), (4096, 3072, 4096),
+                    (1000, 12290, 4095), (1, 12288, 4096), (64, 12288, 4096), (256, 4096, 4096),
+                    (1024, 4096, 4096), (2048, 8192, 1024), (768, 768, 768), (1536, 1536, 1536)]:
+        out.append(("f32", "row", "row", m, n, k))
     return out
 
 
 def dispatch_sweep(h):
     """Time the model's pick (kernel 'auto') and every direct-to-LDS and
-    skinny variant at each split on every sweep shape.  Each candidate: three
+    skinny variant at each split (FP32: every FP32 kernel) on every sweep
+    shape.  Each candidate: three
     warm-up launches, then 10-40 launches back to back behind a stream hold,
     between two HIP events.  Operands whose B has at least 16 MiB rotate over
     four copies; smaller ones stay resident (warm last-level cache, as in the
@@ -619,8 +626,8 @@ def dispatch_sweep(h):
     rows = []
     shapes = sweep_shapes()
     for si, (dtype, la, lb, M, N, K) in enumerate(shapes):
-        td = torch.float16 if dtype == "f16" else torch.bfloat16
-        rot = 4 if K * N * 2 >= 16 * 2 ** 20 else 1
+        td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+        rot = 4 if K * N * td.itemsize >= 16 * 2 ** 20 else 1
         g = torch.Generator(device="cuda").manual_seed(M * 7 + N * 3 + K)
         A = [(torch.rand((M * K,), generator=g, device="cuda") - 0.5).to(td) for _ in range(rot)]
         B = [(torch.rand((K * N,), generator=g, device="cuda") * 0.04 - 0.02).to(td)
@@ -632,14 +639,16 @@ def dispatch_sweep(h):
         est = 2.0 * M * N * K / 1e9 + 8.0
         nk = K // 32
         cands = [("auto", 0)]
-        for kern, (bm, bn) in SWEEP_TILES.items():
+        if dtype == "f32":
+            cands += [(k, 1) for k in ("f32_fast", "f32_fast_128", "f32_fast_u", "f32_sk", "f32_mfma")]
+        for kern, (bm, bn) in (SWEEP_TILES.items() if dtype != "f32" else ()):
             seen = set()
             for req in SWEEP_SPLITS:
                 ks = ranges(req, nk)
                 if ks not in seen and -(-M // bm) * -(-N // bn) * ks <= 6144:
                     seen.add(ks)
                     cands.append((kern, req))
-        if M <= 64:
+        if M <= 64 and dtype != "f32":
             seen = set()
             for req in SWEEP_SPLITS:
                 ks = ranges(req, nk)
@@ -657,7 +666,8 @@ def dispatch_sweep(h):
                 us = time_one(launch, est)
             except mg.MgemmError:
                 continue                        # the variant does not run this shape
-            key = model if kern == "auto" else (kern, ranges(req, nk) if kern != "skinny" else 1)
+            key = model if kern == "auto" else (kern, ranges(req, nk) if kern != "skinny" and
+                                                dtype != "f32" else 1)
             times[key] = min(us, times.get(key, float("inf")))
         best = min(times.items(), key=lambda kv: kv[1])
         rows.append([dtype, la, lb, M, N, K, model[0], model[1], round(times[model], 2),
@@ -1076,7 +1086,7 @@ def main():
                     help="add an entry printed by --record-counters to profiles/traffic.json")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="instead of the workloads: time the built-in model's pick against every "
-                         "direct-to-LDS and skinny variant on a sweep of 16-bit shapes")
+                         "variant on a sweep of FP16/BF16 and FP32 shapes")
     args = ap.parse_args()
     if args.record_counters or args.merge_record:
         if args.record_counters:
