@@ -25,7 +25,7 @@ KERNELS = ["auto", "general", "f32_mfma", "h_mfma_256x256", "h_mfma_256x192", "h
            "skinny", "reserved_7", "f32_fast", "f32_fast_128",
            "h_dma_256x256", "skinny_sk", "h_dma_256x192", "f32_fast_u",
            "f8_mfma_256x256", "f8_general", "f8_mfma_256x192", "f32_sk", "h_dma_128x192",
-           "h_dma_64x192"]
+           "h_dma_64x192", "f8_mfma_128x192"]
 MGEMM_KERNEL_AUTO = 0
 MGEMM_EPILOGUE_NONE, MGEMM_EPILOGUE_SILU = 0, 1
 _EPILOGUE = {"none": MGEMM_EPILOGUE_NONE, "silu": MGEMM_EPILOGUE_SILU}

@@ -33,7 +33,7 @@
 // Restrictions of the MFMA kernel (host-checked): K >= 64 (a last partial
 // slice is staged by ordinary loads with zero codes past K), lda and ldb
 // multiples of 16, 16-byte aligned code buffers; k_f8_general takes the rest.
-#include "common.h"
+#include "f8_tiles.h"
 
 namespace mgemm {
 namespace {
@@ -233,16 +233,21 @@ __global__ __launch_bounds__(256) void k_quant_rows_reg(int64_t /*M: one workgro
 #ifndef MGEMM_F8_SLOTS
 #define MGEMM_F8_SLOTS 4
 #endif
-constexpr int BM = 256, BK = 64, NT = 256;
+constexpr int BK = 64, NT = 256;
 constexpr int SLOTS = MGEMM_F8_SLOTS, AHEAD = SLOTS - 1;   // slices in flight
 constexpr int ROW = BK;                          // bytes per operand row per slice
-constexpr int A_BYTES = BM * ROW;                // 16 KiB of A per slot
-constexpr int A_COPIES = 4;                      // 1 KiB copies of A per wave per slice
-constexpr int TM = 4;                            // 32-row blocks per wave (128 rows)
 
-template <int BN>
+// BMT is the tile height: 256 (the four waves laid out 2x2 hold 128 x BN/2
+// each), or 128 with the 192-wide slot (64 x 96 per wave) for products whose
+// 256-row grid would leave CUs idle.
+template <int BN, int BMT = 256>
 struct F8Cfg {
     static_assert(BN == 256 || BN == 192, "tile width");
+    static_assert(BMT == 256 || (BMT == 128 && BN == 192), "tile height");
+    static constexpr int A_BYTES = BMT * ROW;    // 16 or 8 KiB of A per slot
+    static constexpr int A_COPIES = BMT / 64;    // 1 KiB copies of A per wave per slice
+    static constexpr int WROWS = BMT / 2;        // rows per wave
+    static constexpr int TM = WROWS / 32;        // 32-row blocks per wave
     static constexpr int B_COPIES = BN / 64;     // 1 KiB copies of B per wave per slice
     static constexpr int COPIES = A_COPIES + B_COPIES;
     static constexpr int SLOT_BYTES = A_BYTES + BN * ROW;
@@ -276,7 +281,7 @@ __device__ __forceinline__ void slice_barrier() {
     fence_sched();
 }
 
-template <int TN>
+template <int TM, int TN>
 struct Frags {
     i32x4 a[TM][2];
     i32x4 b[TN][2];
@@ -335,12 +340,12 @@ __device__ __forceinline__ void store4(void* C, int64_t ldc, int64_t m, int64_t 
 // 10 us per call when every column's scale was loaded next to its store).
 // The 256-wide tile does this in two halves of its columns to stay within
 // the registers.
-template <int CT, int BN>
-__device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[TM][BN / 64], const Problem& p,
+template <int CT, int BN, int BMT>
+__device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[BMT / 64][BN / 64], const Problem& p,
                                             const float* sa, const float* sb, void* C, int lane,
                                             int wm, int wn, int64_t m0, int64_t n0, int mlim,
                                             int nlim) {
-    constexpr int TN = BN / 64;
+    constexpr int TM = BMT / 64, TN = BN / 64, WROWS = BMT / 2;
     constexpr int PH = BN == 256 ? 2 : 1, TNP = TN / PH;    // column phases
     const int fr = lane & 31, nq = 4 * (lane >> 5);
     const int es = CT == F32 ? 4 : 2;
@@ -349,7 +354,7 @@ __device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[TM][BN / 64], co
     float sav[TM];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int mi = 128 * wm + 32 * tm + fr;
+        const int mi = WROWS * wm + 32 * tm + fr;
         sav[tm] = mi < mlim ? sa[m0 + mi] : 0.0f;
     }
 #pragma unroll
@@ -369,7 +374,7 @@ __device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[TM][BN / 64], co
             }
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const int mi = 128 * wm + 32 * tm + fr;
+            const int mi = WROWS * wm + 32 * tm + fr;
             if (mi >= mlim) continue;
 #pragma unroll
             for (int t = 0; t < TNP; ++t)
@@ -389,11 +394,12 @@ __device__ __forceinline__ void f8_epilogue(const f32x16 (&acc)[TM][BN / 64], co
     }
 }
 
-template <int CT, int BN, bool PARTIAL>
+template <int CT, int BN, bool PARTIAL, int BMT = 256>
 __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
-    using G = F8Cfg<BN>;
-    constexpr int TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
-    using Fr = Frags<TN>;
+    using G = F8Cfg<BN, BMT>;
+    constexpr int BM = BMT, TM = G::TM, TN = G::TN, COPIES = G::COPIES, SLOT_BYTES = G::SLOT_BYTES;
+    constexpr int A_COPIES = G::A_COPIES, A_BYTES = G::A_BYTES, WROWS = G::WROWS;
+    using Fr = Frags<TM, TN>;
     extern __shared__ __align__(16) unsigned char smem[];
     const ClockStamp stamp0 = clock_stamp_begin();
     const int tid = threadIdx.x, lane = tid & 63;
@@ -423,11 +429,11 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
     int dst[COPIES];
 #pragma unroll
     for (int i = 0; i < A_COPIES; ++i) {
-        const int r = 64 * wave + 16 * i + (lane >> 2);
+        const int r = BM / 4 * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
         const int ra = r < mlim ? r : mlim - 1;
         src[i] = A + (m0 + ra) * p.lda + 16 * c;
-        dst[i] = (64 * wave + 16 * i) * ROW;
+        dst[i] = (BM / 4 * wave + 16 * i) * ROW;
     }
 #pragma unroll
     for (int i = 0; i < G::B_COPIES; ++i) {
@@ -449,7 +455,7 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         const int c = 2 * (lane >> 5) + h;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const int ra = 128 * wm + 32 * t + (lane & 31);
+            const int ra = WROWS * wm + 32 * t + (lane & 31);
             a_off[t][h] = ra * ROW + ((c ^ swz(ra)) << 4);
         }
 #pragma unroll
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         unsigned char* slot = smem + (ts % SLOTS) * SLOT_BYTES;
 #pragma unroll
         for (int i = 0; i < COPIES; ++i) {
-            const int r = i < A_COPIES ? 64 * wave + 16 * i + (lane >> 2)
+            const int r = i < A_COPIES ? BM / 4 * wave + 16 * i + (lane >> 2)
                                        : BN / 4 * wave + 16 * (i - A_COPIES) + (lane >> 2);
             const int kfirst = 16 * ((lane & 3) ^ swz(r));
             const uint8_t* s = src[i] + (int64_t)ts * BK;
@@ -588,16 +594,16 @@ __global__ __launch_bounds__(NT, 1) void k_f8_dma(Problem p, F8Args f) {
         clock_stamp_end(p, stamp0);
         return;
     }
-    f8_epilogue<CT, BN>(acc, p, f.sa, f.sb, p.C, lane, wm, wn, m0, n0, mlim, nlim);
+    f8_epilogue<CT, BN, BMT>(acc, p, f.sa, f.sb, p.C, lane, wm, wn, m0, n0, mlim, nlim);
     clock_stamp_end(p, stamp0);
 }
 
 // Second split-K phase: one thread per 16-byte chunk of a tile's
 // accumulators sums the K ranges in range order, then scales and stores the
 // four outputs as the one-phase epilogue would.
-template <int CT, int BN>
+template <int CT, int BN, int BMT = 256>
 __global__ __launch_bounds__(NT) void k_f8_reduce(Problem p, F8Args f) {
-    constexpr int TN = BN / 64, CH = TM * TN * 4;
+    constexpr int BM = BMT, TM = BMT / 64, TN = BN / 64, CH = TM * TN * 4;
     constexpr int64_t TILE_FLOATS = (int64_t)NT * TM * TN * 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -610,7 +616,7 @@ __global__ __launch_bounds__(NT) void k_f8_reduce(Problem p, F8Args f) {
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const int mlim = (int)(p.M - m0 < BM ? p.M - m0 : BM);
     const int nlim = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-    const int mi = 128 * wm + 32 * tm + (lane & 31);
+    const int mi = BMT / 2 * wm + 32 * tm + (lane & 31);
     const int ni = BN / 2 * wn + 32 * tn + 8 * q + 4 * (lane >> 5);
     if (mi >= mlim || ni >= nlim) return;
     const float* src = f.part + (int64_t)(tmi * tiles_n + tni) * f.ksplit * TILE_FLOATS + (int64_t)c * NT * 4 + 4 * tid;
@@ -719,10 +725,11 @@ hipError_t launch_quant_xt(int64_t M, int64_t K, const void* X, int64_t ldx, uin
     return hipGetLastError();
 }
 
-template <int CT, int BN, bool PARTIAL>
+template <int CT, int BN, bool PARTIAL, int BMT = 256>
 hipError_t launch_f8_dma(const Problem& p, const F8Args& f, hipStream_t s) {
-    auto kern = k_f8_dma<CT, BN, PARTIAL>;
-    const size_t lds = (size_t)SLOTS * F8Cfg<BN>::SLOT_BYTES;
+    constexpr int BM = BMT;
+    auto kern = k_f8_dma<CT, BN, PARTIAL, BMT>;
+    const size_t lds = (size_t)SLOTS * F8Cfg<BN, BMT>::SLOT_BYTES;
     static bool attr_set[MAX_DEVICES] = {};
     if (hipError_t e = set_lds_limit_once((const void*)kern, (int)lds, attr_set); e != hipSuccess)
         return e;
@@ -730,15 +737,19 @@ hipError_t launch_f8_dma(const Problem& p, const F8Args& f, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * f.ksplit)), dim3(NT), lds, s, p, f);
     if constexpr (PARTIAL) {
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-        constexpr int CH = TM * (BN / 64) * 4;
-        hipLaunchKernelGGL((k_f8_reduce<CT, BN>), dim3((unsigned)(tiles * CH)), dim3(NT), 0, s, p, f);
+        constexpr int CH = F8Cfg<BN, BMT>::TM * (BN / 64) * 4;
+        hipLaunchKernelGGL((k_f8_reduce<CT, BN, BMT>), dim3((unsigned)(tiles * CH)), dim3(NT), 0, s, p, f);
     }
     return hipGetLastError();
 }
 
-// bn: 256 or 192 for the MFMA kernel, 0 for the scalar kernel.
+// bn: 256 or 192 for the MFMA kernel, 0 for the scalar kernel; bm: 256, or
+// 128 with bn = 192.
 template <int CT>
-hipError_t launch_f8_ct(const Problem& p, const F8Args& f, int bn, hipStream_t s) {
+hipError_t launch_f8_ct(const Problem& p, const F8Args& f, int bn, int bm, hipStream_t s) {
+    if (bm == 128 && bn == 192)
+        return f.ksplit > 1 ? launch_f8_dma<CT, 192, true, 128>(p, f, s)
+                            : launch_f8_dma<CT, 192, false, 128>(p, f, s);
     if (bn == 256)
         return f.ksplit > 1 ? launch_f8_dma<CT, 256, true>(p, f, s) : launch_f8_dma<CT, 256, false>(p, f, s);
     if (bn == 192)
@@ -757,8 +768,10 @@ hipError_t launch_quantize_fp8(int64_t M, int64_t K, const void* X, int64_t ldx,
     return launch_quant_xt<BF16>(M, K, X, ldx, (uint8_t*)Q, ldq, scales, s);
 }
 
-bool f8_mfma_supports(const Problem& p, int bn) {
+bool f8_mfma_supports_bm(const Problem& p, int bn, int bm) {
     if (bn != 256 && bn != 192) return false;
+    if (bm != 256 && (bm != 128 || bn != 192)) return false;
+    const int BM = bm;
     // K >= 64; a last partial slice (K not a multiple of 64) is staged by
     // ordinary loads with zero codes past K.
     if (p.K < BK || p.lda % 16 != 0 || p.ldb % 16 != 0) return false;
@@ -767,11 +780,14 @@ bool f8_mfma_supports(const Problem& p, int bn) {
     return tiles > 0 && tiles <= 0x7fffffff;
 }
 
+bool f8_mfma_supports(const Problem& p, int bn) { return f8_mfma_supports_bm(p, bn, 256); }
+
 bool f8_general_supports(const Problem& p) {
     return ((p.M + FG_T - 1) / FG_T) * ((p.N + FG_T - 1) / FG_T) <= 0x7fffffff;
 }
 
-int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws) {
+int f8_splits_bm(const Problem& p, int bn, int bm, int requested, const Workspace& ws) {
+    const int BM = bm;
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + bn - 1) / bn);
     const int64_t nk = p.K / BK;
     if (requested <= 1 || nk < 2) return 1;
@@ -782,17 +798,26 @@ int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws) {
     return (int)ks;
 }
 
-hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, int ksplit,
-                          const Workspace& ws, hipStream_t s) {
+int f8_splits(const Problem& p, int bn, int requested, const Workspace& ws) {
+    return f8_splits_bm(p, bn, 256, requested, ws);
+}
+
+hipError_t launch_f8_gemm_bm(const Problem& p, const float* sa, const float* sb, int bn, int bm,
+                             int ksplit, const Workspace& ws, hipStream_t s) {
     F8Args f{sa, sb, (float*)ws.part, 1, (int)(p.K / BK)};
     if (bn != 0 && ksplit > 1) {
         const int nk = (int)(p.K / BK);
         f.nks = (nk + ksplit - 1) / ksplit;
         f.ksplit = (nk + f.nks - 1) / f.nks;
     }
-    if (p.dtype == F32) return launch_f8_ct<F32>(p, f, bn, s);
-    if (p.dtype == F16) return launch_f8_ct<F16>(p, f, bn, s);
-    return launch_f8_ct<BF16>(p, f, bn, s);
+    if (p.dtype == F32) return launch_f8_ct<F32>(p, f, bn, bm, s);
+    if (p.dtype == F16) return launch_f8_ct<F16>(p, f, bn, bm, s);
+    return launch_f8_ct<BF16>(p, f, bn, bm, s);
+}
+
+hipError_t launch_f8_gemm(const Problem& p, const float* sa, const float* sb, int bn, int ksplit,
+                          const Workspace& ws, hipStream_t s) {
+    return launch_f8_gemm_bm(p, sa, sb, bn, 256, ksplit, ws, s);
 }
 
 }  // namespace mgemm

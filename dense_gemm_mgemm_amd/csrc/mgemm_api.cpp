@@ -5,7 +5,9 @@
 
 #include <new>
 #include <string.h>
+#include <utility>
 
+#include "f8_tiles.h"
 #include "host.h"
 
 namespace mgemm_host {
@@ -592,7 +594,8 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
     if (ksplit < 0 || ksplit > MGEMM_MAX_KSPLIT || (kernel == MGEMM_KERNEL_AUTO && ksplit != 0))
         return MGEMM_ERR_INVALID_ARG;
     if (kernel != MGEMM_KERNEL_AUTO && kernel != MGEMM_KERNEL_F8_MFMA &&
-        kernel != MGEMM_KERNEL_F8_MFMA_192 && kernel != MGEMM_KERNEL_F8_GENERAL)
+        kernel != MGEMM_KERNEL_F8_MFMA_192 && kernel != MGEMM_KERNEL_F8_MFMA_128 &&
+        kernel != MGEMM_KERNEL_F8_GENERAL)
         return MGEMM_ERR_INVALID_ARG;
     if (lda < max1(K) || ldb < max1(K) || ldc < max1(N)) return MGEMM_ERR_INVALID_ARG;
     const int64_t lim = (int64_t)1 << 62;
@@ -617,48 +620,54 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
         return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
     }
     if (!A || !B || !sa || !sb) return MGEMM_ERR_INVALID_ARG;
-    // The MFMA kernel's time per (width, split) by the 16-bit time model: a
+    // The MFMA kernel's time per (tile, split) by the 16-bit time model: a
     // 64-wide FP8 slice moves the bytes of a 32-wide 16-bit slice and measured
     // the same time per slice (0.59 us for 256x192 tiles at 1024x12288).
     Problem q = p;
     q.K = p.K / 2;
-    auto best_split = [&](int w, double* t_out) {
+    auto best_split = [&](int w, int bm, double* t_out) {
         int best = 1;
         double bt = 1e300;
         for (int req = 1, last = 0; req <= MGEMM_MAX_KSPLIT; ++req) {
-            const int ks = mgemm::f8_splits(p, w, req, h->ws);
+            const int ks = mgemm::f8_splits_bm(p, w, bm, req, h->ws);
             if (ks <= last) continue;
             last = ks;
-            const double t = predict_us(q, 256, w, w, w == 256 ? 1.4 : 1.3, 1, ks);
+            const double t = predict_us(q, bm, w, w, w == 256 ? 1.4 : 1.3, 1, ks);
             if (t < bt) { bt = t; best = ks; }
         }
         if (t_out) *t_out = bt;
         return best;
     };
-    int bn = -1, ks = 1;                 // MFMA tile width (0 = scalar kernel), K ranges
-    if (kernel == MGEMM_KERNEL_F8_MFMA || kernel == MGEMM_KERNEL_F8_MFMA_192) {
+    // MFMA tile width (0 = scalar kernel) and height, K ranges.
+    int bn = -1, bm = 256, ks = 1;
+    if (kernel == MGEMM_KERNEL_F8_MFMA || kernel == MGEMM_KERNEL_F8_MFMA_192 ||
+        kernel == MGEMM_KERNEL_F8_MFMA_128) {
         bn = kernel == MGEMM_KERNEL_F8_MFMA ? 256 : 192;
-        if (!mgemm::f8_mfma_supports(p, bn)) return MGEMM_ERR_UNSUPPORTED;
-        ks = ksplit == 0 ? best_split(bn, nullptr) : mgemm::f8_splits(p, bn, ksplit, h->ws);
+        bm = kernel == MGEMM_KERNEL_F8_MFMA_128 ? 128 : 256;
+        if (!mgemm::f8_mfma_supports_bm(p, bn, bm)) return MGEMM_ERR_UNSUPPORTED;
+        ks = ksplit == 0 ? best_split(bn, bm, nullptr)
+                         : mgemm::f8_splits_bm(p, bn, bm, ksplit, h->ws);
         if (ks < 1) return MGEMM_ERR_UNSUPPORTED;
     } else if (kernel == MGEMM_KERNEL_F8_GENERAL) {
         if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
         if (ksplit > 1) return MGEMM_ERR_UNSUPPORTED;
         bn = 0;
     } else {
+        // 128-row tiles (width 192) where a grid of 256-row tiles leaves CUs
+        // idle: FP8 4096x1536x4096, 128 tiles of 256x192, against 256 of 128x192.
         double best_t = 1e300;
-        for (int w : {256, 192}) {
-            if (!mgemm::f8_mfma_supports(p, w)) continue;
+        for (const auto& [w, tm] : {std::pair<int, int>{256, 256}, {192, 256}, {192, 128}}) {
+            if (!mgemm::f8_mfma_supports_bm(p, w, tm)) continue;
             double t;
-            const int k2 = best_split(w, &t);
-            if (t < best_t) { best_t = t; bn = w; ks = k2; }
+            const int k2 = best_split(w, tm, &t);
+            if (t < best_t) { best_t = t; bn = w; bm = tm; ks = k2; }
         }
         if (bn < 0) {
             if (!mgemm::f8_general_supports(p)) return MGEMM_ERR_UNSUPPORTED;
             bn = 0;
         }
     }
-    hipError_t e = mgemm::launch_f8_gemm(p, sa, sb, bn, ks, h->ws, stream);
+    hipError_t e = mgemm::launch_f8_gemm_bm(p, sa, sb, bn, bm, ks, h->ws, stream);
     return e == hipSuccess ? MGEMM_SUCCESS : MGEMM_ERR_HIP;
 }
 
@@ -757,6 +766,7 @@ const char* mgemm_kernel_name(mgemm_kernel_t k) {
     case MGEMM_KERNEL_F8_MFMA: return "f8_mfma_256x256";
     case MGEMM_KERNEL_F8_GENERAL: return "f8_general";
     case MGEMM_KERNEL_F8_MFMA_192: return "f8_mfma_256x192";
+    case MGEMM_KERNEL_F8_MFMA_128: return "f8_mfma_128x192";
     case MGEMM_KERNEL_F32_SK: return "f32_sk";
     case MGEMM_KERNEL_H_DMA_128: return "h_dma_128x192";
     case MGEMM_KERNEL_H_DMA_64: return "h_dma_64x192";

@@ -87,7 +87,10 @@ typedef enum {
     MGEMM_KERNEL_H_DMA_64 = 19,  /* FP16/BF16, A' K-contiguous, 64x192 tiles, 4 waves of 32x96,
                                     direct-to-LDS ring (32 < M <= 64: streams B from HBM;
                                     also small grids with a small B) */
-    MGEMM_KERNEL_COUNT = 20
+    MGEMM_KERNEL_F8_MFMA_128 = 20, /* FP8 codes (mgemm_run_fp8 only): 128x192 tiles, 4 waves of
+                                      64x96, f8f6f4 MFMA (grids of 256-row tiles that leave CUs
+                                      idle) */
+    MGEMM_KERNEL_COUNT = 21
 } mgemm_kernel_t;
 
 /* Output epilogues (see mgemm_run_ex). */
@@ -435,12 +438,12 @@ mgemm_status_t mgemm_quantize_fp8(mgemm_handle_t h, int64_t M, int64_t K, const 
  *        out_features x in_features; row stride ldb >= max(1, K)), sb: N scales;
  *   C  : M x N, row-major, ldc >= max(1, N), element type ctype (F32, F16,
  *        BF16); beta == 0 never reads C.
- *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA or
- *        MGEMM_KERNEL_F8_MFMA_192 (K >= 64, lda and ldb multiples of 16,
+ *   kernel : MGEMM_KERNEL_AUTO, MGEMM_KERNEL_F8_MFMA, MGEMM_KERNEL_F8_MFMA_192
+ *        or MGEMM_KERNEL_F8_MFMA_128 (K >= 64, lda and ldb multiples of 16,
  *        16-byte aligned A and B; a K that is not a multiple of 64 ends with
  *        a partial slice) or MGEMM_KERNEL_F8_GENERAL (anything).
- *        AUTO takes the MFMA tile width and split of K with the smallest
- *        predicted time.
+ *        AUTO takes the MFMA tile (256x256, 256x192 or 128x192) and split
+ *        of K with the smallest predicted time.
  *   ksplit : 0 = the library's choice, 1 = no split, 2 .. MGEMM_MAX_KSPLIT =
  *        at most that many K ranges of whole 64-element slices (MFMA kernels
  *        only), summed in range order by a second launch as mgemm_run_variant

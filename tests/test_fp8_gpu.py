@@ -132,7 +132,8 @@ def test_fp8_gemm_integer_bit_exact(h, M, N, K, ctype):
     want = oracle.encode(ctype, exact)
     ran = 0
     for kernel, ks in (("auto", 0), ("f8_mfma_256x256", 1), ("f8_mfma_256x256", 3),
-                       ("f8_mfma_256x192", 0), ("f8_mfma_256x192", 32), ("f8_general", 1)):
+                       ("f8_mfma_256x192", 0), ("f8_mfma_256x192", 32), ("f8_mfma_128x192", 1),
+                       ("f8_mfma_128x192", 5), ("f8_general", 1)):
         dA = torch.from_numpy(pa.ravel()).cuda()
         dB = torch.from_numpy(pb.ravel()).cuda()
         dsa, dsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
@@ -150,7 +151,7 @@ def test_fp8_gemm_integer_bit_exact(h, M, N, K, ctype):
         assert bad.size == 0, (kernel, bad[:5], got[tuple(bad[0])], want[tuple(bad[0])])
         assert np.array_equal(got[:, N:], c0_bits[:, N:])   # ldc padding untouched
         ran += 1
-    assert ran == 6
+    assert ran == 8
 
 
 def fp8_inputs(case):
