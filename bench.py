@@ -557,8 +557,8 @@ SWEEP_TILES = {"h_dma_256x256": (256, 256), "h_dma_256x192": (256, 192),
 def sweep_shapes():
     """Shapes of the dispatch sweep: BF16 projections x W[K x N] of common
     widths at 1 to 4096 rows, square column-major FP16 products, a few x W^T
-    (B column-major) skinny shapes, and FP32 products (square, ragged and
-    short M)."""
+    (B column-major) skinny shapes, FP32 products (square, ragged and short
+    M), and FP8 E4M3 products (codes M x K and N x K, BF16 out)."""
     out = []
     for n, k in [(1536, 4096), (4096, 4096), (12288, 4096), (4096, 12288), (4096, 1024),
                  (1024, 2048)]:
@@ -583,13 +583,18 @@ def sweep_shapes():
                     (1000, 12290, 4095), (1, 12288, 4096), (64, 12288, 4096), (256, 4096, 4096),
                     (1024, 4096, 4096), (2048, 8192, 1024), (768, 768, 768), (1536, 1536, 1536)]:
         out.append(("f32", "row", "row", m, n, k))
+    for m, n, k in [(4096, 1536, 4096), (1024, 12288, 4096), (1024, 1536, 4096), (2048, 4096, 4096),
+                    (512, 4096, 4096), (256, 12288, 4096), (8192, 8192, 8192), (4096, 4096, 4096),
+                    (2048, 1536, 4096), (3072, 3072, 4096)]:
+        out.append(("fp8", "row", "col", m, n, k))
     return out
 
 
 def dispatch_sweep(h):
     """Time the model's pick (kernel 'auto') and every direct-to-LDS and
-    skinny variant at each split (FP32: every FP32 kernel) on every sweep
-    shape.  Each candidate: three
+    skinny variant at each split (FP32: every FP32 kernel; FP8: every MFMA
+    tile at 1-8 K ranges, the model's pick timed as the 'auto' call) on
+    every sweep shape.  Each candidate: three
     warm-up launches, then 10-40 launches back to back behind a stream hold,
     between two HIP events.  Operands whose B has at least 16 MiB rotate over
     four copies; smaller ones stay resident (warm last-level cache, as in the
@@ -626,6 +631,29 @@ def dispatch_sweep(h):
     rows = []
     shapes = sweep_shapes()
     for si, (dtype, la, lb, M, N, K) in enumerate(shapes):
+        if dtype == "fp8":
+            g = torch.Generator(device="cuda").manual_seed(M * 7 + N * 3 + K)
+            qa = torch.randint(0, 0x70, (M * K,), generator=g, dtype=torch.uint8, device="cuda")
+            qb = torch.randint(0, 0x70, (N * K,), generator=g, dtype=torch.uint8, device="cuda")
+            sa, sb = torch.ones(M, device="cuda"), torch.ones(N, device="cuda")
+            C = torch.empty(M * N, dtype=torch.bfloat16, device="cuda")
+            times = {}
+            for kern in ("auto", "f8_mfma_256x256", "f8_mfma_256x192", "f8_mfma_128x192"):
+                for ks in ((0,) if kern == "auto" else (1, 2, 3, 4, 6, 8)):
+                    def launch(i, kern=kern, ks=ks):
+                        mg.mgemm_run_fp8(h, kern, M, N, K, 1.0, qa, K, sa, qb, K, sb, 0.0, C, N,
+                                         "bf16", stream=s, ksplit=ks)
+                    try:
+                        times[(kern, ks)] = time_one(launch, M * N * K / 1e9 + 8.0)
+                    except mg.MgemmError:
+                        continue
+            best = min((kv for kv in times.items() if kv[0][0] != "auto"), key=lambda kv: kv[1])
+            rows.append([dtype, la, lb, M, N, K, "auto", 0, round(times[("auto", 0)], 2),
+                         best[0][0], best[0][1], round(best[1], 2)])
+            log("sweep %d/%d fp8 %dx%dx%d: model %.2f us, best %s/%d %.2f us" % (
+                si + 1, len(shapes), M, N, K, times[("auto", 0)], best[0][0], best[0][1], best[1]))
+            del qa, qb, C
+            continue
         td = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
         rot = 4 if K * N * td.itemsize >= 16 * 2 ** 20 else 1
         g = torch.Generator(device="cuda").manual_seed(M * 7 + N * 3 + K)
@@ -679,7 +707,11 @@ def dispatch_sweep(h):
         torch.cuda.empty_cache()
     ratios = [r[8] / r[11] for r in rows]
     worst = sorted(rows, key=lambda r: -r[8] / r[11])[:10]
+    by_dtype = {}
+    for r, x in zip(rows, ratios):
+        by_dtype.setdefault("fp16/bf16" if r[0] in ("f16", "bf16") else r[0], []).append(x)
     return {"shapes": len(rows), "mean_model_over_best": round(statistics.mean(ratios), 4),
+            "mean_by_dtype": {k: [len(v), round(statistics.mean(v), 4)] for k, v in by_dtype.items()},
             "max_model_over_best": round(max(ratios), 3),
             "model_over_best_above_1.05": sum(x > 1.05 for x in ratios),
             "columns": ["dtype", "layoutA", "layoutB", "M", "N", "K", "model_kernel", "model_ks",
