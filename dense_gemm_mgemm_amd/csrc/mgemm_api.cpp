@@ -113,9 +113,12 @@ bool variant_supports(const Problem& p, mgemm_kernel_t k) {
 // 2.58 ms).  A slice never takes less than its operand bytes ((bm + bn) x 32
 // 16-bit values) at 60 KB/us per CU: the rate one CU's copies reach (128-
 // and 64-row tiles of 1024^3, 512x1024x2048 and 256x1536x4096 spend 0.33 and
-// 0.25-0.27 us per slice, above their share of the MFMA time).
-double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int per_cu, int ks) {
-    constexpr double SLICE_US = 0.98, WG_US = 2.0, PASS_US = 4.0, PART_BYTES_PER_US = 2.6e6;
+// 0.25-0.27 us per slice, above their share of the MFMA time).  `part_rate`
+// replaces the partials' 2.6 TB/s where a caller measured its own.
+double predict_us(const Problem& p, int bm, int bn, int out_n, double speed, int per_cu, int ks,
+                  double part_rate = 0.0) {
+    constexpr double SLICE_US = 0.98, WG_US = 2.0, PASS_US = 4.0;
+    const double PART_BYTES_PER_US = part_rate > 0.0 ? part_rate : 2.6e6;
     constexpr double CU_BYTES_PER_US = 60e3;
     const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
     const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + out_n - 1) / out_n);
@@ -622,7 +625,11 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
     if (!A || !B || !sa || !sb) return MGEMM_ERR_INVALID_ARG;
     // The MFMA kernel's time per (tile, split) by the 16-bit time model: a
     // 64-wide FP8 slice moves the bytes of a 32-wide 16-bit slice and measured
-    // the same time per slice (0.59 us for 256x192 tiles at 1024x12288).
+    // the same time per slice (0.59 us for 256x192 tiles at 1024x12288).  The
+    // partials of a split are priced at 4.5 TB/s: timing every tile at 1-8
+    // ranges on ten FP8 shapes, the 16-bit 2.6 TB/s kept 256x12288x4096 and
+    // 2048x1536x4096 unsplit on 128x192 tiles (31.0 / 30.4 us) where 2 ranges
+    // take 27.2 / 27.6 us; at 4.5 TB/s every pick is within 2.1% of the best.
     Problem q = p;
     q.K = p.K / 2;
     auto best_split = [&](int w, int bm, double* t_out) {
@@ -632,7 +639,7 @@ mgemm_status_t mgemm_run_fp8(mgemm_handle_t h, mgemm_kernel_t kernel, int32_t ks
             const int ks = mgemm::f8_splits_bm(p, w, bm, req, h->ws);
             if (ks <= last) continue;
             last = ks;
-            const double t = predict_us(q, bm, w, w, w == 256 ? 1.4 : 1.3, 1, ks);
+            const double t = predict_us(q, bm, w, w, w == 256 ? 1.4 : 1.3, 1, ks, 4.5e6);
             if (t < bt) { bt = t; best = ks; }
         }
         if (t_out) *t_out = bt;
