@@ -216,9 +216,13 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     }
     // M <= 64 streams B once.  Short K (at most 64 slices) runs whole-K: with
     // few steps per range the exchange of partial rows costs more than a split
-    // saves (BF16, K = 2048: M = 64 17.4 us whole-K against 19.1 us at the best
-    // split; M = 1 / 16 / 32 x 1024 columns 6.8 / 6.7 / 8.0 against 7.2 / 8.7 /
-    // 11.5 on the split skinny kernel; K = 1024, M = 64: 9.4 against 15.7).
+    // saves (BF16, K = 2048, M = 1 / 16 / 32 x 1024 columns 6.8 / 6.7 / 8.0 us
+    // against 7.2 / 8.7 / 11.5 on the split skinny kernel; M = 64 x 12288
+    // columns 14.7 against 15.3 on 64-row tiles in 3 ranges; K = 1024, M = 64
+    // x 12288: 10.0 against 11.7).  Above 32 rows and 32 slices the whole-K
+    // kernel's 64-column blocks need N >= 8192 (128 workgroups) to keep up
+    // (K = 2048, M = 64 x 6144 / 4096 / 1024 columns: 13.7 / 13.1 / 10.5 us
+    // against 11.1 / 10.4 / 8.6 on 64-row tiles with a K split).
     // Longer K splits over workgroups.  The split skinny kernel reads B in
     // 512-byte row segments of 256-column blocks; it wins only for M <= 16,
     // only where at most 16 ranges of those blocks still give three quarters
@@ -230,7 +234,9 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // 7.6 / 7.9 / 8.5 us against 8.8 / 11.4 / 16.3 on the skinny kernel; M =
     // 32 x W[4096 x 4096] 15.0 against 17.1; M = 64 x W[4096 x 12288] 26.0
     // against 31.5).
-    if (p.M <= 64 && p.K <= 2048 && mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
+    if (p.M <= 64 && p.K <= 2048 && (p.M <= 32 || p.K <= 1024 || p.N >= 8192) &&
+        mgemm::skinny_supports(p))
+        return {MGEMM_KERNEL_SKINNY, 1};
     const int64_t sk_blocks = (p.N + 255) / 256;
     // The split skinny kernel's own choice of ranges, moved to the nearest
     // count (within one round of workgroups) whose ranges do not conflict.

@@ -892,6 +892,8 @@ def test_skinny_dispatch_rules(h):
         return mg.mgemm_select_variant(h, "row", "row", M, N, K, 1.0, 256, K, 256, N, 0.0, 256, N,
                                        "bf16")
     assert sel(16, 1024, 2048) == ("skinny", 1)
+    assert sel(64, 12288, 2048) == ("skinny", 1)
+    assert sel(64, 1024, 2048)[0] == "h_dma_64x192"
     assert sel(1, 12288, 4096)[0] == "skinny_sk"
     assert sel(32, 1536, 4096)[0] == "h_dma_64x192"
     for M, N, K in ((32, 4096, 4096), (32, 4096, 8192), (1, 4096, 12288), (64, 4096, 4096)):
@@ -899,7 +901,8 @@ def test_skinny_dispatch_rules(h):
         nks = -(-(K // 32) // ks)
         say("skinny rule", (M, N, K), name, ks)
         assert ks > 1 and (nks * 32 * N * 2) % (2 << 20) != 0, (M, N, K, name, ks)
-    for M, N, K in ((32, 1536, 4096), (32, 4096, 8192), (1, 4096, 12288), (16, 1024, 2048)):
+    for M, N, K in ((32, 1536, 4096), (32, 4096, 8192), (1, 4096, 12288), (16, 1024, 2048),
+                    (64, 1024, 2048)):
         case = W.Case("skinny_rule", M, N, K, "bf16", kindA="int", kindB="int", seeds=(M, N, K))
         say("skinny rule parity", (M, N, K), sel(M, N, K))
         P.check_bit_exact(case, *P.run_gpu(h, case))
