@@ -229,11 +229,11 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // of the CUs a workgroup, and above 4 rows only where 6 ranges do (BF16 x
     // W[4096 x 12288], M = 1 / 16: 21.0 / 22.4 us against 22.2 / 22.8 on
     // 64-row tiles).  Narrower B, or more rows (whose cost the skinny
-    // kernel's 16-row MFMA blocks pay in full), go to the time model below, which picks the 64- or 128-row tiles of the
-    // direct-to-LDS kernel with a K split (M = 1 / 16 / 32 x W[4096 x 1536]:
-    // 7.6 / 7.9 / 8.5 us against 8.8 / 11.4 / 16.3 on the skinny kernel; M =
-    // 32 x W[4096 x 4096] 15.0 against 17.1; M = 64 x W[4096 x 12288] 26.0
-    // against 31.5).
+    // kernel's 16-row MFMA blocks pay in full), go to the time model below,
+    // which picks the 64- or 128-row tiles of the direct-to-LDS kernel with a
+    // K split (M = 1 / 16 / 32 x W[4096 x 1536]: 7.6 / 7.9 / 8.5 us against
+    // 8.8 / 11.4 / 16.3 on the skinny kernel; M = 32 x W[4096 x 4096] 15.0
+    // against 17.1; M = 64 x W[4096 x 12288] 26.0 against 31.5).
     if (p.M <= 64 && p.K <= 2048 && (p.M <= 32 || p.K <= 1024 || p.N >= 8192) &&
         mgemm::skinny_supports(p))
         return {MGEMM_KERNEL_SKINNY, 1};
