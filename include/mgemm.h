@@ -85,8 +85,9 @@ typedef enum {
     MGEMM_KERNEL_H_DMA_128 = 18, /* FP16/BF16, A' K-contiguous (row-major A), 128x192 tiles, 4 waves
                                     of 64x96, direct-to-LDS ring (short M) */
     MGEMM_KERNEL_H_DMA_64 = 19,  /* FP16/BF16, A' K-contiguous, 64x192 tiles, 4 waves of 32x96,
-                                    direct-to-LDS ring (32 < M <= 64: streams B from HBM;
-                                    also small grids with a small B) */
+                                    direct-to-LDS ring (M <= 64 beyond the skinny kernels'
+                                    shapes: streams B from HBM with a K split; also small
+                                    grids with a small B) */
     MGEMM_KERNEL_F8_MFMA_128 = 20, /* FP8 codes (mgemm_run_fp8 only): 128x192 tiles, 4 waves of
                                       64x96, f8f6f4 MFMA (grids of 256-row tiles that leave CUs
                                       idle) */
