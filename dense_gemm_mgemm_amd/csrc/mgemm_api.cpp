@@ -192,11 +192,18 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         // last wave and every CU gets at least two K slices (measured:
         // 1000x12290x4095 892 against 1063 us, 3000^3 466 against 754 us,
         // 4096x3072x4096 799 against 985 us, 1000^3 78 against 126 us).
+        // Aligned shapes whose 128x128 tiles fill whole waves of one per CU
+        // take those instead (2048^3 159-162 against 171-172 us on stream-K,
+        // 4096x3072x4096 770-771 against 794; 1024x4096x4096 306-307 against
+        // 297-307, depending on the box).
         {
             const int64_t pairs = ((p.M + 255) / 256) * ((p.N + 255) / 256) * ((p.K + 31) / 32);
             if (fill(256, 256, 1) < 0.95 && pairs >= 2 * slots && mgemm::f32_unaligned_supports(p) &&
-                mgemm::f32_sk_fits(p, ws))
+                mgemm::f32_sk_fits(p, ws)) {
+                if (fill(128, 128, 1) >= 0.95 && mgemm::f32_fast_supports(p, false))
+                    return {MGEMM_KERNEL_F32_FAST_128, 1};
                 return {MGEMM_KERNEL_F32_SK, 1};
+            }
         }
         const bool big = mgemm::f32_fast_supports(p, true), small = mgemm::f32_fast_supports(p, false);
         if (big && (!small || fill(256, 256, 1) >= fill(128, 128, 2) * 0.9))
