@@ -58,9 +58,22 @@ def test_timed_path_does_not_import_the_oracle():
     # only torch, the library binding and the input generators.
     tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
     fn = {n.name: n for n in tree.body if isinstance(n, ast.FunctionDef)}
-    for name in ("measure", "measure_mix", "hold_stream", "roofline_entry"):
+    for name in ("measure", "measure_mix", "hold_stream", "roofline_entry", "dispatch_sweep"):
         for node in ast.walk(fn[name]):
             if isinstance(node, (ast.Import, ast.ImportFrom)):
                 mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module]
                 for m in mods:
                     assert not (m or "").startswith(("oracle", "tests")), (name, m)
+
+
+def test_dispatch_sweep_shapes():
+    # The sweep covers the three families, each shape once, with the leading
+    # dimensions the sweep derives from the layouts.
+    shapes = bench.sweep_shapes()
+    assert len(shapes) == len(set(shapes)) == 132
+    fams = {}
+    for dtype, la, lb, M, N, K in shapes:
+        assert M >= 1 and N >= 1 and K >= 1 and la in ("row", "col") and lb in ("row", "col")
+        fams[dtype] = fams.get(dtype, 0) + 1
+    assert fams == {"bf16": 98, "f16": 8, "f32": 16, "fp8": 10}
+    assert all(lb == "col" for d, la, lb, *_ in shapes if d == "fp8")
