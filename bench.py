@@ -573,7 +573,8 @@ def sweep_shapes():
                     (1024, 8192, 4096), (1, 4096, 8192), (32, 4096, 8192), (64, 4096, 8192),
                     (256, 4096, 8192), (16, 2048, 4096), (64, 2048, 8192), (1, 4096, 14336),
                     (32, 4096, 14336), (64, 4096, 14336), (512, 4096, 14336), (1, 14336, 4096),
-                    (32, 14336, 4096), (8, 8192, 8192), (1, 4096, 6144), (16, 4096, 6144)]:
+                    (32, 14336, 4096), (8, 8192, 8192), (1, 4096, 6144), (16, 4096, 6144),
+                    (1536, 12288, 4096), (640, 8192, 4096)]:
         out.append(("bf16", "row", "row", m, n, k))
     for m, n, k in [(1, 4096, 4096), (16, 4096, 4096), (32, 4096, 4096), (16, 1536, 4096),
                     (16, 12288, 4096), (32, 12288, 4096)]:

@@ -289,9 +289,14 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // x W[4096 x 12288] 33.5 / 36.5 us against 38.3 / 40.8 on 256-row tiles,
     // but M = 192 / 256 45.3 / 52.3 against 44.1 / 47.4 (W is 96 MiB); the
     // FFN share 1024x1536x4096 25.9 against 28.6 us, 512x1024x2048 15.9
-    // against 19.4, 256x4096x4096 22.1 against 25.0.
+    // against 19.4, 256x4096x4096 22.1 against 25.0.  From M = 1024 the
+    // 256-row tiles read each B panel four or more times already, and the
+    // 128-row grid can fill a last round that 256-row tiles leave half empty
+    // (M = 1536 x W[4096 x 12288]: 161.6 us against 182.3; the time model
+    // keeps 256-row tiles at M = 1024, 1280, 1792, 2048, 2560 and 3072, where
+    // they are the faster).
     const bool b_small = (double)p.K * (double)p.N * 2.0 <= 32.0 * 1024 * 1024;
-    if ((p.M <= 128 || b_small) && mgemm::h_dma_supports(p, 192, 128)) {
+    if ((p.M <= 128 || b_small || p.M >= 1024) && mgemm::h_dma_supports(p, 192, 128)) {
         double t;
         const int ks = auto_split(p, 192, false, ws, &t, 128);
         if (t < best_t) { best_t = t; best = {MGEMM_KERNEL_H_DMA_128, ks}; }

@@ -70,10 +70,10 @@ def test_dispatch_sweep_shapes():
     # The sweep covers the three families, each shape once, with the leading
     # dimensions the sweep derives from the layouts.
     shapes = bench.sweep_shapes()
-    assert len(shapes) == len(set(shapes)) == 132
+    assert len(shapes) == len(set(shapes)) == 134
     fams = {}
     for dtype, la, lb, M, N, K in shapes:
         assert M >= 1 and N >= 1 and K >= 1 and la in ("row", "col") and lb in ("row", "col")
         fams[dtype] = fams.get(dtype, 0) + 1
-    assert fams == {"bf16": 98, "f16": 8, "f32": 16, "fp8": 10}
+    assert fams == {"bf16": 100, "f16": 8, "f32": 16, "fp8": 10}
     assert all(lb == "col" for d, la, lb, *_ in shapes if d == "fp8")
