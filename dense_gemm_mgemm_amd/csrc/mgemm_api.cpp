@@ -154,6 +154,22 @@ bool conflicting_split(const Problem& p, int ks) {
     return (nks * 32 * pitch) % ((int64_t)2 << 20) == 0;
 }
 
+// The split skinny kernel's own choice of ranges, moved to the nearest count
+// (within one round of workgroups) whose ranges do not conflict as above.
+int skinny_sk_auto(const Problem& p, const mgemm::Workspace& ws) {
+    const int64_t slots = p.num_cu > 0 ? p.num_cu : 256;
+    const int64_t blocks = (p.N + 255) / 256;
+    const int ks = mgemm::skinny_sk_splits(p, ws, 0);
+    if (!conflicting_split(p, ks)) return ks;
+    for (int d : {-1, 1, -2, 2, -3, 3}) {
+        const int r = ks + d;
+        if (r < 2 || blocks * r > slots) continue;
+        const int k2 = mgemm::skinny_sk_splits(p, ws, r);
+        if (k2 >= 2 && !conflicting_split(p, k2)) return k2;
+    }
+    return ks;
+}
+
 // Split of K with the smallest predicted time for the direct-to-LDS kernel
 // (tile width bn; the gated pair's tile holds 96 output columns), among the
 // splits that fit the workspace and do not conflict as above.
@@ -245,19 +261,6 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
         mgemm::skinny_supports(p))
         return {MGEMM_KERNEL_SKINNY, 1};
     const int64_t sk_blocks = (p.N + 255) / 256;
-    // The split skinny kernel's own choice of ranges, moved to the nearest
-    // count (within one round of workgroups) whose ranges do not conflict.
-    auto sk_split = [&]() {
-        const int ks = mgemm::skinny_sk_splits(p, ws, 0);
-        if (!conflicting_split(p, ks)) return ks;
-        for (int d : {-1, 1, -2, 2, -3, 3}) {
-            const int r = ks + d;
-            if (r < 2 || sk_blocks * r > slots) continue;
-            const int k2 = mgemm::skinny_sk_splits(p, ws, r);
-            if (k2 >= 2 && !conflicting_split(p, k2)) return k2;
-        }
-        return ks;
-    };
     // Its last-arriving workgroup per block sums the other ranges' partial
     // rows (M of them, through device-scope memory): cheap for a few rows or
     // ranges, but for 8-16 rows over 8-16 ranges the 64-row tiles' separate
@@ -267,11 +270,11 @@ Choice model_choice(const Problem& p, const mgemm::Workspace& ws) {
     // M = 8 x W[8192 x 8192] 27.5 against 29.2, M = 1 x W[4096 x 4096] in 10
     // ranges 10.9 against 11.2).
     if (p.M <= 16 && sk_blocks * 16 * 4 >= slots * 3 && mgemm::skinny_sk_supports(p)) {
-        const int ks = sk_split();
+        const int ks = skinny_sk_auto(p, ws);
         if (p.M <= 4 || ks <= 6) return {MGEMM_KERNEL_SKINNY_SK, ks};
     }
     if (p.M <= 64 && !mgemm::h_dma_supports(p, 192, 64)) {
-        if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, sk_split()};
+        if (mgemm::skinny_sk_supports(p)) return {MGEMM_KERNEL_SKINNY_SK, skinny_sk_auto(p, ws)};
         if (mgemm::skinny_supports(p)) return {MGEMM_KERNEL_SKINNY, 1};
     }
     // 16-bit: the variant (and split of K) with the smallest predicted time.
@@ -348,7 +351,8 @@ int forced_splits(const Problem& p, const mgemm::Workspace& ws, mgemm_kernel_t k
     case MGEMM_KERNEL_H_DMA_64:
         return requested == 0 ? auto_split(p, 192, false, ws, nullptr, 64)
                               : mgemm::h_dma_splits(p, 192, false, requested, ws, 64);
-    case MGEMM_KERNEL_SKINNY_SK: return mgemm::skinny_sk_splits(p, ws, requested);
+    case MGEMM_KERNEL_SKINNY_SK:
+        return requested == 0 ? skinny_sk_auto(p, ws) : mgemm::skinny_sk_splits(p, ws, requested);
     case MGEMM_KERNEL_F32_SK: return requested <= 1 && mgemm::f32_sk_fits(p, ws) ? 1 : 0;
     default: return requested <= 1 ? 1 : 0;
     }
